@@ -1,0 +1,217 @@
+/*
+ * mla.h -- C ABI of libmla: Multi-head Latent Attention (MLA) for a block of
+ * L query rows (a speculative-decoding verify step) against a long
+ * compressed latent KV cache, on AMD Instinct MI355X (gfx950).
+ *
+ * Method (pages: "One guard, 110x off the verify step", sections "The
+ * defect", "The threshold is not a constant" and "The change"; mlx-lm PR
+ * #1817 "fix: Speed up multi-token decode by computing the absorbed MLA
+ * threshold", opening paragraphs).  MLA caches per token t a latent c_kv[t]
+ * of width r (kv_lora_rank) and a rope key k_pe[t] of width `rope` shared by
+ * every head.  Attention of the L new rows can be taken two ways that agree
+ * up to rounding:
+ *   absorbed      fold W_UK into the query (mla_fold_query), score against
+ *                 the latent plus the rope key, softmax, accumulate in latent
+ *                 space, up-project through W_UV (mla_absorbed_attention);
+ *                 cost grows with the number of new rows;
+ *   materialised  expand the cache into per-head K and V
+ *                 (mla_materialize_kv), then ordinary attention
+ *                 (mla_materialized_attention); cost grows with the cache.
+ * mla_select_path picks between them with the integer query-count threshold.
+ *
+ * Symbols: r = kv_lora_rank, n = qk_nope_head_dim, v = v_head_dim,
+ * rope = rope width, H = heads, B = sequences, L = query rows per sequence,
+ * Kv_b = positions sequence b attends over (its L new rows included).
+ *
+ * Conventions for every entry point:
+ *   - All functions are extern "C", never throw, and return an int status:
+ *     MLA_OK or a negative MLA_E_* code.  mla_status_string() names it.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is launched and output buffers are untouched.
+ *   - The caller owns every buffer.  The library never allocates, frees,
+ *     copies between host and device, or synchronises.  Device pointers
+ *     must stay valid until the work enqueued on `stream` has finished.
+ *   - `stream` is a hipStream_t (NULL = the default stream); all launches
+ *     are asynchronous on it.  Calls that share a workspace must not run
+ *     concurrently.
+ *   - All tensors are dense, row-major and contiguous.  Element type is
+ *     given by mla_dtype: MLA_BF16 = bfloat16 storage, MLA_F32 = float.
+ *     Outputs of the attention entry points are always float32.
+ *   - Causal rule of a verify block: the L new rows of sequence b are its
+ *     last L positions, so row i (0-based) sees the first Kv_b - L + i + 1
+ *     positions of the sequence.  Kv_b >= L is required.
+ *   - Packed variable-length caches: sequence b owns cache positions
+ *     kv_offsets[b] .. kv_offsets[b+1]-1 of c_kv / k_pe (or of K / V).
+ *     Offsets are int32, non-decreasing, kv_offsets[0] >= 0.  The same
+ *     offsets are passed twice: a host copy (validation and launch
+ *     planning) and a device copy (read by the kernels); they must hold the
+ *     same values.
+ *   - Supported geometry is listed per entry point; anything else returns
+ *     MLA_E_UNSUPPORTED.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Head geometry of one MLA attention layer. */
+typedef struct mla_geom {
+  int32_t r;     /* kv_lora_rank: width of the latent c_kv                 */
+  int32_t n;     /* qk_nope_head_dim: per-head query/key width without rope */
+  int32_t v;     /* v_head_dim: per-head value width                        */
+  int32_t rope;  /* width of q_pe and of the shared rope key k_pe (may be 0) */
+  int32_t heads; /* H: query heads                                           */
+} mla_geom;
+
+typedef enum mla_dtype { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+typedef enum mla_path { MLA_ABSORBED = 0, MLA_MATERIALIZED = 1 } mla_path;
+
+enum {
+  MLA_OK = 0,
+  MLA_E_NULL = -1,        /* a required pointer is NULL                       */
+  MLA_E_SHAPE = -2,       /* a size or offset is out of range / inconsistent */
+  MLA_E_UNSUPPORTED = -3, /* geometry or dtype not compiled in               */
+  MLA_E_WORKSPACE = -4,   /* workspace missing or too small                  */
+  MLA_E_HIP = -5          /* a HIP launch or runtime call failed             */
+};
+
+/* Static text for a status code ("ok", "null pointer", ...). */
+const char* mla_status_string(int status);
+
+/* Library ABI version (this header: 1). */
+int mla_version(void);
+
+/*
+ * mla_select_path -- choose the absorbed or the materialised path for a
+ * block of L query rows attending over T cached positions (host only, no
+ * device call, integer arithmetic, exact).
+ *
+ * Defined by the query-count threshold of "One guard, 110x off the verify
+ * step", sections "The threshold is not a constant" (cost model) and "The
+ * change" (helper and guard), and the finite-cache form of mlx-lm PR #1817
+ * (opening paragraphs).  With d = n + v:
+ *   if 2r - d <= 0:   max_absorbed = 1
+ *   elif T == 0:      max_absorbed = max(1, floor(r d / (2r - d)))            (long-cache limit)
+ *   else:             max_absorbed = max(1, floor(T r d / (r d + T (2r - d)))) (cache of T)
+ * The path is MLA_ABSORBED iff L <= max_absorbed (ties go to absorbed, as
+ * the guard is `L <= max_absorbed`).  T counts the block's own L rows;
+ * T == 0 asks for the limit form.  Products are formed in 128-bit integers,
+ * so the result is exact for every non-negative int32 geometry and int64 T.
+ *
+ * Arguments: g (host pointer; r >= 1, n >= 0, v >= 0), L >= 1, T >= 0
+ * (T >= L when T > 0).  path_out receives an mla_path value; max_absorbed_out
+ * may be NULL.  Errors: MLA_E_NULL (g or path_out NULL), MLA_E_SHAPE.
+ */
+int mla_select_path(const mla_geom* g, int64_t L, int64_t T, int32_t* path_out,
+                    int64_t* max_absorbed_out);
+
+/*
+ * mla_fold_query -- fold the key up-projection into the query ("One
+ * guard...", section "The defect": the absorbed path folds the
+ * up-projection into the query):
+ *   q_lat[m, h, c] = sum_j q_nope[m, h, j] * w_uk[h, j, c]
+ * for m < rows (rows = B*L), h < H, c < r.
+ *
+ *   q_nope  device, [rows, H, n], dtype dt
+ *   w_uk    device, [H, n, r],   dtype dt
+ *   q_lat   device, [rows, H, r], dtype dt (bf16: accumulated in float32,
+ *           rounded to nearest-even once)
+ * Supported: n % 32 == 0, r % 128 == 0 (bf16); any n, r >= 1 (f32).
+ */
+int mla_fold_query(const mla_geom* g, mla_dtype dt, int64_t rows, const void* q_nope,
+                   const void* w_uk, void* q_lat, void* stream);
+
+/*
+ * mla_absorbed_workspace_size -- bytes of device workspace that
+ * mla_absorbed_attention needs for these sizes (the split-KV partial
+ * results).  kv_offsets_host: host, [B+1].  Same validation as the
+ * attention call.
+ */
+int mla_absorbed_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
+                                const int32_t* kv_offsets_host, size_t* bytes_out);
+
+/*
+ * mla_absorbed_attention -- the absorbed path after the fold ("One
+ * guard...", section "The defect": attend directly against the compressed
+ * latent, then up-project).  For sequence b, row i, head h, with
+ * vis = Kv_b - L + i + 1 and t running over the sequence's first vis
+ * positions:
+ *   s_t        = scale * (q_lat[b,i,h,:] . c_kv[t,:] + q_pe[b,i,h,:] . k_pe[t,:])
+ *   o_lat      = sum_t softmax(s)_t * c_kv[t,:]
+ *   out[b,i,h,:] = o_lat . w_uv[h]
+ * Each latent tile is read once for all L*H (row, head) pairs of a
+ * sequence; positions are split across compute units and the splits are
+ * merged with a log-sum-exp combine that also applies w_uv.
+ *
+ *   q_lat   device, [B, L, H, r], dtype dt
+ *   q_pe    device, [B, L, H, rope], dtype dt (NULL allowed when rope == 0)
+ *   c_kv    device, [sum Kv, r], dtype dt
+ *   k_pe    device, [sum Kv, rope], dtype dt (NULL allowed when rope == 0)
+ *   kv_offsets_host / kv_offsets_dev   [B+1] int32 (see conventions)
+ *   w_uv    device, [H, r, v], dtype dt
+ *   scale   softmax scale (usually 1/sqrt(n + rope))
+ *   out     device, [B, L, H, v], float32
+ *   workspace / workspace_bytes   device scratch of at least
+ *           mla_absorbed_workspace_size() bytes, 256-byte aligned
+ * Supported (bf16): r == 512, rope in {0, 32, 64}, v % 32 == 0, v <= 512.
+ * Supported (f32): r <= 1024, rope <= 128, v <= 1024.
+ * The result is deterministic: no floating-point atomics are used.
+ */
+int mla_absorbed_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
+                           const void* q_lat, const void* q_pe, const void* c_kv,
+                           const void* k_pe, const int32_t* kv_offsets_host,
+                           const int32_t* kv_offsets_dev, const void* w_uv, float scale,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_materialize_kv -- expand the cached latent into full per-head keys
+ * and values ("One guard...", section "The defect": expand the entire
+ * cached latent back into full K and V), for T positions:
+ *   k[t, h, j]     = sum_c w_uk[h, j, c] * c_kv[t, c]     (j < n)
+ *   k[t, h, n + p] = k_pe[t, p]                           (shared rope key)
+ *   v[t, h, e]     = sum_c c_kv[t, c] * w_uv[h, c, e]      (e < v)
+ *
+ *   c_kv [T, r], k_pe [T, rope], w_uk [H, n, r], w_uv [H, r, v]: device, dtype dt
+ *   k    device, [T, H, n + rope], dtype dt
+ *   v    device, [T, H, v], dtype dt
+ * Supported (bf16): r % 64 == 0, n % 64 == 0, v % 64 == 0, rope % 8 == 0.
+ * Supported (f32): any sizes.
+ */
+int mla_materialize_kv(const mla_geom* g, mla_dtype dt, int64_t T, const void* c_kv,
+                       const void* k_pe, const void* w_uk, const void* w_uv, void* k, void* v,
+                       void* stream);
+
+/* Bytes of workspace mla_materialized_attention needs (split-KV partials). */
+int mla_materialized_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
+                                    const int32_t* kv_offsets_host, size_t* bytes_out);
+
+/*
+ * mla_materialized_attention -- ordinary causal attention over the
+ * expanded per-head K and V ("One guard...", section "The defect": then
+ * attend normally).  For sequence b, row i, head h, vis as above:
+ *   s_t = scale * (q_nope[b,i,h,:] . k[t,h,:n] + q_pe[b,i,h,:] . k[t,h,n:])
+ *   out[b,i,h,:] = sum_t softmax(s)_t * v[t,h,:]
+ *
+ *   q_nope [B, L, H, n], q_pe [B, L, H, rope]: device, dtype dt
+ *   k [sum Kv, H, n + rope], v [sum Kv, H, v]: device, dtype dt
+ *   out    device, [B, L, H, v], float32
+ *   workspace: at least mla_materialized_workspace_size() bytes
+ * Supported (bf16): (n + rope) % 32 == 0, n + rope <= 320, v % 64 == 0, v <= 256.
+ * Supported (f32): n + rope <= 1024, v <= 1024.
+ */
+int mla_materialized_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
+                               const void* q_nope, const void* q_pe, const void* k,
+                               const void* v, const int32_t* kv_offsets_host,
+                               const int32_t* kv_offsets_dev, float scale, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,17 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD GPU (gfx950) and the built HIP library")
+    config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+
+
+def golden_path(name: str) -> str:
+    return os.path.join(ROOT, "tests", "golden", name)
