@@ -121,7 +121,7 @@ int mla_select_path(const mla_geom* g, int64_t L, int64_t T, int32_t* path_out,
  *   w_uk    device, [H, n, r],   dtype dt
  *   q_lat   device, [rows, H, r], dtype dt (bf16: accumulated in float32,
  *           rounded to nearest-even once)
- * Supported: n % 32 == 0, r % 128 == 0 (bf16); any n, r >= 1 (f32).
+ * Supported: n % 64 == 0, n <= 256, r % 128 == 0 (bf16); any n, r >= 1 (f32).
  */
 int mla_fold_query(const mla_geom* g, mla_dtype dt, int64_t rows, const void* q_nope,
                    const void* w_uk, void* q_lat, void* stream);
@@ -158,8 +158,8 @@ int mla_absorbed_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int3
  *   out     device, [B, L, H, v], float32
  *   workspace / workspace_bytes   device scratch of at least
  *           mla_absorbed_workspace_size() bytes, 256-byte aligned
- * Supported (bf16): r == 512, rope in {0, 32, 64}, v % 32 == 0, v <= 512.
- * Supported (f32): r <= 1024, rope <= 128, v <= 1024.
+ * Supported (bf16): r == 512, rope in {0, 64}, v % 64 == 0, v <= 512.
+ * Supported (f32): r <= 1024, r + rope <= 1152, v <= 1024.
  * The result is deterministic: no floating-point atomics are used.
  */
 int mla_absorbed_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
@@ -167,6 +167,27 @@ int mla_absorbed_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L
                            const void* k_pe, const int32_t* kv_offsets_host,
                            const int32_t* kv_offsets_dev, const void* w_uv, float scale,
                            float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_absorbed_splits / mla_absorbed_merge -- the two launches that make up
+ * mla_absorbed_attention, exposed separately so that each kernel can be
+ * timed or overlapped on its own.  mla_absorbed_splits runs the split-KV
+ * pass (scores, online softmax and the latent accumulation for every split
+ * of every sequence) and leaves unnormalised partial results in the
+ * workspace; mla_absorbed_merge combines the splits with a log-sum-exp
+ * weighting and applies w_uv, writing out.  Calling splits then merge on
+ * one stream with the same arguments and workspace equals
+ * mla_absorbed_attention.  Arguments as for mla_absorbed_attention (merge
+ * reads only the offsets, w_uv, out and the workspace; the other tensor
+ * pointers are not used by it and may be NULL).
+ */
+int mla_absorbed_splits(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, const void* q_lat,
+                        const void* q_pe, const void* c_kv, const void* k_pe,
+                        const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int mla_absorbed_merge(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
+                       const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, const void* w_uv,
+                       float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * mla_materialize_kv -- expand the cached latent into full per-head keys
@@ -201,8 +222,8 @@ int mla_materialized_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, 
  *   k [sum Kv, H, n + rope], v [sum Kv, H, v]: device, dtype dt
  *   out    device, [B, L, H, v], float32
  *   workspace: at least mla_materialized_workspace_size() bytes
- * Supported (bf16): (n + rope) % 32 == 0, n + rope <= 320, v % 64 == 0, v <= 256.
- * Supported (f32): n + rope <= 1024, v <= 1024.
+ * Supported (bf16): n in {128, 192, 256}, rope in {0, 64}, v in {128, 256}.
+ * Supported (f32): n + rope <= 1152, v <= 1024.
  */
 int mla_materialized_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
                                const void* q_nope, const void* q_pe, const void* k,

@@ -1,0 +1,270 @@
+"""MI355X-native Multi-head Latent Attention for speculative-decoding verify.
+
+A thin Python binding over libmla.so (include/mla.h).  Every function here
+only marshals arguments -- tensor pointers, sizes and the current HIP stream
+-- and calls the C ABI; all computation runs in the library's HIP kernels.
+PyTorch supplies device memory and streams.
+
+Entry points (same names as the C ABI, without the ``mla_`` prefix):
+    select_path, fold_query, absorbed_workspace_size, absorbed_attention,
+    materialize_kv, materialized_workspace_size, materialized_attention
+and two conveniences that chain them: ``absorbed`` (fold + attention) and
+``materialized`` (expand + attention).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Sequence
+
+from . import _lib
+from ._lib import Geom, MlaError, MLA_ABSORBED, MLA_MATERIALIZED  # noqa: F401
+
+__all__ = ["Geom", "MlaError", "MLA_ABSORBED", "MLA_MATERIALIZED", "Offsets", "select_path",
+           "fold_query", "absorbed_workspace_size", "absorbed_attention", "absorbed_splits",
+           "absorbed_merge", "materialize_kv",
+           "materialized_workspace_size", "materialized_attention", "absorbed", "materialized",
+           "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _lib.MLA_BF16
+    if t.dtype == torch.float32:
+        return _lib.MLA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Offsets:
+    """Per-sequence cache offsets [B+1] (int32), held on the host and on the device."""
+
+    def __init__(self, offsets, device=None):
+        torch = _torch()
+        host = torch.as_tensor(offsets, dtype=torch.int32).contiguous().cpu()
+        if host.dim() != 1 or host.numel() < 2:
+            raise ValueError("offsets must be a 1-D sequence of B+1 integers")
+        self.host = host
+        self.dev = host.to(device if device is not None else "cuda")
+        self.B = host.numel() - 1
+
+    @classmethod
+    def dense(cls, B: int, kv: int, device=None) -> "Offsets":
+        return cls([b * kv for b in range(B + 1)], device)
+
+    def host_ptr(self):
+        return ctypes.c_void_p(self.host.data_ptr())
+
+    def dev_ptr(self):
+        return ctypes.c_void_p(self.dev.data_ptr())
+
+
+def _as_offsets(kv_offsets, device) -> Offsets:
+    return kv_offsets if isinstance(kv_offsets, Offsets) else Offsets(kv_offsets, device)
+
+
+def select_path(geom: Geom, L: int, T: int = 0) -> tuple[int, int]:
+    """(path, max_absorbed) for L query rows over T cached positions (T = 0: limit form)."""
+    lib = _lib.load()
+    path = ctypes.c_int32()
+    m = ctypes.c_int64()
+    _lib.check("mla_select_path", lib.mla_select_path(ctypes.byref(geom), int(L), int(T),
+                                                      ctypes.byref(path), ctypes.byref(m)))
+    return int(path.value), int(m.value)
+
+
+def fold_query(q_nope, w_uk, out=None, stream=None):
+    """q_lat[m, h, :] = q_nope[m, h, :] @ w_uk[h].  q_nope [..., H, n] -> [..., H, r]."""
+    torch = _torch()
+    lib = _lib.load()
+    H, n, r = w_uk.shape
+    rows = q_nope.numel() // (H * n)
+    g = Geom(r, n, 1, 0, H)
+    if out is None:
+        out = torch.empty(q_nope.shape[:-1] + (r,), dtype=q_nope.dtype, device=q_nope.device)
+    dt = _dtype_code(q_nope)
+    if _dtype_code(w_uk) != dt or _dtype_code(out) != dt:
+        raise TypeError("q_nope, w_uk and q_lat must share one dtype")
+    _lib.check("mla_fold_query", lib.mla_fold_query(ctypes.byref(g), dt, rows, _ptr(_dev(q_nope, "q_nope")),
+                                                    _ptr(_dev(w_uk, "w_uk")), _ptr(out), _stream(stream)))
+    return out
+
+
+def absorbed_workspace_size(geom: Geom, dtype_code: int, L: int, kv_offsets: Offsets) -> int:
+    lib = _lib.load()
+    sz = ctypes.c_size_t()
+    _lib.check("mla_absorbed_workspace_size",
+               lib.mla_absorbed_workspace_size(ctypes.byref(geom), dtype_code, kv_offsets.B, int(L),
+                                               kv_offsets.host_ptr(), ctypes.byref(sz)))
+    return int(sz.value)
+
+
+def absorbed_attention(q_lat, q_pe, c_kv, k_pe, w_uv, kv_offsets, scale=None, out=None, workspace=None,
+                       stream=None, n=None):
+    """Absorbed attention after the fold.  q_lat [B, L, H, r], q_pe [B, L, H, rope],
+    c_kv [sumKv, r], k_pe [sumKv, rope], w_uv [H, r, v] -> out [B, L, H, v] float32.
+    ``scale`` defaults to 1/sqrt(n + rope) (n must then be given)."""
+    torch = _torch()
+    lib = _lib.load()
+    B, L, H, r = q_lat.shape
+    rope = q_pe.shape[-1] if q_pe is not None else 0
+    v = w_uv.shape[-1]
+    offs = _as_offsets(kv_offsets, q_lat.device)
+    if offs.B != B:
+        raise ValueError("offsets do not match the batch")
+    if scale is None:
+        if n is None:
+            raise ValueError("give scale, or n to default it to 1/sqrt(n + rope)")
+        scale = 1.0 / math.sqrt(n + rope)
+    g = Geom(r, int(n) if n is not None else 0, v, rope, H)
+    dt = _dtype_code(q_lat)
+    need = absorbed_workspace_size(g, dt, L, offs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q_lat.device)
+    if out is None:
+        out = torch.empty((B, L, H, v), dtype=torch.float32, device=q_lat.device)
+    _lib.check("mla_absorbed_attention", lib.mla_absorbed_attention(
+        ctypes.byref(g), dt, B, L, _ptr(_dev(q_lat, "q_lat")), _ptr(q_pe) if rope else None,
+        _ptr(_dev(c_kv, "c_kv")), _ptr(k_pe) if rope else None, offs.host_ptr(), offs.dev_ptr(),
+        _ptr(_dev(w_uv, "w_uv")), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def absorbed_splits(q_lat, q_pe, c_kv, k_pe, kv_offsets: Offsets, geom: Geom, scale: float, workspace,
+                    stream=None):
+    """Split-KV pass of the absorbed attention (one kernel); partials go to ``workspace``."""
+    lib = _lib.load()
+    B, L = q_lat.shape[0], q_lat.shape[1]
+    rope = geom.rope
+    _lib.check("mla_absorbed_splits", lib.mla_absorbed_splits(
+        ctypes.byref(geom), _dtype_code(q_lat), B, L, _ptr(_dev(q_lat, "q_lat")), _ptr(q_pe) if rope else None,
+        _ptr(_dev(c_kv, "c_kv")), _ptr(k_pe) if rope else None, kv_offsets.host_ptr(), kv_offsets.dev_ptr(),
+        ctypes.c_float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def absorbed_merge(w_uv, out, kv_offsets: Offsets, geom: Geom, L: int, workspace, stream=None):
+    """Merge pass of the absorbed attention (one kernel): log-sum-exp combine and W_UV."""
+    lib = _lib.load()
+    _lib.check("mla_absorbed_merge", lib.mla_absorbed_merge(
+        ctypes.byref(geom), _dtype_code(w_uv), kv_offsets.B, int(L), kv_offsets.host_ptr(), kv_offsets.dev_ptr(),
+        _ptr(_dev(w_uv, "w_uv")), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out
+
+
+def materialize_kv(c_kv, k_pe, w_uk, w_uv, k=None, v=None, stream=None):
+    """K [T, H, n+rope], V [T, H, v] from the latent cache."""
+    torch = _torch()
+    lib = _lib.load()
+    T, r = c_kv.shape
+    rope = k_pe.shape[-1] if k_pe is not None else 0
+    H, n, _ = w_uk.shape
+    vd = w_uv.shape[-1]
+    g = Geom(r, n, vd, rope, H)
+    if k is None:
+        k = torch.empty((T, H, n + rope), dtype=c_kv.dtype, device=c_kv.device)
+    if v is None:
+        v = torch.empty((T, H, vd), dtype=c_kv.dtype, device=c_kv.device)
+    _lib.check("mla_materialize_kv", lib.mla_materialize_kv(
+        ctypes.byref(g), _dtype_code(c_kv), T, _ptr(_dev(c_kv, "c_kv")), _ptr(k_pe) if rope else None,
+        _ptr(w_uk), _ptr(w_uv), _ptr(k), _ptr(v), _stream(stream)))
+    return k, v
+
+
+def materialized_workspace_size(geom: Geom, dtype_code: int, L: int, kv_offsets: Offsets) -> int:
+    lib = _lib.load()
+    sz = ctypes.c_size_t()
+    _lib.check("mla_materialized_workspace_size",
+               lib.mla_materialized_workspace_size(ctypes.byref(geom), dtype_code, kv_offsets.B, int(L),
+                                                   kv_offsets.host_ptr(), ctypes.byref(sz)))
+    return int(sz.value)
+
+
+def materialized_attention(q_nope, q_pe, k, v, kv_offsets, scale=None, out=None, workspace=None, stream=None):
+    """Ordinary causal attention over expanded K [sumKv, H, n+rope] and V [sumKv, H, v]."""
+    torch = _torch()
+    lib = _lib.load()
+    B, L, H, n = q_nope.shape
+    rope = q_pe.shape[-1] if q_pe is not None else 0
+    vd = v.shape[-1]
+    offs = _as_offsets(kv_offsets, q_nope.device)
+    if offs.B != B:
+        raise ValueError("offsets do not match the batch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(n + rope)
+    g = Geom(1, n, vd, rope, H)
+    dt = _dtype_code(q_nope)
+    need = materialized_workspace_size(g, dt, L, offs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q_nope.device)
+    if out is None:
+        out = torch.empty((B, L, H, vd), dtype=torch.float32, device=q_nope.device)
+    _lib.check("mla_materialized_attention", lib.mla_materialized_attention(
+        ctypes.byref(g), dt, B, L, _ptr(_dev(q_nope, "q_nope")), _ptr(q_pe) if rope else None,
+        _ptr(_dev(k, "k")), _ptr(_dev(v, "v")), offs.host_ptr(), offs.dev_ptr(), ctypes.c_float(scale),
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def absorbed(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, kv_offsets, scale=None, stream=None, q_lat=None,
+             out=None, workspace=None):
+    """Whole absorbed path: fold_query then absorbed_attention."""
+    q_lat = fold_query(q_nope, w_uk, out=q_lat, stream=stream)
+    return absorbed_attention(q_lat, q_pe, c_kv, k_pe, w_uv, kv_offsets, scale=scale, out=out,
+                              workspace=workspace, stream=stream, n=q_nope.shape[-1])
+
+
+def materialized(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, kv_offsets, scale=None, stream=None, k=None, v=None,
+                 out=None, workspace=None):
+    """Whole materialised path: materialize_kv then materialized_attention."""
+    k, v = materialize_kv(c_kv, k_pe, w_uk, w_uv, k=k, v=v, stream=stream)
+    return materialized_attention(q_nope, q_pe, k, v, kv_offsets, scale=scale, out=out, workspace=workspace,
+                                  stream=stream)
+
+
+def chosen_path(geom: Geom, L: int, T: int) -> int:
+    return select_path(geom, L, T)[0]
+
+
+def forward(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, kv_offsets: Sequence[int] | Offsets, scale=None, stream=None):
+    """Verify-step attention with the path picked by select_path (T = longest cache)."""
+    offs = _as_offsets(kv_offsets, q_nope.device)
+    H, n, r = w_uk.shape
+    L = q_nope.shape[1]
+    rope = q_pe.shape[-1] if q_pe is not None else 0
+    T = int((offs.host[1:] - offs.host[:-1]).max())
+    g = Geom(r, n, w_uv.shape[-1], rope, H)
+    if select_path(g, L, T)[0] == MLA_ABSORBED:
+        return absorbed(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, offs, scale=scale, stream=stream)
+    return materialized(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, offs, scale=scale, stream=stream)

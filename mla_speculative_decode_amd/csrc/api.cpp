@@ -1,0 +1,292 @@
+// api.cpp -- the C ABI of libmla (declared in include/mla.h): argument
+// validation on the host, split-KV planning, and kernel launches.  No call
+// here allocates, frees, copies or synchronises.
+
+#include "../../include/mla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "internal.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr int kCUs = 256;            // MI355X compute units (planning target)
+constexpr int kTile = 64;            // positions per attention tile, query rows per workgroup
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dtype_ok(mla_dtype dt) { return dt == MLA_F32 || dt == MLA_BF16; }
+
+int check_geom(const mla_geom* g) {
+  if (!g) return MLA_E_NULL;
+  if (g->r < 1 || g->n < 0 || g->v < 1 || g->rope < 0 || g->heads < 1) return MLA_E_SHAPE;
+  return MLA_OK;
+}
+
+// Offsets: B >= 1, off[0] >= 0, every Kv_b >= L, and the packed length fits int32.
+int check_offsets(int32_t B, int32_t L, const int32_t* off) {
+  if (!off) return MLA_E_NULL;
+  if (B < 1 || L < 1) return MLA_E_SHAPE;
+  if (off[0] < 0) return MLA_E_SHAPE;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t kv = (int64_t)off[b + 1] - (int64_t)off[b];
+    if (kv < L) return MLA_E_SHAPE;
+  }
+  return MLA_OK;
+}
+
+// Split-KV plan: aim for about one workgroup per compute unit on a single
+// sequence and about four per unit across a batch (variable lengths need the
+// slack to balance), never splitting finer than one 64-position tile.
+int make_plan(int32_t B, int32_t L, int32_t H, const int32_t* off, int rows_slot, int head_slots, int DV,
+              SplitPlan* p) {
+  const int64_t row_tiles = (rows_slot + kTile - 1) / kTile;
+  int64_t total_tiles = 0;
+  for (int32_t b = 0; b < B; ++b) total_tiles += (off[b + 1] - off[b] + kTile - 1) / kTile;
+  const int64_t units = row_tiles * head_slots * total_tiles;
+  const int64_t target = (int64_t)kCUs * (B > 1 ? 4 : 1);
+  const int64_t chunk_tiles = std::max<int64_t>(1, (units + target - 1) / target);
+  if (chunk_tiles * kTile > INT32_MAX) return MLA_E_SHAPE;
+  const int chunk = (int)(chunk_tiles * kTile);
+  int64_t splits = 0;
+  for (int32_t b = 0; b < B; ++b) splits += (off[b + 1] - off[b] + chunk - 1) / chunk;
+  const int64_t items = splits * head_slots * row_tiles;
+  const int64_t f32_items = splits * head_slots * rows_slot;
+  if (items > INT32_MAX || f32_items > INT32_MAX || splits > INT32_MAX) return MLA_E_SHAPE;
+  p->chunk = chunk;
+  p->n_splits = (int)splits;
+  p->row_tiles = (int)row_tiles;
+  p->head_slots = head_slots;
+  p->n_items = (int)items;
+  const size_t rows_total = (size_t)L * H;
+  p->ws_o_floats = (size_t)splits * rows_total * DV;
+  p->ws_ml_floats = (size_t)splits * rows_total * 2;
+  p->ws_bytes = align_up(p->ws_o_floats * 4) + align_up(p->ws_ml_floats * 4);
+  return MLA_OK;
+}
+
+int absorbed_supported(const mla_geom* g, mla_dtype dt) {
+  if (dt == MLA_BF16) {
+    if (g->r != 512 || !(g->rope == 0 || g->rope == 64) || g->v % 64 != 0 || g->v > 512)
+      return MLA_E_UNSUPPORTED;
+  } else {
+    if (g->r > 1024 || g->r + g->rope > 1152 || g->v > 1024) return MLA_E_UNSUPPORTED;
+  }
+  return MLA_OK;
+}
+
+int materialized_supported(const mla_geom* g, mla_dtype dt) {
+  if (dt == MLA_BF16) {
+    if (!materialized_bf16_supported(g->n, g->rope, g->v)) return MLA_E_UNSUPPORTED;
+  } else {
+    if (g->n + g->rope > 1152 || g->v > 1024) return MLA_E_UNSUPPORTED;
+  }
+  return MLA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_E_NULL: return "null pointer";
+    case MLA_E_SHAPE: return "size or offset out of range";
+    case MLA_E_UNSUPPORTED: return "geometry or dtype not supported";
+    case MLA_E_WORKSPACE: return "workspace missing or too small";
+    case MLA_E_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int mla_version(void) { return 1; }
+
+int mla_select_path(const mla_geom* g, int64_t L, int64_t T, int32_t* path_out, int64_t* max_absorbed_out) {
+  if (!g || !path_out) return MLA_E_NULL;
+  if (g->r < 1 || g->n < 0 || g->v < 0 || L < 1 || T < 0 || (T > 0 && T < L)) return MLA_E_SHAPE;
+  const __int128 r = g->r, d = (__int128)g->n + g->v;
+  const __int128 denom = 2 * r - d;
+  __int128 m;
+  if (denom <= 0) {
+    m = 1;
+  } else if (T == 0) {
+    m = (r * d) / denom;                       // floor: both operands positive
+  } else {
+    const __int128 t = T;
+    m = (t * r * d) / (r * d + t * denom);     // absorbed while L <= T r d / (r d + T (2r - d))
+  }
+  if (m < 1) m = 1;
+  if (m > (__int128)INT64_MAX) m = INT64_MAX;
+  *path_out = ((__int128)L <= m) ? MLA_ABSORBED : MLA_MATERIALIZED;
+  if (max_absorbed_out) *max_absorbed_out = (int64_t)m;
+  return MLA_OK;
+}
+
+int mla_fold_query(const mla_geom* g, mla_dtype dt, int64_t rows, const void* q_nope, const void* w_uk,
+                   void* q_lat, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!dtype_ok(dt)) return MLA_E_UNSUPPORTED;
+  if (rows < 1 || g->n < 1 || rows * g->heads > INT32_MAX) return MLA_E_SHAPE;
+  if (!q_nope || !w_uk || !q_lat) return MLA_E_NULL;
+  if (dt == MLA_BF16 && (g->n % 64 != 0 || g->n > 256 || g->r % 128 != 0)) return MLA_E_UNSUPPORTED;
+  return hip_status(fold_query(dt == MLA_BF16 ? kBF16 : kF32, (int)rows, g->heads, g->n, g->r, q_nope, w_uk,
+                               q_lat, (hipStream_t)stream));
+}
+
+int mla_absorbed_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
+                                const int32_t* kv_offsets_host, size_t* bytes_out) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!dtype_ok(dt)) return MLA_E_UNSUPPORTED;
+  if (!bytes_out) return MLA_E_NULL;
+  if ((st = check_offsets(B, L, kv_offsets_host))) return st;
+  if ((int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
+  if ((st = absorbed_supported(g, dt))) return st;
+  SplitPlan p{};
+  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L * g->heads, 1, g->r, &p))) return st;
+  *bytes_out = p.ws_bytes;
+  return MLA_OK;
+}
+
+namespace {
+
+// Validation and planning shared by the absorbed launches.  need_inputs:
+// the split pass reads q_lat, q_pe, c_kv, k_pe; need_merge: the merge reads
+// w_uv and writes out.
+int absorbed_prepare(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                     const void* c_kv, const void* k_pe, const int32_t* off_h, const int32_t* off_d,
+                     const void* w_uv, const float* out, void* workspace, size_t workspace_bytes, float scale,
+                     bool need_inputs, bool need_merge, AbsorbedLaunch* q) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!dtype_ok(dt)) return MLA_E_UNSUPPORTED;
+  if ((st = check_offsets(B, L, off_h))) return st;
+  if ((int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
+  if (!off_d) return MLA_E_NULL;
+  if (need_inputs) {
+    if (!q_lat || !c_kv) return MLA_E_NULL;
+    if (g->rope > 0 && (!q_pe || !k_pe)) return MLA_E_NULL;
+  }
+  if (need_merge && (!w_uv || !out)) return MLA_E_NULL;
+  if ((st = absorbed_supported(g, dt))) return st;
+  SplitPlan p{};
+  if ((st = make_plan(B, L, g->heads, off_h, L * g->heads, 1, g->r, &p))) return st;
+  if (!workspace || workspace_bytes < p.ws_bytes) return MLA_E_WORKSPACE;
+  q->r = g->r; q->rope = g->rope; q->v_dim = g->v; q->H = g->heads; q->B = B; q->L = L;
+  q->q_lat = q_lat; q->q_pe = q_pe; q->c_kv = c_kv; q->k_pe = k_pe; q->w_uv = w_uv;
+  q->off_dev = off_d; q->scale = scale;
+  q->ws_o = (float*)workspace;
+  q->ws_ml = (float*)((char*)workspace + align_up(p.ws_o_floats * 4));
+  q->plan = p;
+  return MLA_OK;
+}
+
+int absorbed_split_launch(const AbsorbedLaunch& q, mla_dtype dt, hipStream_t s) {
+  return hip_status(dt == MLA_BF16 ? absorbed_attn_bf16(q, s) : attn_f32(&q, nullptr, s));
+}
+
+}  // namespace
+
+int mla_absorbed_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, const void* q_lat,
+                           const void* q_pe, const void* c_kv, const void* k_pe, const int32_t* kv_offsets_host,
+                           const int32_t* kv_offsets_dev, const void* w_uv, float scale, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  AbsorbedLaunch q{};
+  int st = absorbed_prepare(g, dt, B, L, q_lat, q_pe, c_kv, k_pe, kv_offsets_host, kv_offsets_dev, w_uv, out,
+                            workspace, workspace_bytes, scale, true, true, &q);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = absorbed_split_launch(q, dt, s))) return st;
+  return hip_status(combine_upproj(q, dt == MLA_BF16 ? kBF16 : kF32, out, s));
+}
+
+int mla_absorbed_splits(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, const void* q_lat,
+                        const void* q_pe, const void* c_kv, const void* k_pe, const int32_t* kv_offsets_host,
+                        const int32_t* kv_offsets_dev, float scale, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  AbsorbedLaunch q{};
+  int st = absorbed_prepare(g, dt, B, L, q_lat, q_pe, c_kv, k_pe, kv_offsets_host, kv_offsets_dev, nullptr,
+                            nullptr, workspace, workspace_bytes, scale, true, false, &q);
+  if (st) return st;
+  return absorbed_split_launch(q, dt, (hipStream_t)stream);
+}
+
+int mla_absorbed_merge(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, const int32_t* kv_offsets_host,
+                       const int32_t* kv_offsets_dev, const void* w_uv, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  AbsorbedLaunch q{};
+  int st = absorbed_prepare(g, dt, B, L, nullptr, nullptr, nullptr, nullptr, kv_offsets_host, kv_offsets_dev,
+                            w_uv, out, workspace, workspace_bytes, 0.f, false, true, &q);
+  if (st) return st;
+  return hip_status(combine_upproj(q, dt == MLA_BF16 ? kBF16 : kF32, out, (hipStream_t)stream));
+}
+
+int mla_materialize_kv(const mla_geom* g, mla_dtype dt, int64_t T, const void* c_kv, const void* k_pe,
+                       const void* w_uk, const void* w_uv, void* k, void* v, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!dtype_ok(dt)) return MLA_E_UNSUPPORTED;
+  if (T < 1 || T > INT32_MAX) return MLA_E_SHAPE;
+  if (!c_kv || !w_uk || !w_uv || !k || !v) return MLA_E_NULL;
+  if (g->rope > 0 && !k_pe) return MLA_E_NULL;
+  if (dt == MLA_BF16 && (g->r % 64 != 0 || g->n % 64 != 0 || g->v % 64 != 0 || g->rope % 8 != 0))
+    return MLA_E_UNSUPPORTED;
+  return hip_status(materialize_kv(dt == MLA_BF16 ? kBF16 : kF32, T, g->heads, g->r, g->n, g->v, g->rope, c_kv,
+                                   k_pe, w_uk, w_uv, k, v, (hipStream_t)stream));
+}
+
+int mla_materialized_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
+                                    const int32_t* kv_offsets_host, size_t* bytes_out) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!dtype_ok(dt)) return MLA_E_UNSUPPORTED;
+  if (!bytes_out) return MLA_E_NULL;
+  if ((st = check_offsets(B, L, kv_offsets_host))) return st;
+  if ((int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
+  if ((st = materialized_supported(g, dt))) return st;
+  SplitPlan p{};
+  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L, g->heads, g->v, &p))) return st;
+  *bytes_out = p.ws_bytes;
+  return MLA_OK;
+}
+
+int mla_materialized_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, const void* q_nope,
+                               const void* q_pe, const void* k, const void* v, const int32_t* kv_offsets_host,
+                               const int32_t* kv_offsets_dev, float scale, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!dtype_ok(dt)) return MLA_E_UNSUPPORTED;
+  if ((st = check_offsets(B, L, kv_offsets_host))) return st;
+  if ((int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
+  if (!q_nope || !k || !v || !kv_offsets_dev || !out) return MLA_E_NULL;
+  if (g->rope > 0 && !q_pe) return MLA_E_NULL;
+  if (g->n < 1) return MLA_E_SHAPE;
+  if ((st = materialized_supported(g, dt))) return st;
+  SplitPlan p{};
+  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L, g->heads, g->v, &p))) return st;
+  if (!workspace || workspace_bytes < p.ws_bytes) return MLA_E_WORKSPACE;
+  MaterializedLaunch q{};
+  q.n = g->n; q.rope = g->rope; q.v_dim = g->v; q.H = g->heads; q.B = B; q.L = L;
+  q.q_nope = q_nope; q.q_pe = q_pe; q.k = k; q.v = v;
+  q.off_dev = kv_offsets_dev; q.scale = scale;
+  q.ws_o = (float*)workspace;
+  q.ws_ml = (float*)((char*)workspace + align_up(p.ws_o_floats * 4));
+  q.plan = p;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = (dt == MLA_BF16) ? materialized_attn_bf16(q, s) : attn_f32(nullptr, &q, s);
+  if (e != hipSuccess) return MLA_E_HIP;
+  return hip_status(combine_materialized(q, out, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// bench_driver.cpp -- native timing loop for bench.py (built as a separate
+// libmla_bench.so; not part of libmla's ABI).  Issues the absorbed verify
+// step -- mla_fold_query, mla_absorbed_splits, mla_absorbed_merge -- from C so
+// that host launch cost stays below the GPU time per step, and times it with
+// HIP events on the caller's stream.  Input sets are rotated so that a set is
+// evicted from the caches before it is used again when enough sets are given.
+
+#include "../../include/mla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <vector>
+
+namespace {
+
+struct Sets {
+  void* const* q_nope; void* const* q_pe; void* const* c_kv; void* const* k_pe;
+  void* const* w_uk; void* const* w_uv; void* const* q_lat; float* const* out;
+};
+
+int step(const mla_geom* g, int B, int L, const Sets& s, int k, const int32_t* off_h, const int32_t* off_d,
+         float scale, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev) {
+  int rc;
+  if (ev) hipEventRecord(ev[0], st);
+  if ((rc = mla_fold_query(g, MLA_BF16, (int64_t)B * L, s.q_nope[k], s.w_uk[k], s.q_lat[k], st))) return rc;
+  if (ev) hipEventRecord(ev[1], st);
+  if ((rc = mla_absorbed_splits(g, MLA_BF16, B, L, s.q_lat[k], s.q_pe[k], s.c_kv[k], s.k_pe[k], off_h, off_d, scale,
+                                ws, ws_bytes, st)))
+    return rc;
+  if (ev) hipEventRecord(ev[2], st);
+  if ((rc = mla_absorbed_merge(g, MLA_BF16, B, L, off_h, off_d, s.w_uv[k], s.out[k], ws, ws_bytes, st))) return rc;
+  if (ev) hipEventRecord(ev[3], st);
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+// res[0] us/step, plain back-to-back steps (events only around the run)
+// res[1] us fold, res[2] us splits, res[3] us merge (per-launch means, evented run)
+// res[4] us/step of the evented run
+int mlab_absorbed_run(const mla_geom* g, int B, int L, int nsets, void* const* q_nope, void* const* q_pe,
+                      void* const* c_kv, void* const* k_pe, void* const* w_uk, void* const* w_uv,
+                      void* const* q_lat, float* const* out, const int32_t* off_h, const int32_t* off_d,
+                      float scale, void* ws, size_t ws_bytes, void* stream, int warmup, int steps, double* res) {
+  hipStream_t st = (hipStream_t)stream;
+  Sets s{q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, q_lat, out};
+  int rc;
+  for (int i = 0; i < warmup; ++i)
+    if ((rc = step(g, B, L, s, i % nsets, off_h, off_d, scale, ws, ws_bytes, st, nullptr))) return rc;
+  hipEvent_t a, b;
+  hipEventCreate(&a);
+  hipEventCreate(&b);
+  hipStreamSynchronize(st);
+  hipEventRecord(a, st);
+  for (int i = 0; i < steps; ++i)
+    if ((rc = step(g, B, L, s, i % nsets, off_h, off_d, scale, ws, ws_bytes, st, nullptr))) return rc;
+  hipEventRecord(b, st);
+  hipStreamSynchronize(st);
+  float ms = 0.f;
+  hipEventElapsedTime(&ms, a, b);
+  res[0] = 1e3 * ms / steps;
+
+  std::vector<hipEvent_t> ev((size_t)steps * 4);
+  for (auto& e : ev) hipEventCreate(&e);
+  hipStreamSynchronize(st);
+  for (int i = 0; i < steps; ++i)
+    if ((rc = step(g, B, L, s, i % nsets, off_h, off_d, scale, ws, ws_bytes, st, &ev[(size_t)i * 4]))) return rc;
+  hipStreamSynchronize(st);
+  double t[3] = {0, 0, 0};
+  for (int i = 0; i < steps; ++i) {
+    for (int j = 0; j < 3; ++j) {
+      float x = 0.f;
+      hipEventElapsedTime(&x, ev[(size_t)i * 4 + j], ev[(size_t)i * 4 + j + 1]);
+      t[j] += x;
+    }
+  }
+  float whole = 0.f;
+  hipEventElapsedTime(&whole, ev[0], ev[(size_t)(steps - 1) * 4 + 3]);
+  for (int j = 0; j < 3; ++j) res[1 + j] = 1e3 * t[j] / steps;
+  res[4] = 1e3 * whole / steps;
+  for (auto& e : ev) hipEventDestroy(e);
+  hipEventDestroy(a);
+  hipEventDestroy(b);
+  return hipGetLastError() == hipSuccess ? 0 : MLA_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// internal.h -- launch descriptors shared between the C ABI layer (api.cpp)
+// and the kernel files (attn.hip, gemm.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+enum mla_dtype_t { kF32 = 0, kBF16 = 1 };
+
+// Split-KV launch plan.  Sequence b is cut into ceil(Kv_b / chunk) splits;
+// work item = (split, head slot, row tile).
+struct SplitPlan {
+  int chunk;       // positions per split, multiple of 64
+  int n_splits;    // total splits over all sequences
+  int row_tiles;   // ceil(rows per head slot / 64)
+  int head_slots;  // absorbed: 1; materialised: H
+  int n_items;     // n_splits * head_slots * row_tiles
+  size_t ws_o_floats, ws_ml_floats;
+  size_t ws_bytes;
+};
+
+struct AbsorbedLaunch {
+  int r, rope, v_dim, H, B, L;
+  const void* q_lat; const void* q_pe; const void* c_kv; const void* k_pe; const void* w_uv;
+  const int32_t* off_dev;
+  float scale;
+  float* ws_o; float* ws_ml;
+  SplitPlan plan;
+};
+
+struct MaterializedLaunch {
+  int n, rope, v_dim, H, B, L;
+  const void* q_nope; const void* q_pe; const void* k; const void* v;
+  const int32_t* off_dev;
+  float scale;
+  float* ws_o; float* ws_ml;
+  SplitPlan plan;
+};
+
+// attn.hip
+hipError_t absorbed_attn_bf16(const AbsorbedLaunch& q, hipStream_t st);
+hipError_t materialized_attn_bf16(const MaterializedLaunch& q, hipStream_t st);
+bool materialized_bf16_supported(int n, int rope, int v);
+hipError_t attn_f32(const AbsorbedLaunch* qa, const MaterializedLaunch* qm, hipStream_t st);
+hipError_t combine_materialized(const MaterializedLaunch& q, float* out, hipStream_t st);
+hipError_t combine_upproj(const AbsorbedLaunch& q, mla_dtype_t dt, float* out, hipStream_t st);
+
+// gemm.hip
+hipError_t fold_query(mla_dtype_t dt, int rows, int H, int n, int r, const void* q_nope, const void* w_uk,
+                      void* q_lat, hipStream_t st);
+hipError_t materialize_kv(mla_dtype_t dt, long long T, int H, int r, int n, int v, int rope, const void* c_kv,
+                          const void* k_pe, const void* w_uk, const void* w_uv, void* k, void* vout,
+                          hipStream_t st);
+
+}  // namespace mla

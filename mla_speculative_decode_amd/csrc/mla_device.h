@@ -1,0 +1,128 @@
+// mla_device.h -- device-side building blocks for the gfx950 (CDNA4) kernels
+// of libmla: vector types, MFMA wrappers, bfloat16 conversion, LDS swizzles,
+// an 8x8 bf16 register transpose, XCD-aware work mapping and the split-KV
+// plan decode shared by the attention and combine kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;   // CDNA wavefront width
+constexpr int kXcds = 8;    // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// ---- MFMA (bf16 inputs, fp32 accumulate) --------------------------------
+// 32x32x16: A lane l holds row l%32, k = 8*(l/32)+j; B lane l holds col l%32,
+// same k; C lane l holds col l%32, rows 8*(i/4) + 4*(l/32) + i%4, i < 16.
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// 16x16x32: A lane l holds row l%16, k = 8*(l/16)+j; B lane l holds col l%16,
+// same k; C lane l holds col l%16, rows 4*(l/16) + i, i < 4.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---- bfloat16 ----------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// Round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// ---- memory --------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// 8x8 transpose of bf16 held as 8 rows of 16 bytes: in[r] holds elements
+// (r, 0..7); out[c] receives elements (0..7, c).  32 byte-permutes.
+__device__ __forceinline__ void transpose8x8_bf16(const u32x4 in[8], u32x4 out[8]) {
+  // out[c] dword q = (in[2q] element c, in[2q+1] element c); element c of a
+  // row sits in dword c/2, low half when c is even.
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t a = in[2 * q][c >> 1], b = in[2 * q + 1][c >> 1];
+      // v_perm_b32 selector: bytes of (b:a); pick the c-even/odd half of each.
+      out[c][q] = (c & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
+                          : __builtin_amdgcn_perm(b, a, 0x05040100u);
+    }
+  }
+}
+
+// ---- work mapping ----------------------------------------------------------
+// Workgroups are dispatched round-robin over the XCDs (block id b runs on XCD
+// b % 8).  Give each XCD a contiguous range of work items so that items that
+// share data (the row tiles of one KV split) share that XCD's L2.
+__device__ __forceinline__ int xcd_item(int bid, int n_items) {
+  int per = (n_items + kXcds - 1) / kXcds;
+  return (bid % kXcds) * per + bid / kXcds;
+}
+
+// Split-KV plan: sequence b (Kv_b = off[b+1]-off[b] positions) is cut into
+// S_b = ceil(Kv_b / chunk) splits; splits are numbered globally in sequence
+// order.  decode_split maps a global split g to (b, s); every lane of the
+// wave computes the same answer.  Kv_b >= 1 for every b.
+struct SplitPos { int b, s, g0; };
+__device__ __forceinline__ SplitPos decode_split(int g, const int32_t* __restrict__ off, int B, int chunk) {
+  const int lane = threadIdx.x % kWave;
+  int base = 0;
+  for (int b0 = 0; b0 < B; b0 += kWave) {
+    int b = b0 + lane;
+    int sb = 0;
+    if (b < B) sb = (off[b + 1] - off[b] + chunk - 1) / chunk;
+    // inclusive prefix sum over the wave
+    int incl = sb;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      int t = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += t;
+    }
+    int excl = incl - sb;
+    bool mine = (b < B) && (g >= base + excl) && (g < base + incl);
+    unsigned long long m = __ballot(mine);
+    if (m) {
+      int src = __ffsll((long long)m) - 1;
+      int ex = __shfl(excl, src, kWave);
+      SplitPos p;
+      p.b = b0 + src;
+      p.g0 = base + ex;
+      p.s = g - p.g0;
+      return p;
+    }
+    base += __shfl(incl, kWave - 1, kWave);
+  }
+  SplitPos p{B, 0, base};  // unreachable for a valid g
+  return p;
+}
+
+// First global split index of sequence b and its split count.
+__device__ __forceinline__ void seq_splits(int b, const int32_t* __restrict__ off, int chunk, int* g0, int* sb) {
+  const int lane = threadIdx.x % kWave;
+  int acc = 0;
+  for (int b0 = 0; b0 < b; b0 += kWave) {
+    int bb = b0 + lane;
+    int s = 0;
+    if (bb < b) s = (off[bb + 1] - off[bb] + chunk - 1) / chunk;
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d, kWave);
+    acc += s;
+  }
+  *g0 = acc;
+  *sb = (off[b + 1] - off[b] + chunk - 1) / chunk;
+}
+
+}  // namespace mla
