@@ -121,7 +121,7 @@ int mla_select_path(const mla_geom* g, int64_t L, int64_t T, int32_t* path_out,
  *   w_uk    device, [H, n, r],   dtype dt
  *   q_lat   device, [rows, H, r], dtype dt (bf16: accumulated in float32,
  *           rounded to nearest-even once)
- * Supported: n % 64 == 0, n <= 256, r % 128 == 0 (bf16); any n, r >= 1 (f32).
+ * Supported: n % 32 == 0, n <= 512, r % 64 == 0 (bf16); any n, r >= 1 (f32).
  */
 int mla_fold_query(const mla_geom* g, mla_dtype dt, int64_t rows, const void* q_nope,
                    const void* w_uk, void* q_lat, void* stream);
@@ -158,7 +158,7 @@ int mla_absorbed_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int3
  *   out     device, [B, L, H, v], float32
  *   workspace / workspace_bytes   device scratch of at least
  *           mla_absorbed_workspace_size() bytes, 256-byte aligned
- * Supported (bf16): r == 512, rope in {0, 64}, v % 64 == 0, v <= 512.
+ * Supported (bf16): r == 512, rope in {0, 64}, v % 64 == 0.
  * Supported (f32): r <= 1024, r + rope <= 1152, v <= 1024.
  * The result is deterministic: no floating-point atomics are used.
  */

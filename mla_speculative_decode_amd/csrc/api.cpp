@@ -45,7 +45,7 @@ int check_offsets(int32_t B, int32_t L, const int32_t* off) {
 // sequence and about four per unit across a batch (variable lengths need the
 // slack to balance), never splitting finer than one 64-position tile.
 int make_plan(int32_t B, int32_t L, int32_t H, const int32_t* off, int rows_slot, int head_slots, int DV,
-              SplitPlan* p) {
+              int o_elem_bytes, SplitPlan* p) {
   const int64_t row_tiles = (rows_slot + kTile - 1) / kTile;
   int64_t total_tiles = 0;
   for (int32_t b = 0; b < B; ++b) total_tiles += (off[b + 1] - off[b] + kTile - 1) / kTile;
@@ -65,15 +65,23 @@ int make_plan(int32_t B, int32_t L, int32_t H, const int32_t* off, int rows_slot
   p->head_slots = head_slots;
   p->n_items = (int)items;
   const size_t rows_total = (size_t)L * H;
-  p->ws_o_floats = (size_t)splits * rows_total * DV;
+  p->ws_o_bytes = (size_t)splits * rows_total * DV * o_elem_bytes;
   p->ws_ml_floats = (size_t)splits * rows_total * 2;
-  p->ws_bytes = align_up(p->ws_o_floats * 4) + align_up(p->ws_ml_floats * 4);
+  p->ws_lat_bytes = 0;
+  p->ws_bytes = align_up(p->ws_o_bytes) + align_up(p->ws_ml_floats * 4);
   return MLA_OK;
+}
+
+// The bf16 merge keeps the merged latent (float32 [B*L*H, r]) between its two launches.
+void add_latent(SplitPlan* p, int32_t B, int32_t L, const mla_geom* g, mla_dtype dt) {
+  if (dt != MLA_BF16) return;
+  p->ws_lat_bytes = (size_t)B * L * g->heads * g->r * 4;
+  p->ws_bytes += align_up(p->ws_lat_bytes);
 }
 
 int absorbed_supported(const mla_geom* g, mla_dtype dt) {
   if (dt == MLA_BF16) {
-    if (g->r != 512 || !(g->rope == 0 || g->rope == 64) || g->v % 64 != 0 || g->v > 512)
+    if (g->r != 512 || !(g->rope == 0 || g->rope == 64) || g->v % 64 != 0)
       return MLA_E_UNSUPPORTED;
   } else {
     if (g->r > 1024 || g->r + g->rope > 1152 || g->v > 1024) return MLA_E_UNSUPPORTED;
@@ -138,7 +146,7 @@ int mla_fold_query(const mla_geom* g, mla_dtype dt, int64_t rows, const void* q_
   if (!dtype_ok(dt)) return MLA_E_UNSUPPORTED;
   if (rows < 1 || g->n < 1 || rows * g->heads > INT32_MAX) return MLA_E_SHAPE;
   if (!q_nope || !w_uk || !q_lat) return MLA_E_NULL;
-  if (dt == MLA_BF16 && (g->n % 64 != 0 || g->n > 256 || g->r % 128 != 0)) return MLA_E_UNSUPPORTED;
+  if (dt == MLA_BF16 && (g->n % 32 != 0 || g->n > 512 || g->r % 64 != 0)) return MLA_E_UNSUPPORTED;
   return hip_status(fold_query(dt == MLA_BF16 ? kBF16 : kF32, (int)rows, g->heads, g->n, g->r, q_nope, w_uk,
                                q_lat, (hipStream_t)stream));
 }
@@ -153,7 +161,8 @@ int mla_absorbed_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int3
   if ((int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
   if ((st = absorbed_supported(g, dt))) return st;
   SplitPlan p{};
-  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L * g->heads, 1, g->r, &p))) return st;
+  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L * g->heads, 1, g->r, dt == MLA_BF16 ? 2 : 4, &p))) return st;
+  add_latent(&p, B, L, g, dt);
   *bytes_out = p.ws_bytes;
   return MLA_OK;
 }
@@ -180,13 +189,16 @@ int absorbed_prepare(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, cons
   if (need_merge && (!w_uv || !out)) return MLA_E_NULL;
   if ((st = absorbed_supported(g, dt))) return st;
   SplitPlan p{};
-  if ((st = make_plan(B, L, g->heads, off_h, L * g->heads, 1, g->r, &p))) return st;
+  if ((st = make_plan(B, L, g->heads, off_h, L * g->heads, 1, g->r, dt == MLA_BF16 ? 2 : 4, &p))) return st;
+  add_latent(&p, B, L, g, dt);
   if (!workspace || workspace_bytes < p.ws_bytes) return MLA_E_WORKSPACE;
   q->r = g->r; q->rope = g->rope; q->v_dim = g->v; q->H = g->heads; q->B = B; q->L = L;
   q->q_lat = q_lat; q->q_pe = q_pe; q->c_kv = c_kv; q->k_pe = k_pe; q->w_uv = w_uv;
   q->off_dev = off_d; q->scale = scale;
-  q->ws_o = (float*)workspace;
-  q->ws_ml = (float*)((char*)workspace + align_up(p.ws_o_floats * 4));
+  q->ws_o = workspace;
+  q->ws_ml = (float*)((char*)workspace + align_up(p.ws_o_bytes));
+  q->ws_lat = p.ws_lat_bytes ? (float*)((char*)workspace + align_up(p.ws_o_bytes) + align_up(p.ws_ml_floats * 4))
+                             : nullptr;
   q->plan = p;
   return MLA_OK;
 }
@@ -255,7 +267,7 @@ int mla_materialized_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, 
   if ((int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
   if ((st = materialized_supported(g, dt))) return st;
   SplitPlan p{};
-  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L, g->heads, g->v, &p))) return st;
+  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L, g->heads, g->v, 4, &p))) return st;
   *bytes_out = p.ws_bytes;
   return MLA_OK;
 }
@@ -274,19 +286,19 @@ int mla_materialized_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32
   if (g->n < 1) return MLA_E_SHAPE;
   if ((st = materialized_supported(g, dt))) return st;
   SplitPlan p{};
-  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L, g->heads, g->v, &p))) return st;
+  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L, g->heads, g->v, 4, &p))) return st;
   if (!workspace || workspace_bytes < p.ws_bytes) return MLA_E_WORKSPACE;
   MaterializedLaunch q{};
   q.n = g->n; q.rope = g->rope; q.v_dim = g->v; q.H = g->heads; q.B = B; q.L = L;
   q.q_nope = q_nope; q.q_pe = q_pe; q.k = k; q.v = v;
   q.off_dev = kv_offsets_dev; q.scale = scale;
-  q.ws_o = (float*)workspace;
-  q.ws_ml = (float*)((char*)workspace + align_up(p.ws_o_floats * 4));
+  q.ws_o = workspace;
+  q.ws_ml = (float*)((char*)workspace + align_up(p.ws_o_bytes));
   q.plan = p;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = (dt == MLA_BF16) ? materialized_attn_bf16(q, s) : attn_f32(nullptr, &q, s);
   if (e != hipSuccess) return MLA_E_HIP;
-  return hip_status(combine_materialized(q, out, s));
+  return hip_status(combine_materialized(q, dt == MLA_BF16 ? kBF16 : kF32, out, s));
 }
 
 }  // extern "C"

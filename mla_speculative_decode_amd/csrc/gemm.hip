@@ -9,11 +9,12 @@
 //
 // bf16 uses MFMA with fp32 accumulation.  MFMA operands need the contraction
 // index contiguous per lane; W_UK [H, n, r] (fold contracts over n) and W_UV
-// [H, r, v] (expand contracts over r) store it strided, so those tiles are
-// transposed in registers (8x8 bf16 blocks) on their way into LDS.  The fold
-// is a small-M product (M = B*L rows per head): each workgroup reads its
-// weight tile once for up to 64 rows, the weight stream being the cost.
-// float32 uses plain VALU loops.
+// [H, r, v] (expand and up-projection contract over r) store it strided: the
+// small-M GEMM reads those fragments transposed from LDS (ds_read_b64_tr_b16),
+// the expand transposes its W_UV tiles in registers (8x8 bf16 blocks) on the
+// way into LDS.  The fold is a small-M product (M = B*L rows per head): each
+// workgroup reads its weight tile once for up to 64 rows, the weight stream
+// being the cost.  float32 uses plain VALU loops.
 
 #include "mla_device.h"
 #include "internal.h"
@@ -21,79 +22,151 @@
 namespace mla {
 
 // ---------------------------------------------------------------------------
-// fold, bf16: workgroup = (head, 128 latent columns, 64 rows); wave w owns
-// columns 32w..32w+31 as two 16x16 MFMA blocks over four 16-row blocks.
+// Small-M batched GEMM per head, bf16 MFMA:  C[h][m, :] = A[h][m, :] . W[h]
+// with W[h] row-major [K x N] (N contiguous).  Used for the fold (A = q_nope,
+// W = W_UK[h], C = q_lat in bf16) and for the up-projection of the merged
+// latent (A = o_lat in float32, taken as a bf16 pair hi + lo, W = W_UV[h],
+// C = out in float32).  Workgroup = (head, 64 output columns, MT rows): the W
+// tile [K x 64] and the A tile are loaded into registers with 16-byte loads,
+// written to LDS (padded rows), and multiplied with 16x16x32 MFMAs, W
+// fragments read transposed from the row-major tile (ds_read_b64_tr_b16).
+// Each wave owns 16 output columns; the weight stream is read once per
+// MT rows.
 // ---------------------------------------------------------------------------
-constexpr int kFoldMaxN = 256;
-
-__global__ __launch_bounds__(256) void fold_bf16_kernel(const uint16_t* __restrict__ q_nope,
-                                                        const uint16_t* __restrict__ w_uk,
-                                                        uint16_t* __restrict__ q_lat, int M, int H, int n, int r,
-                                                        int n_items) {
-  __shared__ __attribute__((aligned(16))) uint8_t wt[128 * kFoldMaxN * 2];  // [col][k], k contiguous
+// A_F32: A is float32 (hi/lo split); C_BF16: C stored as bf16.  MT rows per workgroup.
+template <bool A_F32, bool C_BF16, int MT, int KMAX>
+__global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
+  constexpr int WRB = 64 * 2 + 16;          // W row: 64 bf16 + pad
+  constexpr int ARB = KMAX * 2 + 16;        // A row: K bf16 + pad
+  constexpr int NA = A_F32 ? 2 : 1;         // A tiles (hi, lo)
+  constexpr int RB = MT / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t wt[KMAX * WRB];
+  __shared__ __attribute__((aligned(16))) uint8_t at[NA][MT * ARB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int item = xcd_item(blockIdx.x, n_items);
-  if (item >= n_items) return;
-  const int CT = r / 128, MT = (M + 63) / 64;
-  const int mt = item % MT;
-  const int tmp = item / MT;
+  const int item = xcd_item(blockIdx.x, g.n_items);
+  if (item >= g.n_items) return;
+  const int CT = g.N / 64, MTS = (g.M + MT - 1) / MT;
+  const int mt = item % MTS;
+  const int tmp = item / MTS;
   const int ct = tmp % CT, h = tmp / CT;
-  const int NKG = n / 8;                 // k groups of 8
-  const int rowb = n * 2;                // bytes per wt row
+  const int K = g.K, m0 = mt * MT;
 
-  const uint16_t* wsrc = w_uk + (long long)h * n * r + ct * 128;
-  for (int U = tid; U < NKG * 16; U += 256) {
-    const int kg = U % NKG, cc = U / NKG;
-    u32x4 in[8], tr[8];
+  // ---- W tile: K rows x 64 columns (K * 8 chunks of 16 B) --------------------
+  const uint16_t* wsrc = g.W + (long long)h * K * g.N + ct * 64;
+  constexpr int WCH_T = KMAX * 8 / 256;     // chunks per thread at K = KMAX
+  u32x4 wst[WCH_T];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) in[j] = ld16(wsrc + (long long)(8 * kg + j) * r + 8 * cc);
-    transpose8x8_bf16(in, tr);
+  for (int x = 0; x < WCH_T; ++x) {
+    const int C = tid + 256 * x;
+    if (C < K * 8) wst[x] = ld16(wsrc + (long long)(C >> 3) * g.N + 8 * (C & 7));
+  }
+  // ---- A tile: MT rows x K ------------------------------------------------------
+  // bf16: 8 elements per chunk; float32: 4 elements per chunk (two chunks -> 8 bf16 hi + 8 lo)
+  constexpr int AE = A_F32 ? 4 : 8;         // elements per 16-byte chunk
+  constexpr int ACH_T = MT * KMAX / AE / 256;
+  u32x4 ast[ACH_T];
+  const int KC = K / AE;                    // chunks per A row
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int col = 8 * cc + e;
-      st16(wt + col * rowb + ((kg ^ (col & 7)) * 16), tr[e]);
+  for (int x = 0; x < ACH_T; ++x) {
+    const int C = tid + 256 * x;
+    const int r = C / KC, c = C % KC;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (C < MT * KC && m0 + r < g.M) {
+      const char* a = reinterpret_cast<const char*>(g.A) +
+                      ((long long)h * g.a_head + (long long)(m0 + r) * g.a_row + (long long)c * AE) * (A_F32 ? 4 : 2);
+      v = ld16(a);
+    }
+    ast[x] = v;
+  }
+#pragma unroll
+  for (int x = 0; x < WCH_T; ++x) {
+    const int C = tid + 256 * x;
+    if (C < K * 8) st16(wt + (C >> 3) * WRB + 16 * (C & 7), wst[x]);
+  }
+#pragma unroll
+  for (int x = 0; x < ACH_T; ++x) {
+    const int C = tid + 256 * x;
+    const int r = C / KC, c = C % KC;
+    if (C < MT * KC) {
+      if (A_F32) {
+        const f32x4 f = __builtin_bit_cast(f32x4, ast[x]);
+        u32x2 hi, lo;
+        hi[0] = pack_bf16(f[0], f[1]);
+        hi[1] = pack_bf16(f[2], f[3]);
+        lo[0] = pack_bf16(f[0] - bf16_lo(hi[0]), f[1] - bf16_hi(hi[0]));
+        lo[1] = pack_bf16(f[2] - bf16_lo(hi[1]), f[3] - bf16_hi(hi[1]));
+        *reinterpret_cast<u32x2*>(at[0] + r * ARB + c * 8) = hi;
+        *reinterpret_cast<u32x2*>(at[NA - 1] + r * ARB + c * 8) = lo;
+      } else {
+        st16(at[0] + r * ARB + c * 16, ast[x]);
+      }
     }
   }
   __syncthreads();
 
+  // ---- MFMA: wave w -> columns 16w..16w+15 ------------------------------------
   const int r16 = lane & 15, kq = lane >> 4;
-  const int m0 = mt * 64;
-  f32x4 acc[4][2];
+  const int s16 = lane & 15, G = lane >> 4;
+  const uint8_t* wb = wt + (8 * G + (s16 >> 2)) * WRB + (16 * w + 4 * (s16 & 3)) * 2;
+  f32x4 acc[RB];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nrb = min(RB, (g.M - m0 + 15) / 16);
+  for (int ks = 0; ks < K / 32; ++ks) {
+    u32x4 bv;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kc = 0; kc < n / 32; ++kc) {
-    u32x4 bv[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int col = 32 * w + 16 * cb + r16;
-      const int ch = 4 * kc + kq;
-      bv[cb] = *reinterpret_cast<const u32x4*>(wt + col * rowb + ((ch ^ (col & 7)) * 16));
+    for (int ld = 0; ld < 2; ++ld) {
+      const v4i16 rr = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(wb + (32 * ks + 4 * ld) * WRB));
+      const u32x2 r2 = __builtin_bit_cast(u32x2, rr);
+      bv[2 * ld] = r2[0];
+      bv[2 * ld + 1] = r2[1];
     }
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      if (m0 + 16 * rb >= M) break;
-      const int m = m0 + 16 * rb + r16;
-      u32x4 a = {0u, 0u, 0u, 0u};
-      if (m < M) a = ld16(q_nope + ((long long)m * H + h) * n + 32 * kc + 8 * kq);
+    for (int rb = 0; rb < RB; ++rb) {
+      if (rb < nrb) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma16(a, bv[cb], acc[rb][cb]);
-    }
-  }
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int m = m0 + 16 * rb + 4 * kq + x;
-        if (m < M) {
-          const int c = ct * 128 + 32 * w + 16 * cb + r16;
-          __bf16 o = (__bf16)acc[rb][cb][x];
-          q_lat[((long long)m * H + h) * r + c] = __builtin_bit_cast(uint16_t, o);
+        for (int t = 0; t < NA; ++t) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(at[t] + (16 * rb + r16) * ARB + (32 * ks + 8 * kq) * 2);
+          acc[rb] = mfma16(a, bv, acc[rb]);
         }
       }
+    }
+  }
+  // C layout: lane holds column 16w + lane%16, rows 4*(lane/16) + x
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int m = m0 + 16 * rb + 4 * kq + x;
+      if (m < g.M) {
+        const long long o = (long long)h * g.c_head + (long long)m * g.c_row + ct * 64 + 16 * w + r16;
+        if (C_BF16) reinterpret_cast<uint16_t*>(g.C)[o] = __builtin_bit_cast(uint16_t, (__bf16)acc[rb][x]);
+        else reinterpret_cast<float*>(g.C)[o] = acc[rb][x];
+      }
+    }
+}
+
+hipError_t gemm_smallm(bool a_f32, bool c_bf16, const GemmArgs& a0, hipStream_t st) {
+  GemmArgs a = a0;
+  if (a.K % 32 != 0 || a.K > 512 || a.N % 64 != 0) return hipErrorInvalidValue;
+  // rows per workgroup: 16 for small M; otherwise 64 (bf16 A) or 32 (float32 A, whose hi/lo
+  // tiles take twice the LDS)
+  const int MT = a.M <= 16 ? 16 : (a_f32 ? 32 : 64);
+  a.n_items = a.H * (a.N / 64) * ((a.M + MT - 1) / MT);
+  const unsigned grid = (unsigned)(((a.n_items + kXcds - 1) / kXcds) * kXcds);
+  // LDS and staging registers are sized by KMAX: small K keeps several workgroups per CU
+  const int KM = a.K <= 128 ? 128 : (a.K <= 256 ? 256 : 512);
+#define MLA_GEMM(AF, CB, M_, KM_)                                                                   \
+  if (a_f32 == AF && c_bf16 == CB && MT == M_ && KM == KM_) {                                       \
+    hipLaunchKernelGGL((gemm_smallm_kernel<AF, CB, M_, KM_>), dim3(grid), dim3(256), 0, st, a);     \
+    return hipGetLastError();                                                                       \
+  }
+  MLA_GEMM(false, true, 16, 128) MLA_GEMM(false, true, 64, 128) MLA_GEMM(false, true, 16, 256)
+  MLA_GEMM(false, true, 64, 256) MLA_GEMM(false, true, 16, 512) MLA_GEMM(false, true, 64, 512)
+  MLA_GEMM(true, false, 16, 512) MLA_GEMM(true, false, 32, 512)
+#undef MLA_GEMM
+  return hipErrorInvalidValue;
 }
 
 __global__ __launch_bounds__(256) void fold_f32_kernel(const float* __restrict__ q_nope, const float* __restrict__ w_uk,
@@ -113,17 +186,18 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const float* __restrict__
 hipError_t fold_query(mla_dtype_t dt, int rows, int H, int n, int r, const void* q_nope, const void* w_uk,
                       void* q_lat, hipStream_t st) {
   if (dt == kBF16) {
-    if (n % 64 != 0 || n > kFoldMaxN || r % 128 != 0) return hipErrorInvalidValue;
-    const int n_items = H * (r / 128) * ((rows + 63) / 64);
-    const unsigned grid = (unsigned)(((n_items + kXcds - 1) / kXcds) * kXcds);
-    hipLaunchKernelGGL(fold_bf16_kernel, dim3(grid), dim3(256), 0, st, (const uint16_t*)q_nope,
-                       (const uint16_t*)w_uk, (uint16_t*)q_lat, rows, H, n, r, n_items);
-  } else {
-    const long long total = (long long)rows * H * r;
-    const long long blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(fold_f32_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, st,
-                       (const float*)q_nope, (const float*)w_uk, (float*)q_lat, total, H, n, r);
+    if (n % 32 != 0 || n > 512 || r % 64 != 0) return hipErrorInvalidValue;
+    GemmArgs a{};
+    a.A = q_nope; a.a_row = (long long)H * n; a.a_head = n;
+    a.W = (const uint16_t*)w_uk;
+    a.C = q_lat; a.c_row = (long long)H * r; a.c_head = r;
+    a.M = rows; a.K = n; a.N = r; a.H = H;
+    return gemm_smallm(false, true, a, st);
   }
+  const long long total = (long long)rows * H * r;
+  const long long blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(fold_f32_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, st,
+                     (const float*)q_nope, (const float*)w_uk, (float*)q_lat, total, H, n, r);
   return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;   // CDNA wavefront width
 constexpr int kXcds = 8;    // MI355X: 8 accelerator complex dies, 32 CUs each
@@ -121,6 +122,15 @@ __device__ __forceinline__ void seq_splits(int b, const int32_t* __restrict__ of
     for (int d = kWave / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d, kWave);
     acc += s;
   }
+  *g0 = acc;
+  *sb = (off[b + 1] - off[b] + chunk - 1) / chunk;
+}
+
+// Same as seq_splits, computed by one thread alone (no wave collectives), for
+// callers whose lanes belong to different sequences.
+__device__ __forceinline__ void seq_splits_lane(int b, const int32_t* __restrict__ off, int chunk, int* g0, int* sb) {
+  int acc = 0;
+  for (int bb = 0; bb < b; ++bb) acc += (off[bb + 1] - off[bb] + chunk - 1) / chunk;
   *g0 = acc;
   *sb = (off[b + 1] - off[b] + chunk - 1) / chunk;
 }

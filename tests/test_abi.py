@@ -95,8 +95,9 @@ def test_workspace_size_and_validation(lib):
     sz = ctypes.c_size_t()
     off = _offs([0, 8192])
     assert lib.mla_absorbed_workspace_size(ctypes.byref(g), 1, 1, 8, off, ctypes.byref(sz)) == 0
-    # 16 splits of 512 positions x 1024 rows x (512 + 2) floats
-    assert sz.value == 16 * 1024 * 512 * 4 + 16 * 1024 * 2 * 4
+    # 16 splits of 512 positions x 1024 rows: bf16 partial sums (512) + float32 (max, sum),
+    # plus the float32 merged latent of the 1024 rows
+    assert sz.value == 16 * 1024 * 512 * 2 + 16 * 1024 * 2 * 4 + 1024 * 512 * 4
     assert lib.mla_absorbed_workspace_size(ctypes.byref(g), 1, 1, 8, None, ctypes.byref(sz)) == -1
     assert lib.mla_absorbed_workspace_size(ctypes.byref(g), 1, 1, 8, off, None) == -1
     assert lib.mla_absorbed_workspace_size(ctypes.byref(g), 1, 0, 8, off, ctypes.byref(sz)) == -2
@@ -124,7 +125,7 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.mla_fold_query(None, 1, 4, FAKE, FAKE, FAKE, None) == -1
     assert lib.mla_fold_query(ctypes.byref(g), 1, 0, FAKE, FAKE, FAKE, None) == -2
     assert lib.mla_fold_query(ctypes.byref(g), 1, 4, None, FAKE, FAKE, None) == -1
-    assert lib.mla_fold_query(ctypes.byref(Geom(512, 96, 128, 64, 16)), 1, 4, FAKE, FAKE, FAKE, None) == -3
+    assert lib.mla_fold_query(ctypes.byref(Geom(512, 80, 128, 64, 16)), 1, 4, FAKE, FAKE, FAKE, None) == -3
     # absorbed attention
     args = lambda ws, wsb, **kw: [ctypes.byref(kw.get("g", g)), kw.get("dt", 1), kw.get("B", 1), kw.get("L", 4),
                                   kw.get("ql", FAKE), FAKE, FAKE, FAKE, kw.get("offh", off), FAKE, FAKE, f,
