@@ -36,6 +36,25 @@ METRIC = "absorbed MLA verify µs/call + latent-cache HBM GB/s (L=8, Kv=8192, H=
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
+# HBM traffic of the split kernel per launch, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# (KiB per dispatch) scaled by what the same counters read for a plain 256 MiB device copy
+# (FETCH x2.00, WRITE x1.00); valid only for the kernel source it was measured on.
+SPLIT_TRAFFIC = {"source_sha256": "9f13d2572987440632198bbbc3391764f658073e51ea798f59a3021a1f4634b0",
+                 "fetch_kib": 10027.2, "write_kib": 17792.0, "fetch_factor": 2.0, "write_factor": 1.0}
+KERNEL_SOURCES = ("mla_speculative_decode_amd/csrc/attn.hip", "mla_speculative_decode_amd/csrc/mla_device.h")
+
+
+def split_traffic_bytes():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    t = SPLIT_TRAFFIC
+    if h.hexdigest() != t["source_sha256"]:
+        return None   # the kernel changed since the counters were taken
+    return round(1024 * (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]))
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -47,6 +66,8 @@ def parse():
                     help="total bytes of rotated input sets (cold protocol); 0 = warm only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -64,6 +85,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
+        return
     lib = _lib.load()
     blib = ctypes.CDLL(os.path.join(ROOT, "mla_speculative_decode_amd", "libmla_bench.so"))
     blib.mlab_absorbed_run.restype = ctypes.c_int
@@ -145,7 +175,7 @@ def main():
         "warm_per_launch_us": {"fold": round(warm[1], 3), "splits": round(warm[2], 3), "merge": round(warm[3], 3)},
         "roofline": {"kernel": "attn_bf16_kernel (mla_absorbed_splits)", "bound": "mfma",
                      "achieved": round(achieved_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4), "traffic": split_traffic_bytes()},
         "wall_s": round(wall, 3),
     }
 
