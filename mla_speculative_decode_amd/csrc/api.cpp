@@ -67,16 +67,8 @@ int make_plan(int32_t B, int32_t L, int32_t H, const int32_t* off, int rows_slot
   const size_t rows_total = (size_t)L * H;
   p->ws_o_bytes = (size_t)splits * rows_total * DV * o_elem_bytes;
   p->ws_ml_floats = (size_t)splits * rows_total * 2;
-  p->ws_lat_bytes = 0;
   p->ws_bytes = align_up(p->ws_o_bytes) + align_up(p->ws_ml_floats * 4);
   return MLA_OK;
-}
-
-// The bf16 merge keeps the merged latent (float32 [B*L*H, r]) between its two launches.
-void add_latent(SplitPlan* p, int32_t B, int32_t L, const mla_geom* g, mla_dtype dt) {
-  if (dt != MLA_BF16) return;
-  p->ws_lat_bytes = (size_t)B * L * g->heads * g->r * 4;
-  p->ws_bytes += align_up(p->ws_lat_bytes);
 }
 
 int absorbed_supported(const mla_geom* g, mla_dtype dt) {
@@ -162,7 +154,6 @@ int mla_absorbed_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int3
   if ((st = absorbed_supported(g, dt))) return st;
   SplitPlan p{};
   if ((st = make_plan(B, L, g->heads, kv_offsets_host, L * g->heads, 1, g->r, dt == MLA_BF16 ? 2 : 4, &p))) return st;
-  add_latent(&p, B, L, g, dt);
   *bytes_out = p.ws_bytes;
   return MLA_OK;
 }
@@ -190,15 +181,13 @@ int absorbed_prepare(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, cons
   if ((st = absorbed_supported(g, dt))) return st;
   SplitPlan p{};
   if ((st = make_plan(B, L, g->heads, off_h, L * g->heads, 1, g->r, dt == MLA_BF16 ? 2 : 4, &p))) return st;
-  add_latent(&p, B, L, g, dt);
   if (!workspace || workspace_bytes < p.ws_bytes) return MLA_E_WORKSPACE;
   q->r = g->r; q->rope = g->rope; q->v_dim = g->v; q->H = g->heads; q->B = B; q->L = L;
   q->q_lat = q_lat; q->q_pe = q_pe; q->c_kv = c_kv; q->k_pe = k_pe; q->w_uv = w_uv;
   q->off_dev = off_d; q->scale = scale;
+  q->off0 = off_h[0]; q->kv1 = off_h[1] - off_h[0];
   q->ws_o = workspace;
   q->ws_ml = (float*)((char*)workspace + align_up(p.ws_o_bytes));
-  q->ws_lat = p.ws_lat_bytes ? (float*)((char*)workspace + align_up(p.ws_o_bytes) + align_up(p.ws_ml_floats * 4))
-                             : nullptr;
   q->plan = p;
   return MLA_OK;
 }
@@ -292,6 +281,7 @@ int mla_materialized_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32
   q.n = g->n; q.rope = g->rope; q.v_dim = g->v; q.H = g->heads; q.B = B; q.L = L;
   q.q_nope = q_nope; q.q_pe = q_pe; q.k = k; q.v = v;
   q.off_dev = kv_offsets_dev; q.scale = scale;
+  q.off0 = kv_offsets_host[0]; q.kv1 = kv_offsets_host[1] - kv_offsets_host[0];
   q.ws_o = workspace;
   q.ws_ml = (float*)((char*)workspace + align_up(p.ws_o_bytes));
   q.plan = p;

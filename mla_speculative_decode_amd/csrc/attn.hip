@@ -29,6 +29,7 @@
 // and small exchange arrays; the next tile is prefetched into registers and
 // written to kt while PV runs, and to vt right after it.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "mla_device.h"
@@ -46,6 +47,7 @@ struct AttnArgs {
   const uint16_t* vv;   // value source, row for position p at vv + p*vv_ks + head*vv_hs
   long long ka_ks, ka_hs, vv_ks, vv_hs;
   const int32_t* off;   // [B+1] device offsets
+  int off0, kv1;        // B == 1: off[0] and off[1] - off[0]
   void* ws_o;           // [G][rows_total][DV] unnormalised partial sums: bf16 (absorbed), float32 (materialised)
   float* ws_ml;         // [G][rows_total][2]
   int B, L, H;
@@ -101,7 +103,6 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t pl[BM * PRB];
   __shared__ float red[2 * BM];
   __shared__ __attribute__((aligned(16))) float al[BM];
-  __shared__ __attribute__((aligned(16))) int rflag[4];   // per score wave: some row rescaled this tile
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
@@ -112,15 +113,16 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   const int hs = tmp % p.head_slots;
   const int g = tmp / p.head_slots;
   // the split is the same for the whole workgroup: keep its bounds in scalar registers
-  int b = 0, ps = g;
+  // (one sequence: its start and length come from the host, no load of the offsets)
+  int b = 0, ps = g, off_b = p.off0, Kv = p.kv1;
   if (p.B > 1) {
     const SplitPos sp = decode_split(g, p.off, p.B, p.chunk);
     b = __builtin_amdgcn_readfirstlane(sp.b);
     ps = __builtin_amdgcn_readfirstlane(sp.s);
+    off_b = __builtin_amdgcn_readfirstlane(p.off[b]);
+    Kv = __builtin_amdgcn_readfirstlane(p.off[b + 1]) - off_b;
   }
-  const int off_b = __builtin_amdgcn_readfirstlane(p.off[b]);
   const long long p0 = off_b;
-  const int Kv = __builtin_amdgcn_readfirstlane(p.off[b + 1]) - off_b;
   const int k0 = ps * p.chunk;
   const int k1 = min(Kv, k0 + p.chunk);
   const int idx0 = rt * BM;
@@ -217,9 +219,52 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   {
     const int idx = idx0 + rq;
     const int i = idx / p.hpr;
+    kend = min(k1, Kv - p.L + i + 1);
+  }
+  if (VK) {
+    // absorbed: the rows of the tile are consecutive in q_lat / q_pe.  The query
+    // block goes to the idle tile buffer once (q_lat row = one 1 KB direct load,
+    // q_pe staged through registers), then every wave reads its fragments.
+    // Rows past the last query row repeat it (their results are never stored).
+    constexpr int QP_T = (BM * RCH + 255) / 256;
+    u32x4 qst[QP_T > 0 ? QP_T : 1];
+    const long long qflat0 = (long long)b * p.L * p.H + idx0;   // flat row of tile row 0
+    const uint16_t* qlseq = p.qa + qflat0 * DA + 8 * lane;
+#pragma unroll
+    for (int x = 0; x < BM / 4; ++x) {
+      const int row = wu + 4 * x;
+      __builtin_amdgcn_global_load_lds(qlseq + (unsigned)min(row, nrows - 1) * (unsigned)DA,
+                                       (__attribute__((address_space(3))) void*)(buf1 + row * KRB), 16, 0, 0);
+    }
+#pragma unroll
+    for (int x = 0; x < QP_T; ++x) {
+      const int C = tid + 256 * x;
+      if (C < BM * RCH) {
+        const int row = C / RCH, ch = C % RCH;
+        qst[x] = ld16(p.qb + (qflat0 + min(row, nrows - 1)) * DR + 8 * ch);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int x = 0; x < QP_T; ++x) {
+      const int C = tid + 256 * x;
+      if (C < BM * RCH) {
+        const int row = C / RCH, ch = C % RCH;
+        st16(buf1 + row * KRB + (DA / 8 + ch) * 16, qst[x]);
+      }
+    }
+    store_rope(buf0);
+    __syncthreads();   // query block (and tile 0) in LDS
+    const uint8_t* qrow = buf1 + rq * KRB + 16 * half;
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qrow + 32 * c);
+    // buf1 receives tile 1 after the first barrier of the loop: finish reading it first
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  } else {
+    const int idx = idx0 + rq;
+    const int i = idx / p.hpr;
     const int h = hs + idx % p.hpr;
     const long long flat = ((long long)b * p.L + i) * p.H + h;
-    kend = min(k1, Kv - p.L + i + 1);
 #pragma unroll
     for (int c = 0; c < DCH; ++c) {
       const int dim = 16 * c + 8 * half;
@@ -231,10 +276,10 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       qf[c] = v;
     }
   }
-  if (VK) store_rope(buf0);   // waits for the first tile's loads, which overlapped the query loads
 
   // ---- running state ------------------------------------------------------
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;   // score layout: row rq, this wave's key half
+  float m_all = -INFINITY;                 // reference maximum of row `lane` (same in every wave)
   f32x16 O[2][NCB];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -294,44 +339,60 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       pmax = fmaxf(pmax, s[i]);
     }
     pmax = fmaxf(pmax, __shfl_xor(pmax, 32, 64));
-    if (half == 0) red[wk * BM + rq] = pmax;
-    __syncthreads();  // (B) partial maxima visible
-
-    {
-      // Lazy rescaling: the reference maximum only moves when the tile raises
-      // it by more than 2^8 (or on the first finite score), so P <= 256 and
-      // the O accumulators are rescaled rarely.
-      const float tmax = fmaxf(pmax, red[(1 - wk) * BM + rq]);
-      const bool raise = tmax > m_run + 8.f;
-      const float m_new = raise ? tmax : m_run;
-      const bool none = (m_new == -INFINITY);
-      const float alpha = (raise && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      float psum = 0.f;
+    // Lazy rescaling: the reference maximum of a row only moves when a tile
+    // raises it by more than 2^8 (or on its first finite score), so P <= 256
+    // and the O accumulators are rescaled rarely.  P is computed here against
+    // the current reference and published with the partial maxima; a tile that
+    // raises some row recomputes it below.
+    uint8_t* prow = pl + rq * PRB + 64 * wk + 8 * half;
+    auto write_p = [&](float mref, float* psum) {
+      float ps = 0.f;
+      float e[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[i] = none ? 0.f : __builtin_amdgcn_exp2f(s[i] - m_new);
-        psum += s[i];
+        e[i] = s[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[i] - mref);
+        ps += e[i];
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      uint8_t* prow = pl + rq * PRB + 64 * wk + 8 * half;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         u32x2 v;
-        v[0] = pack_bf16(s[4 * q + 0], s[4 * q + 1]);
-        v[1] = pack_bf16(s[4 * q + 2], s[4 * q + 3]);
+        v[0] = pack_bf16(e[4 * q + 0], e[4 * q + 1]);
+        v[1] = pack_bf16(e[4 * q + 2], e[4 * q + 3]);
         *reinterpret_cast<u32x2*>(prow + 16 * q) = v;
       }
+      *psum = ps;
+    };
+    float psum;
+    write_p(m_run, &psum);
+    if (half == 0) red[wk * BM + rq] = pmax;
+    __syncthreads();  // (B) P and partial maxima visible
+
+    // Every wave decides for all 64 rows (lane = row) from the same partial
+    // maxima with the same arithmetic, so the decision is uniform over the
+    // workgroup and the branch below (with its barrier) is taken by all waves
+    // or by none.
+    const float tm_all = fmaxf(red[lane], red[BM + lane]);
+    const bool raise_all = tm_all > m_all + 8.f;
+    // O needs rescaling only where a row with a finite reference was raised
+    const bool resc = __ballot(raise_all && m_all != -INFINITY) != 0;
+    if (__ballot(raise_all) != 0) {
+      m_all = raise_all ? tm_all : m_all;
+      const float tmax = fmaxf(pmax, red[(1 - wk) * BM + rq]);
+      const bool raise = tmax > m_run + 8.f;
+      const float m_new = raise ? tmax : m_run;
+      const float alpha = (raise && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      write_p(m_new, &psum);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
       if (wk == 0 && half == 0) al[rq] = alpha;
-      const bool resc = __ballot(alpha != 1.f) != 0;
-      if (lane == 0) rflag[w] = resc ? 1 : 0;
+      __syncthreads();  // (C) recomputed P and the rescale factors visible
+    } else {
+      l_run += psum;
     }
-    __syncthreads();  // (C) P and rescale factors visible
 
     // ---- PV: O[64 rows x CPW] for this wave's columns ----------------------
     {
-      const int4 rf = *reinterpret_cast<const int4*>(rflag);
-      if (rf.x | rf.y | rf.z | rf.w) {
+      if (resc) {
         f32x4 alv[2][4];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -397,9 +458,12 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     }
     if (VK) store_rope(nxt);   // the other buffer is not read until barrier (A)
   };
+  // Tiles go in pairs (one per buffer) with no branch between them, so the
+  // accumulators flow straight through the loop; an odd tile count ends with
+  // a tile past the split, whose keys all fail key < kend and add nothing.
   for (int t0 = k0; t0 < k1; t0 += 2 * BN) {
     step(t0, buf0, buf1);
-    if (t0 + BN < k1) step(t0 + BN, buf1, buf0);
+    step(t0 + BN, buf1, buf0);
   }
 
   // ---- epilogue: row sums, partial results ---------------------------------
@@ -616,72 +680,213 @@ __global__ __launch_bounds__(256) void combine_upproj_f32_kernel(const float* __
   }
 }
 
-// Absorbed route, bf16, step 1 of the merge: o_lat[b,i,h,:] = sum_s w_s o_s
-// in float32, from the bf16 partial sums.  One thread per 8 latent columns of
-// one (row, head) pair; the splits are read 8 at a time with independent
-// 16-byte loads.  Step 2 (the W_UV product) is the small-M GEMM of gemm.hip.
-template <int R>
-__global__ __launch_bounds__(256) void merge_latent_kernel(const uint16_t* __restrict__ ws_o, const float* __restrict__ ws_ml,
-                                                           const int32_t* __restrict__ off, int B, int L, int H, int chunk,
-                                                           float* __restrict__ lat, long long n_rows) {
-  static_assert(R / 8 == kWave, "one wave per (row, head): R/8 lanes of 8 columns");
-  const int tid = threadIdx.x, lane = tid & 63;
-  const long long row = (long long)blockIdx.x * 4 + (tid >> 6);    // flat (b, i, h); one wave per row
-  if (row >= n_rows) return;
-  const int h = (int)(row % H), i = (int)((row / H) % L), b = (int)(row / ((long long)H * L));
-  const int rows_total = L * H;
-  const int prow = i * H + h;
-  int g0, S;
-  seq_splits_lane(b, off, chunk, &g0, &S);
-  // merge weights: lane s holds split s (splits beyond 64 are folded in by the loop)
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += kWave) {
-    const int sidx = s0 + lane;
-    const float m = sidx < S ? ws_ml[((long long)(g0 + sidx) * rows_total + prow) * 2] : -INFINITY;
-    M = fmaxf(M, m);
-  }
+// Absorbed route, bf16: merge of the splits and up-projection in one pass,
+//   out[b,i,h,:] = (sum_s w_s o_s[b,i,h,:]) . W_UV[h],  w_s = 2^(m_s - M) / den,
+// from the bf16 partial sums.  Work item = (sequence b, head h, 16 query rows,
+// 64 output columns), the column tile varying fastest so that the items that
+// read the same partial sums run on one XCD and share its L2.  The W_UV tile
+// [r x 64] goes global -> LDS with direct loads while the partial sums come
+// into registers, 32 16-byte loads per lane in flight.  Wave w merges rows
+// w, w+4, .. (RPW of them; lane l: latent columns 8l..8l+7) in float32,
+// stores the merged latent as a bf16 pair hi + lo (hi = bf16(x),
+// lo = bf16(x - hi)) and multiplies both with 16x16x32 MFMAs, W fragments
+// read transposed from LDS.
+struct MergeUpArgs {
+  const uint16_t* ws_o; const float* ws_ml; const int32_t* off;
+  const uint16_t* w_uv;   // [H][R][V]
+  float* out;             // [B][L][H][V]
+  int B, L, H, V, chunk;
+  int S1;                 // splits of the sequence when B == 1
+  int MTS, CT, n_items;   // row tiles of 16 per sequence, column tiles of 64, items
+};
+
+// RPW: query rows per wave (1, 2 or 4: a row tile holds up to 4 * RPW rows).
+template <int R, int RPW>
+__global__ __launch_bounds__(256, 1) void merge_upproj_kernel(MergeUpArgs p) {
+  static_assert(R / 8 == kWave, "one lane per 8 latent columns");
+  constexpr int WRB = 64 * 2 + 16;            // W row: 64 bf16 + pad (bytes)
+  constexpr int WCH = WRB / 16;               // 16-byte slots per W row (8 data + 1 pad)
+  constexpr int WINST = R * WCH / kWave;      // direct-load wave instructions for the tile
+  constexpr int ARB = R * 2 + 16;             // A row: R bf16 + pad
+  constexpr int SB = 32 / RPW;                // splits per row per round of loads
+  static_assert(WINST % 4 == 0 && kWave % SB == 0, "tile split over 4 waves; rounds inside a 64-split window");
+  __shared__ __attribute__((aligned(1024))) uint8_t wt[R * WRB];
+  __shared__ __attribute__((aligned(16))) uint8_t at[2][16 * ARB];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int item = xcd_item(blockIdx.x, p.n_items);
+  if (item >= p.n_items) return;
+  const int ct = item % p.CT;
+  int tmp = item / p.CT;
+  const int mt = tmp % p.MTS;
+  tmp /= p.MTS;
+  const int h = tmp % p.H, b = tmp / p.H;
+  const int rows_total = p.L * p.H;
+  const int i0 = 16 * mt;
+  const int mrows = min(16, p.L - i0);
+
+  // ---- W_UV tile -> LDS (slot j*64 + lane = (row, 16-byte chunk); pad slots load chunk 0)
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint16_t* wsrc = p.w_uv + (long long)h * R * p.V + ct * 64;
+  auto issue_w = [&]() {
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, kWave));
-  float den = 0.f;
-  for (int s0 = 0; s0 < S; s0 += kWave) {
-    const int sidx = s0 + lane;
-    if (sidx < S) {
-      const float* ml = ws_ml + ((long long)(g0 + sidx) * rows_total + prow) * 2;
-      if (ml[0] != -INFINITY) den += __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
+    for (int x = 0; x < WINST / 4; ++x) {
+      const int j = wu + 4 * x;
+      const int pos = kWave * j + lane;
+      const int row = pos / WCH;
+      int ch = pos - row * WCH;
+      if (ch == WCH - 1) ch = 0;
+      __builtin_amdgcn_global_load_lds(wsrc + (long long)row * p.V + 8 * ch,
+                                       (__attribute__((address_space(3))) void*)(wt + 1024 * j), 16, 0, 0);
+    }
+  };
+
+  // splits of sequence b: g0 .. g0+S-1 (one sequence: given by the host)
+  int g0 = 0, S = p.S1;
+  if (p.B > 1) {
+    seq_splits(b, p.off, p.chunk, &g0, &S);
+    g0 = __builtin_amdgcn_readfirstlane(g0);
+    S = __builtin_amdgcn_readfirstlane(S);
+  }
+  // rows of this wave: w + 4 rr for rr < nr (row m of the tile is query row i0 + m)
+  const int nr = min(RPW, mrows > wu ? (mrows - wu + 3) / 4 : 0);
+  const uint16_t* obase = p.ws_o + (long long)g0 * rows_total * R + 8 * lane;
+  // flat partial-sum row of each slot; slots past this wave's rows repeat its last row
+  // (a wave without rows reads nothing)
+  int prow[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) prow[rr] = (i0 + (nr > 0 ? wu + 4 * min(rr, nr - 1) : 0)) * p.H + h;
+
+  float o[RPW][8];
+  float M[RPW], inv[RPW], wl[RPW];   // wl: merge weight of split 64*(s0/64) + lane
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[rr][c] = 0.f;
+    M[rr] = -INFINITY; inv[rr] = 0.f; wl[rr] = 0.f;
+  }
+
+  // (max, sum) of split `lane` for every row: loaded before the partial sums, so that
+  // waiting for them does not wait for the partial sums
+  float mv[RPW], lv[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    mv[rr] = -INFINITY;
+    lv[rr] = 0.f;
+    if (nr > 0 && lane < S) {
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(p.ws_ml + ((long long)(g0 + lane) * rows_total + prow[rr]) * 2);
+      mv[rr] = ml[0];
+      lv[rr] = ml[1];
     }
   }
+
+  for (int s0 = 0; s0 < (nr > 0 ? S : 0); s0 += SB) {
+    // one round of loads: splits s0 .. s0+SB-1 of every row of the wave (clamped; the
+    // surplus gets weight 0)
+    u32x4 v[RPW][SB];
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d, kWave);
-  const float inv = 1.f / den;
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const uint16_t* src0 = ws_o + ((long long)g0 * rows_total + prow) * R + 8 * lane;
-  constexpr int US = 16;
-  for (int s0 = 0; s0 < S; s0 += kWave) {
-    const int sl = s0 + lane;
-    float my_w = 0.f;
-    if (sl < S) {
-      const float m = ws_ml[((long long)(g0 + sl) * rows_total + prow) * 2];
-      my_w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M) * inv;
-    }
-    const int ns = min(kWave, S - s0);
-    for (int u0 = 0; u0 < ns; u0 += US) {
-      u32x4 v[US];
+    for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
-      for (int u = 0; u < US; ++u) v[u] = ld16(src0 + (long long)(s0 + min(u0 + u, ns - 1)) * rows_total * R);
+      for (int j = 0; j < SB; ++j)
+        v[rr][j] = ld16(obase + ((long long)min(s0 + j, S - 1) * rows_total + prow[rr]) * R);
+    if (s0 == 0) issue_w();
+    if (s0 % kWave == 0) {
+      // merge statistics of every row (first round) and the weights of the splits
+      // s0 + lane (the window of this round)
 #pragma unroll
-      for (int u = 0; u < US; ++u) {
-        const float wgt = (u0 + u < ns) ? __shfl(my_w, u0 + u, kWave) : 0.f;
+      for (int rr = 0; rr < RPW; ++rr) {
+        if (s0 == 0) {
+          float mx = mv[rr], den = mv[rr] == -INFINITY ? 0.f : lv[rr];
+          for (int t0 = kWave; t0 < S; t0 += kWave) {   // more than 64 splits
+            const int s = t0 + lane;
+            float m = -INFINITY, l = 0.f;
+            if (s < S) {
+              const f32x2 ml = *reinterpret_cast<const f32x2*>(p.ws_ml + ((long long)(g0 + s) * rows_total + prow[rr]) * 2);
+              m = ml[0];
+              l = ml[1];
+            }
+            const float nm = fmaxf(mx, m);   // running (max, sum) over this lane's splits
+            if (nm != -INFINITY)
+              den = (mx == -INFINITY ? 0.f : den * __builtin_amdgcn_exp2f(mx - nm)) +
+                    (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - nm));
+            mx = nm;
+          }
+          float wmx = mx;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o[2 * q] = fmaf(wgt, bf16_lo(v[u][q]), o[2 * q]);
-          o[2 * q + 1] = fmaf(wgt, bf16_hi(v[u][q]), o[2 * q + 1]);
+          for (int d = 32; d >= 1; d >>= 1) wmx = fmaxf(wmx, __shfl_xor(wmx, d, kWave));
+          den = (mx == -INFINITY) ? 0.f : den * __builtin_amdgcn_exp2f(mx - wmx);
+#pragma unroll
+          for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d, kWave);
+          M[rr] = wmx;
+          inv[rr] = 1.f / den;
         }
+        const int s = s0 + lane;
+        float m = mv[rr];
+        if (s0 > 0) m = s < S ? p.ws_ml[((long long)(g0 + s) * rows_total + prow[rr]) * 2] : -INFINITY;
+        wl[rr] = (m == -INFINITY || rr >= nr) ? 0.f : __builtin_amdgcn_exp2f(m - M[rr]) * inv[rr];
       }
     }
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        // weight of split s0 + j, read from its lane of the window (uniform lane index)
+        const float wf = (s0 + j < S) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl[rr]), (s0 + j) % kWave)) : 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          o[rr][2 * c] = fmaf(wf, bf16_lo(v[rr][j][c]), o[rr][2 * c]);
+          o[rr][2 * c + 1] = fmaf(wf, bf16_hi(v[rr][j][c]), o[rr][2 * c + 1]);
+        }
+      }
   }
-  float* dst = lat + row * R + 8 * lane;
-  *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
-  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+
+  if (nr == 0) issue_w();
+
+  // ---- merged latent -> LDS as hi + lo bf16 (rows without a query row are zero)
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int m = wu + 4 * rr;
+    u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+    if (rr < RPW && rr < nr) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float x0 = o[rr < RPW ? rr : 0][2 * c], x1 = o[rr < RPW ? rr : 0][2 * c + 1];
+        hi[c] = pack_bf16(x0, x1);
+        lo[c] = pack_bf16(x0 - bf16_lo(hi[c]), x1 - bf16_hi(hi[c]));
+      }
+    }
+    st16(at[0] + m * ARB + 16 * lane, hi);
+    st16(at[1] + m * ARB + 16 * lane, lo);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of the W tile has landed
+  __syncthreads();
+
+  // ---- out tile [16 rows x 64 columns]: wave w -> columns 16w..16w+15
+  const int r16 = lane & 15, G = lane >> 4;
+  const uint8_t* wb = wt + (8 * G + (r16 >> 2)) * WRB + (16 * w + 4 * (r16 & 3)) * 2;
+  const uint8_t* ab0 = at[0] + r16 * ARB + 16 * G;
+  const uint8_t* ab1 = at[1] + r16 * ARB + 16 * G;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < R / 32; ++ks) {
+    u32x4 bv;
+#pragma unroll
+    for (int ld = 0; ld < 2; ++ld) {
+      const v4i16 rr = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(wb + (32 * ks + 4 * ld) * WRB));
+      const u32x2 r2 = __builtin_bit_cast(u32x2, rr);
+      bv[2 * ld] = r2[0];
+      bv[2 * ld + 1] = r2[1];
+    }
+    acc = mfma16(*reinterpret_cast<const u32x4*>(ab0 + 64 * ks), bv, acc);
+    acc = mfma16(*reinterpret_cast<const u32x4*>(ab1 + 64 * ks), bv, acc);
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int m = 4 * G + x;
+    if (m < mrows)
+      p.out[(((long long)b * p.L + i0 + m) * p.H + h) * p.V + ct * 64 + 16 * w + r16] = acc[x];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -700,7 +905,7 @@ hipError_t absorbed_attn_bf16(const AbsorbedLaunch& q, hipStream_t st) {
   a.qa = (const uint16_t*)q.q_lat; a.qb = (const uint16_t*)q.q_pe;
   a.ka = (const uint16_t*)q.k_pe; a.ka_ks = q.rope; a.ka_hs = 0;
   a.vv = (const uint16_t*)q.c_kv; a.vv_ks = q.r; a.vv_hs = 0;
-  a.off = q.off_dev; a.ws_o = q.ws_o; a.ws_ml = q.ws_ml;
+  a.off = q.off_dev; a.off0 = q.off0; a.kv1 = q.kv1; a.ws_o = q.ws_o; a.ws_ml = q.ws_ml;
   a.B = q.B; a.L = q.L; a.H = q.H; a.hpr = q.H; a.rows_slot = q.L * q.H; a.head_slots = 1;
   a.row_tiles = q.plan.row_tiles; a.chunk = q.plan.chunk; a.n_items = q.plan.n_items;
   a.rows_total = q.L * q.H; a.sl2 = q.scale * 1.4426950408889634f;
@@ -718,7 +923,7 @@ hipError_t materialized_attn_bf16(const MaterializedLaunch& q, hipStream_t st) {
   a.qa = (const uint16_t*)q.q_nope; a.qb = (const uint16_t*)q.q_pe;
   a.ka = (const uint16_t*)q.k; a.ka_ks = (long long)q.H * D; a.ka_hs = D;
   a.vv = (const uint16_t*)q.v; a.vv_ks = (long long)q.H * q.v_dim; a.vv_hs = q.v_dim;
-  a.off = q.off_dev; a.ws_o = q.ws_o; a.ws_ml = q.ws_ml;
+  a.off = q.off_dev; a.off0 = q.off0; a.kv1 = q.kv1; a.ws_o = q.ws_o; a.ws_ml = q.ws_ml;
   a.B = q.B; a.L = q.L; a.H = q.H; a.hpr = 1; a.rows_slot = q.L; a.head_slots = q.H;
   a.row_tiles = q.plan.row_tiles; a.chunk = q.plan.chunk; a.n_items = q.plan.n_items;
   a.rows_total = q.L * q.H; a.sl2 = q.scale * 1.4426950408889634f;
@@ -786,18 +991,21 @@ hipError_t combine_upproj(const AbsorbedLaunch& q, mla_dtype_t dt, float* out, h
     return hipGetLastError();
   }
   if (q.r != 512 || q.v_dim % 64 != 0) return hipErrorInvalidValue;
-  const long long n_rows = (long long)q.B * q.L * q.H;
-  hipLaunchKernelGGL(merge_latent_kernel<512>, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, st,
-                     (const uint16_t*)q.ws_o, (const float*)q.ws_ml, q.off_dev, q.B, q.L, q.H, q.plan.chunk,
-                     q.ws_lat, n_rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  GemmArgs a{};
-  a.A = q.ws_lat; a.a_row = (long long)q.H * q.r; a.a_head = q.r;
-  a.W = (const uint16_t*)q.w_uv;
-  a.C = out; a.c_row = (long long)q.H * q.v_dim; a.c_head = q.v_dim;
-  a.M = q.B * q.L; a.K = q.r; a.N = q.v_dim; a.H = q.H;
-  return gemm_smallm(true, false, a, st);
+  MergeUpArgs a{};
+  a.ws_o = (const uint16_t*)q.ws_o; a.ws_ml = q.ws_ml; a.off = q.off_dev;
+  a.w_uv = (const uint16_t*)q.w_uv; a.out = out;
+  a.B = q.B; a.L = q.L; a.H = q.H; a.V = q.v_dim; a.chunk = q.plan.chunk;
+  a.S1 = q.plan.n_splits;
+  a.MTS = (q.L + 15) / 16; a.CT = q.v_dim / 64;
+  const long long items = (long long)q.B * q.H * a.MTS * a.CT;
+  if (items > INT32_MAX) return hipErrorInvalidValue;
+  a.n_items = (int)items;
+  const int rpw = (std::min(16, q.L) + 3) / 4;   // query rows per wave
+  const dim3 grid(grid_xcd(a.n_items));
+  if (rpw == 1) hipLaunchKernelGGL((merge_upproj_kernel<512, 1>), grid, dim3(256), 0, st, a);
+  else if (rpw == 2) hipLaunchKernelGGL((merge_upproj_kernel<512, 2>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((merge_upproj_kernel<512, 4>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace mla

@@ -9,7 +9,7 @@
 //
 // bf16 uses MFMA with fp32 accumulation.  MFMA operands need the contraction
 // index contiguous per lane; W_UK [H, n, r] (fold contracts over n) and W_UV
-// [H, r, v] (expand and up-projection contract over r) store it strided: the
+// [H, r, v] (the expand contracts over r) store it strided: the fold's
 // small-M GEMM reads those fragments transposed from LDS (ds_read_b64_tr_b16),
 // the expand transposes its W_UV tiles in registers (8x8 bf16 blocks) on the
 // way into LDS.  The fold is a small-M product (M = B*L rows per head): each
@@ -23,25 +23,21 @@ namespace mla {
 
 // ---------------------------------------------------------------------------
 // Small-M batched GEMM per head, bf16 MFMA:  C[h][m, :] = A[h][m, :] . W[h]
-// with W[h] row-major [K x N] (N contiguous).  Used for the fold (A = q_nope,
-// W = W_UK[h], C = q_lat in bf16) and for the up-projection of the merged
-// latent (A = o_lat in float32, taken as a bf16 pair hi + lo, W = W_UV[h],
-// C = out in float32).  Workgroup = (head, 64 output columns, MT rows): the W
-// tile [K x 64] and the A tile are loaded into registers with 16-byte loads,
-// written to LDS (padded rows), and multiplied with 16x16x32 MFMAs, W
-// fragments read transposed from the row-major tile (ds_read_b64_tr_b16).
-// Each wave owns 16 output columns; the weight stream is read once per
-// MT rows.
+// with W[h] row-major [K x N] (N contiguous), A and C bf16, fp32 accumulation.
+// Used for the fold (A = q_nope, W = W_UK[h], C = q_lat).  Workgroup = (head,
+// 64 output columns, MT rows): the W tile [K x 64] and the A tile are loaded
+// into registers with 16-byte loads, written to LDS (padded rows), and
+// multiplied with 16x16x32 MFMAs, W fragments read transposed from the
+// row-major tile (ds_read_b64_tr_b16).  Each wave owns 16 output columns; the
+// weight stream is read once per MT rows.
 // ---------------------------------------------------------------------------
-// A_F32: A is float32 (hi/lo split); C_BF16: C stored as bf16.  MT rows per workgroup.
-template <bool A_F32, bool C_BF16, int MT, int KMAX>
+template <int MT, int KMAX>
 __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
   constexpr int WRB = 64 * 2 + 16;          // W row: 64 bf16 + pad
   constexpr int ARB = KMAX * 2 + 16;        // A row: K bf16 + pad
-  constexpr int NA = A_F32 ? 2 : 1;         // A tiles (hi, lo)
   constexpr int RB = MT / 16;
   __shared__ __attribute__((aligned(16))) uint8_t wt[KMAX * WRB];
-  __shared__ __attribute__((aligned(16))) uint8_t at[NA][MT * ARB];
+  __shared__ __attribute__((aligned(16))) uint8_t at[MT * ARB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int item = xcd_item(blockIdx.x, g.n_items);
   if (item >= g.n_items) return;
@@ -60,22 +56,17 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
     const int C = tid + 256 * x;
     if (C < K * 8) wst[x] = ld16(wsrc + (long long)(C >> 3) * g.N + 8 * (C & 7));
   }
-  // ---- A tile: MT rows x K ------------------------------------------------------
-  // bf16: 8 elements per chunk; float32: 4 elements per chunk (two chunks -> 8 bf16 hi + 8 lo)
-  constexpr int AE = A_F32 ? 4 : 8;         // elements per 16-byte chunk
-  constexpr int ACH_T = MT * KMAX / AE / 256;
+  // ---- A tile: MT rows x K (8 elements per 16-byte chunk) ----------------------
+  constexpr int ACH_T = MT * KMAX / 8 / 256;
   u32x4 ast[ACH_T];
-  const int KC = K / AE;                    // chunks per A row
+  const int KC = K / 8;                     // chunks per A row
 #pragma unroll
   for (int x = 0; x < ACH_T; ++x) {
     const int C = tid + 256 * x;
     const int r = C / KC, c = C % KC;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (C < MT * KC && m0 + r < g.M) {
-      const char* a = reinterpret_cast<const char*>(g.A) +
-                      ((long long)h * g.a_head + (long long)(m0 + r) * g.a_row + (long long)c * AE) * (A_F32 ? 4 : 2);
-      v = ld16(a);
-    }
+    if (C < MT * KC && m0 + r < g.M)
+      v = ld16(g.A + (long long)h * g.a_head + (long long)(m0 + r) * g.a_row + (long long)c * 8);
     ast[x] = v;
   }
 #pragma unroll
@@ -87,27 +78,13 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
   for (int x = 0; x < ACH_T; ++x) {
     const int C = tid + 256 * x;
     const int r = C / KC, c = C % KC;
-    if (C < MT * KC) {
-      if (A_F32) {
-        const f32x4 f = __builtin_bit_cast(f32x4, ast[x]);
-        u32x2 hi, lo;
-        hi[0] = pack_bf16(f[0], f[1]);
-        hi[1] = pack_bf16(f[2], f[3]);
-        lo[0] = pack_bf16(f[0] - bf16_lo(hi[0]), f[1] - bf16_hi(hi[0]));
-        lo[1] = pack_bf16(f[2] - bf16_lo(hi[1]), f[3] - bf16_hi(hi[1]));
-        *reinterpret_cast<u32x2*>(at[0] + r * ARB + c * 8) = hi;
-        *reinterpret_cast<u32x2*>(at[NA - 1] + r * ARB + c * 8) = lo;
-      } else {
-        st16(at[0] + r * ARB + c * 16, ast[x]);
-      }
-    }
+    if (C < MT * KC) st16(at + r * ARB + c * 16, ast[x]);
   }
   __syncthreads();
 
   // ---- MFMA: wave w -> columns 16w..16w+15 ------------------------------------
-  const int r16 = lane & 15, kq = lane >> 4;
-  const int s16 = lane & 15, G = lane >> 4;
-  const uint8_t* wb = wt + (8 * G + (s16 >> 2)) * WRB + (16 * w + 4 * (s16 & 3)) * 2;
+  const int r16 = lane & 15, G = lane >> 4;
+  const uint8_t* wb = wt + (8 * G + (r16 >> 2)) * WRB + (16 * w + 4 * (r16 & 3)) * 2;
   f32x4 acc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -125,11 +102,8 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (rb < nrb) {
-#pragma unroll
-        for (int t = 0; t < NA; ++t) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(at[t] + (16 * rb + r16) * ARB + (32 * ks + 8 * kq) * 2);
-          acc[rb] = mfma16(a, bv, acc[rb]);
-        }
+        const u32x4 a = *reinterpret_cast<const u32x4*>(at + (16 * rb + r16) * ARB + (32 * ks + 8 * G) * 2);
+        acc[rb] = mfma16(a, bv, acc[rb]);
       }
     }
   }
@@ -138,33 +112,28 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const int m = m0 + 16 * rb + 4 * kq + x;
+      const int m = m0 + 16 * rb + 4 * G + x;
       if (m < g.M) {
         const long long o = (long long)h * g.c_head + (long long)m * g.c_row + ct * 64 + 16 * w + r16;
-        if (C_BF16) reinterpret_cast<uint16_t*>(g.C)[o] = __builtin_bit_cast(uint16_t, (__bf16)acc[rb][x]);
-        else reinterpret_cast<float*>(g.C)[o] = acc[rb][x];
+        g.C[o] = __builtin_bit_cast(uint16_t, (__bf16)acc[rb][x]);
       }
     }
 }
 
-hipError_t gemm_smallm(bool a_f32, bool c_bf16, const GemmArgs& a0, hipStream_t st) {
+hipError_t gemm_smallm(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
   if (a.K % 32 != 0 || a.K > 512 || a.N % 64 != 0) return hipErrorInvalidValue;
-  // rows per workgroup: 16 for small M; otherwise 64 (bf16 A) or 32 (float32 A, whose hi/lo
-  // tiles take twice the LDS)
-  const int MT = a.M <= 16 ? 16 : (a_f32 ? 32 : 64);
+  const int MT = a.M <= 16 ? 16 : 64;       // rows per workgroup
   a.n_items = a.H * (a.N / 64) * ((a.M + MT - 1) / MT);
   const unsigned grid = (unsigned)(((a.n_items + kXcds - 1) / kXcds) * kXcds);
   // LDS and staging registers are sized by KMAX: small K keeps several workgroups per CU
   const int KM = a.K <= 128 ? 128 : (a.K <= 256 ? 256 : 512);
-#define MLA_GEMM(AF, CB, M_, KM_)                                                                   \
-  if (a_f32 == AF && c_bf16 == CB && MT == M_ && KM == KM_) {                                       \
-    hipLaunchKernelGGL((gemm_smallm_kernel<AF, CB, M_, KM_>), dim3(grid), dim3(256), 0, st, a);     \
-    return hipGetLastError();                                                                       \
+#define MLA_GEMM(M_, KM_)                                                                \
+  if (MT == M_ && KM == KM_) {                                                           \
+    hipLaunchKernelGGL((gemm_smallm_kernel<M_, KM_>), dim3(grid), dim3(256), 0, st, a);  \
+    return hipGetLastError();                                                            \
   }
-  MLA_GEMM(false, true, 16, 128) MLA_GEMM(false, true, 64, 128) MLA_GEMM(false, true, 16, 256)
-  MLA_GEMM(false, true, 64, 256) MLA_GEMM(false, true, 16, 512) MLA_GEMM(false, true, 64, 512)
-  MLA_GEMM(true, false, 16, 512) MLA_GEMM(true, false, 32, 512)
+  MLA_GEMM(16, 128) MLA_GEMM(64, 128) MLA_GEMM(16, 256) MLA_GEMM(64, 256) MLA_GEMM(16, 512) MLA_GEMM(64, 512)
 #undef MLA_GEMM
   return hipErrorInvalidValue;
 }
@@ -188,11 +157,11 @@ hipError_t fold_query(mla_dtype_t dt, int rows, int H, int n, int r, const void*
   if (dt == kBF16) {
     if (n % 32 != 0 || n > 512 || r % 64 != 0) return hipErrorInvalidValue;
     GemmArgs a{};
-    a.A = q_nope; a.a_row = (long long)H * n; a.a_head = n;
+    a.A = (const uint16_t*)q_nope; a.a_row = (long long)H * n; a.a_head = n;
     a.W = (const uint16_t*)w_uk;
-    a.C = q_lat; a.c_row = (long long)H * r; a.c_head = r;
+    a.C = (uint16_t*)q_lat; a.c_row = (long long)H * r; a.c_head = r;
     a.M = rows; a.K = n; a.N = r; a.H = H;
-    return gemm_smallm(false, true, a, st);
+    return gemm_smallm(a, st);
   }
   const long long total = (long long)rows * H * r;
   const long long blocks = (total + 255) / 256;

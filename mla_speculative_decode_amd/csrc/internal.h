@@ -19,7 +19,6 @@ struct SplitPlan {
   int head_slots;  // absorbed: 1; materialised: H
   int n_items;     // n_splits * head_slots * row_tiles
   size_t ws_o_bytes, ws_ml_floats;   // partial O: bf16 on the absorbed bf16 route, float32 otherwise
-  size_t ws_lat_bytes;               // merged latent (absorbed bf16 route): float32 [B*L*H, r]
   size_t ws_bytes;
 };
 
@@ -27,8 +26,9 @@ struct AbsorbedLaunch {
   int r, rope, v_dim, H, B, L;
   const void* q_lat; const void* q_pe; const void* c_kv; const void* k_pe; const void* w_uv;
   const int32_t* off_dev;
+  int off0, kv1;   // B == 1: the sequence's start and length (from the host offsets)
   float scale;
-  void* ws_o; float* ws_ml; float* ws_lat;
+  void* ws_o; float* ws_ml;
   SplitPlan plan;
 };
 
@@ -36,6 +36,7 @@ struct MaterializedLaunch {
   int n, rope, v_dim, H, B, L;
   const void* q_nope; const void* q_pe; const void* k; const void* v;
   const int32_t* off_dev;
+  int off0, kv1;   // B == 1: the sequence's start and length (from the host offsets)
   float scale;
   void* ws_o; float* ws_ml;
   SplitPlan plan;
@@ -51,13 +52,13 @@ hipError_t combine_upproj(const AbsorbedLaunch& q, mla_dtype_t dt, float* out, h
 
 // gemm.hip
 struct GemmArgs {
-  const void* A; long long a_row, a_head;   // element strides of A rows / heads
-  const uint16_t* W;                        // [H][K][N]
-  void* C; long long c_row, c_head;
+  const uint16_t* A; long long a_row, a_head;   // element strides of A rows / heads
+  const uint16_t* W;                            // [H][K][N]
+  uint16_t* C; long long c_row, c_head;
   int M, K, N, H;
   int n_items;
 };
-hipError_t gemm_smallm(bool a_f32, bool c_bf16, const GemmArgs& a, hipStream_t st);
+hipError_t gemm_smallm(const GemmArgs& a, hipStream_t st);
 hipError_t fold_query(mla_dtype_t dt, int rows, int H, int n, int r, const void* q_nope, const void* w_uk,
                       void* q_lat, hipStream_t st);
 hipError_t materialize_kv(mla_dtype_t dt, long long T, int H, int r, int n, int v, int rope, const void* c_kv,

@@ -36,6 +36,11 @@ CASES = [
     ("bf16_norope", 512, 128, 128, 0, 8, 8, [190], "bf16"),
     ("bf16_kv_eq_L", 512, 128, 128, 64, 16, 8, [8, 8], "bf16"),
     ("bf16_single_row", 512, 128, 128, 64, 1, 1, [1, 65, 1000], "bf16"),
+    # 79 splits of one sequence (merge weights beyond one 64-split window; L = 3 leaves a
+    # merge wave without rows)
+    ("bf16_many_splits", 512, 128, 128, 64, 2, 3, [5000], "bf16"),
+    # L = 20: two merge row tiles of 16, the second ragged
+    ("bf16_L20", 512, 128, 128, 64, 4, 20, [100, 333], "bf16"),
 ]
 
 
