@@ -21,6 +21,10 @@ LIB = os.path.join(HERE, "libmla.so")
 BENCH_LIB = os.path.join(HERE, "libmla_bench.so")   # timing loop used by bench.py only
 SOURCES = ["attn.hip", "gemm.hip", "api.cpp"]
 ARCH = "gfx950"
+# Per-file extra flags.  attn.hip: MFMA results in VGPRs (the split kernel's O
+# accumulators are rescaled by VALU; left in AGPRs, the compiler copies all of
+# them to VGPRs and back on every tile).
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -44,7 +48,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(objdir, src + ".o")
-        cmd = [cc, *flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags(), *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

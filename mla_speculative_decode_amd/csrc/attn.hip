@@ -296,13 +296,13 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   const int pa_off = l32 * PRB + 16 * half;                               // + rb*32*PRB + 32 kc
 
   // one 64-position tile: scores from `cur`, copy of the next tile into `nxt`
-  auto step = [&](int t0, const uint8_t* cur, uint8_t* nxt) {
+  auto step = [&](int t0, const uint8_t* cur, uint8_t* nxt, bool pf) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // (A) tile t visible; PV(t-1) done, so the other buffer and pl are free
     // The next tile is copied unconditionally (branch-free code keeps the LDS
     // wait counts exact): past the end of the split every row clamps to the
     // last position and lands in the idle buffer, which nothing reads again.
-    if (VK) issue_rope(t0 + BN);
+    if (VK && pf) issue_rope(t0 + BN);
     const uint8_t* kt = cur;
     const uint8_t* vt = VK ? kt : kt + KBYTES;
 
@@ -325,8 +325,10 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         if (c + PF < DCH) ka[c % PF] = *reinterpret_cast<const u32x4*>(kq + 32 * (c + PF));
         acc = mfma32(a, qf[c], acc);
         // next tile's copy, spread over the score MFMAs (NLW instructions)
+        if (pf) {
 #pragma unroll
-        for (int x = (c * NLW) / DCH; x < ((c + 1) * NLW) / DCH; ++x) issue_part(t0 + BN, nxt, x);
+          for (int x = (c * NLW) / DCH; x < ((c + 1) * NLW) / DCH; ++x) issue_part(t0 + BN, nxt, x);
+        }
         __builtin_amdgcn_sched_barrier(0);   // keep the read of step c+PF ahead of MFMA c
       }
     }
@@ -392,18 +394,15 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
 
     // ---- PV: O[64 rows x CPW] for this wave's columns ----------------------
     {
-      if (resc) {
-        f32x4 alv[2][4];
+      if (resc) {   // lane holds row 32 rb + l32 of O
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) alv[rb][q] = *reinterpret_cast<const f32x4*>(&al[32 * rb + 8 * q + 4 * half]);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb) {
+          const float ar = al[32 * rb + l32];
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) O[rb][cb][i] *= alv[rb][i >> 2][i & 3];
+            for (int i = 0; i < 16; ++i) O[rb][cb][i] *= ar;
+        }
       }
       const uint8_t* pa = pl + pa_off;
       const uint8_t* vb = vt + tr_off;
@@ -452,25 +451,54 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
           vq[st % VPF] = vfrag(sn / NCB, sn % NCB);
         }
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) O[rb][cb] = mfma32(a[kc][rb], bcur, O[rb][cb]);
+        for (int rb = 0; rb < 2; ++rb) O[rb][cb] = mfma32(bcur, a[kc][rb], O[rb][cb]);   // O^T += V^T P^T
         __builtin_amdgcn_sched_barrier(0);   // later steps' reads stay ahead of this step's MFMAs
       }
     }
-    if (VK) store_rope(nxt);   // the other buffer is not read until barrier (A)
+    if (VK && pf) store_rope(nxt);   // the other buffer is not read until barrier (A)
   };
   // Tiles go in pairs (one per buffer) with no branch between them, so the
   // accumulators flow straight through the loop; an odd tile count ends with
-  // a tile past the split, whose keys all fail key < kend and add nothing.
+  // a tile past the split (a clamped copy of the last position), whose keys
+  // all fail key < kend and add nothing.  No copy follows the last pair.
   for (int t0 = k0; t0 < k1; t0 += 2 * BN) {
-    step(t0, buf0, buf1);
-    step(t0 + BN, buf1, buf0);
+    step(t0, buf0, buf1, true);
+    step(t0 + BN, buf1, buf0, t0 + 2 * BN < k1);
   }
 
   // ---- epilogue: row sums, partial results ---------------------------------
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last (unused) tile copy has landed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const float lw = l_run + __shfl_xor(l_run, 32, 64);
-  __syncthreads();
+  // absorbed: bf16 partials (its merge keeps the merged latent as a hi/lo
+  // pair, which leaves room for this rounding); materialised: float32
+  constexpr int PB = VK ? 2 : 4;                    // bytes per partial element
+  constexpr int SROW = DV * PB + 16;                // padded staging row (bytes)
+  static_assert((BM / 2) * SROW <= BUF, "O staging must fit in the tile buffers");
+  // rows 0..31 staged in buf0, rows 32..63 in buf1
+  auto srow = [&](int row) -> uint8_t* { return row < BM / 2 ? buf0 + row * SROW : buf1 + (row - BM / 2) * SROW; };
+  __syncthreads();   // every wave is done with the tile buffers and red
   if (half == 0) red[wk * BM + rq] = lw;
+  {
+    // lane holds row 32 rb + l32, columns col0 + 32 cb + 8 q + 4 half + (0..3)
+    const int col0 = w * CPW;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint8_t* dst = srow(32 * rb + l32) + (col0 + 32 * cb + 8 * q + 4 * half) * PB;
+          const f32x16& o = O[rb][cb];
+          if (VK) {
+            u32x2 v;
+            v[0] = pack_bf16(o[4 * q], o[4 * q + 1]);
+            v[1] = pack_bf16(o[4 * q + 2], o[4 * q + 3]);
+            *reinterpret_cast<u32x2*>(dst) = v;
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+          }
+        }
+  }
   __syncthreads();
   const long long gro = (long long)g * p.rows_total;
   if (wk == 0 && half == 0 && rq_ok) {
@@ -478,37 +506,25 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     p.ws_ml[(gro + prow) * 2 + 0] = m_run;
     p.ws_ml[(gro + prow) * 2 + 1] = red[rq] + red[BM + rq];
   }
-  // Partial O: each wave stages its [64 rows x CPW] fp32 block in LDS (the tile
-  // buffers are free now), then writes rows with 16-byte coalesced stores.
   {
-    // absorbed: bf16 partials (its merge keeps the merged latent as a hi/lo
-    // pair, which leaves room for this rounding); materialised: float32
-    constexpr int PB = VK ? 2 : 4;                    // bytes per partial element
-    constexpr int SROW = DV * PB + 16;                // padded row (bytes)
-    static_assert((BM / 2) * SROW <= BUF, "O staging must fit in the tile buffers");
-    // rows 0..31 in buf0, rows 32..63 in buf1
-    auto srow = [&](int row) -> uint8_t* { return row < BM / 2 ? buf0 + row * SROW : buf1 + (row - BM / 2) * SROW; };
-    __syncthreads();                                  // all waves are done with the tile buffers
-    const int col0 = w * CPW;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * rb + 8 * (i >> 2) + 4 * half + (i & 3);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          if (VK) *reinterpret_cast<__bf16*>(srow(row) + (col0 + 32 * cb + l32) * 2) = (__bf16)O[rb][cb][i];
-          else *reinterpret_cast<float*>(srow(row) + (col0 + 32 * cb + l32) * 4) = O[rb][cb][i];
-        }
-      }
-    __syncthreads();
-    constexpr int V16 = DV * PB / 16;                 // 16-byte chunks per row
+    // rows out with 16-byte coalesced stores, all LDS reads first
+    constexpr int V16 = DV * PB / 16;               // 16-byte chunks per row
+    constexpr int NST = BM * V16 / 256;
+    static_assert(BM * V16 % 256 == 0, "whole rounds of stores");
     uint8_t* wso = reinterpret_cast<uint8_t*>(p.ws_o);
-    for (int e = tid; e < BM * V16; e += 256) {
-      const int row = e / V16, c16 = e % V16;
+    u32x4 v[NST];
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int e = tid + 256 * j;
+      v[j] = *reinterpret_cast<const u32x4*>(srow(e / V16) + 16 * (e % V16));
+    }
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int e = tid + 256 * j;
+      const int row = e / V16;
       if (row < nrows) {
         const int prow = hs * p.rows_slot + idx0 + row;
-        st16(wso + ((gro + prow) * DV) * PB + 16 * c16, *reinterpret_cast<const u32x4*>(srow(row) + 16 * c16));
+        st16(wso + ((gro + prow) * DV) * PB + 16 * (e % V16), v[j]);
       }
     }
   }
