@@ -21,8 +21,8 @@
 //   scores  S^T[64 keys x 64 rows] as 2x2 blocks of 32x32; wave (wk, wr)
 //           computes keys 32wk.., rows 32wr.. with the query block held in
 //           registers (B operand) and keys streamed from LDS (A operand);
-//   softmax base-2 online softmax; the two key halves of a row exchange their
-//           partial maxima through LDS;
+//   softmax base-2 online softmax; each lane publishes the maximum of its
+//           16 scores of a row and every wave reads the 4 values of each row;
 //   PV      O[64 rows x DV]: wave w owns columns w*DV/4..; P (bf16) comes from
 //           LDS, V^T from an LDS copy transposed in registers on the way in.
 // LDS holds one key tile row-major (kt), one value tile transposed (vt), P,
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
   __shared__ __attribute__((aligned(16))) uint8_t pl[BM * PRB];
-  __shared__ float red[2 * BM];
+  __shared__ __attribute__((aligned(16))) float red[BM * 4];   // per row: 4 partial values (2 key halves x 2 lane halves)
   __shared__ __attribute__((aligned(16))) float al[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -131,6 +131,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   // key-only source: absorbed k_pe (chunks DA/8..), materialised K (all chunks)
   const uint16_t* kab = p.ka + (long long)hs * p.ka_hs;
   const uint16_t* vvb = p.vv + (long long)hs * p.vv_hs;
+  // absorbed: latent row 0 of the sequence (rows are DA wide), in scalar registers
+  const uint16_t* lbase = uniform_ptr(vvb + p0 * DA);
 
   // ---- tile copy: global -> LDS --------------------------------------------
   // absorbed: each latent row (r = 512 bf16 = 1 KB) is one wave instruction
@@ -150,10 +152,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     if (VK) {
       static_assert(!VK || DA == 512, "absorbed path loads 1 KB latent rows");
       // one latent row per instruction: uniform row address + constant lane offset
-      const uint16_t* lseq = vvb + p0 * p.vv_ks + 8 * lane;
       const int key = wu + 4 * x;
       const int kr = min(t0 + key, k1 - 1);
-      __builtin_amdgcn_global_load_lds(lseq + (unsigned)kr * (unsigned)DA,
+      __builtin_amdgcn_global_load_lds(lbase + kr * DA + 8 * lane,
                                        (__attribute__((address_space(3))) void*)(kdst + key * KRB), 16, 0, 0);
     } else if (x < NLW_K) {
       const int j = wu + 4 * x;
@@ -221,6 +222,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     const int i = idx / p.hpr;
     kend = min(k1, Kv - p.L + i + 1);
   }
+  // positions every row of the tile may see (rows are in increasing query order)
+  const int kfull = min(k1, Kv - p.L + idx0 / p.hpr + 1);
   if (VK) {
     // absorbed: the rows of the tile are consecutive in q_lat / q_pe.  The query
     // block goes to the idle tile buffer once (q_lat row = one 1 KB direct load,
@@ -332,27 +335,37 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         __builtin_amdgcn_sched_barrier(0);   // keep the read of step c+PF ahead of MFMA c
       }
     }
+    // acc[i] = q.k for key t0 + 32 wk + 8 (i >> 2) + 4 half + (i & 3), row rq.
+    // Tiles inside every row's causal range (all but the last ones of a split)
+    // skip the key mask (a uniform branch).
     float s[16];
-    float pmax = -INFINITY;
+    if (t0 + BN <= kfull) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = t0 + 32 * wk + 8 * (i >> 2) + 4 * half + (i & 3);
-      s[i] = key < kend ? acc[i] * p.sl2 : -INFINITY;
-      pmax = fmaxf(pmax, s[i]);
+      for (int i = 0; i < 16; ++i) s[i] = acc[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = t0 + 32 * wk + 8 * (i >> 2) + 4 * half + (i & 3);
+        s[i] = key < kend ? acc[i] : -INFINITY;
+      }
     }
-    pmax = fmaxf(pmax, __shfl_xor(pmax, 32, 64));
+    float pmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    pmax = fmaxf(pmax, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])), fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+    pmax *= p.sl2;   // base-2 logits: scale * log2(e) * q.k
     // Lazy rescaling: the reference maximum of a row only moves when a tile
     // raises it by more than 2^8 (or on its first finite score), so P <= 256
     // and the O accumulators are rescaled rarely.  P is computed here against
     // the current reference and published with the partial maxima; a tile that
-    // raises some row recomputes it below.
+    // raises some row recomputes it below.  A row without a finite reference
+    // uses 0: its masked keys give 2^-inf = 0, and its finite scores raise it.
     uint8_t* prow = pl + rq * PRB + 64 * wk + 8 * half;
     auto write_p = [&](float mref, float* psum) {
-      float ps = 0.f;
+      const float mb = mref == -INFINITY ? 0.f : mref;
       float e[16];
+      float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        e[i] = s[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[i] - mref);
+        e[i] = __builtin_amdgcn_exp2f(fmaf(s[i], p.sl2, -mb));
         ps += e[i];
       }
 #pragma unroll
@@ -366,20 +379,24 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     };
     float psum;
     write_p(m_run, &psum);
-    if (half == 0) red[wk * BM + rq] = pmax;
-    __syncthreads();  // (B) P and partial maxima visible
+    red[rq * 4 + wk * 2 + half] = pmax;   // maximum over this lane's 16 keys
+    lds_barrier();  // (B) P and partial maxima visible (the next tile's copy stays in flight)
 
     // Every wave decides for all 64 rows (lane = row) from the same partial
     // maxima with the same arithmetic, so the decision is uniform over the
     // workgroup and the branch below (with its barrier) is taken by all waves
     // or by none.
-    const float tm_all = fmaxf(red[lane], red[BM + lane]);
+    auto row_max = [&](int row) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&red[row * 4]);
+      return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+    };
+    const float tm_all = row_max(lane);
     const bool raise_all = tm_all > m_all + 8.f;
     // O needs rescaling only where a row with a finite reference was raised
     const bool resc = __ballot(raise_all && m_all != -INFINITY) != 0;
     if (__ballot(raise_all) != 0) {
       m_all = raise_all ? tm_all : m_all;
-      const float tmax = fmaxf(pmax, red[(1 - wk) * BM + rq]);
+      const float tmax = row_max(rq);
       const bool raise = tmax > m_run + 8.f;
       const float m_new = raise ? tmax : m_run;
       const float alpha = (raise && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
@@ -387,7 +404,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       l_run = l_run * alpha + psum;
       m_run = m_new;
       if (wk == 0 && half == 0) al[rq] = alpha;
-      __syncthreads();  // (C) recomputed P and the rescale factors visible
+      lds_barrier();  // (C) recomputed P and the rescale factors visible
     } else {
       l_run += psum;
     }
@@ -468,7 +485,6 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
 
   // ---- epilogue: row sums, partial results ---------------------------------
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  const float lw = l_run + __shfl_xor(l_run, 32, 64);
   // absorbed: bf16 partials (its merge keeps the merged latent as a hi/lo
   // pair, which leaves room for this rounding); materialised: float32
   constexpr int PB = VK ? 2 : 4;                    // bytes per partial element
@@ -477,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   // rows 0..31 staged in buf0, rows 32..63 in buf1
   auto srow = [&](int row) -> uint8_t* { return row < BM / 2 ? buf0 + row * SROW : buf1 + (row - BM / 2) * SROW; };
   __syncthreads();   // every wave is done with the tile buffers and red
-  if (half == 0) red[wk * BM + rq] = lw;
+  red[rq * 4 + wk * 2 + half] = l_run;   // sum over this lane's keys
   {
     // lane holds row 32 rb + l32, columns col0 + 32 cb + 8 q + 4 half + (0..3)
     const int col0 = w * CPW;
@@ -504,7 +520,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   if (wk == 0 && half == 0 && rq_ok) {
     const int prow = hs * p.rows_slot + idx0 + rq;
     p.ws_ml[(gro + prow) * 2 + 0] = m_run;
-    p.ws_ml[(gro + prow) * 2 + 1] = red[rq] + red[BM + rq];
+    const f32x4 a = *reinterpret_cast<const f32x4*>(&red[rq * 4]);
+    p.ws_ml[(gro + prow) * 2 + 1] = (a[0] + a[1]) + (a[2] + a[3]);
   }
   {
     // rows out with 16-byte coalesced stores, all LDS reads first

@@ -38,10 +38,30 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-// Round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Round-to-nearest-even pack of two floats: one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const bf16x2 v = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+// A pointer that is the same in every lane, moved to scalar registers so that
+// address arithmetic on it stays on the scalar unit.
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// ---- workgroup barrier for LDS traffic only ---------------------------------
+// Orders this wave's LDS accesses around s_barrier without waiting for its
+// global loads (__syncthreads() also waits for those, so a tile copy issued
+// earlier would have to land first).  Data written to LDS by direct
+// global -> LDS loads is not covered: wait vmcnt(0) before a full barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---- memory --------------------------------------------------------------
