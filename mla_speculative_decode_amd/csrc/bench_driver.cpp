@@ -38,8 +38,11 @@ int step(const mla_geom* g, int B, int L, const Sets& s, int k, const int32_t* o
 extern "C" {
 
 // res[0] us/step, plain back-to-back steps (events only around the run)
-// res[1] us fold, res[2] us splits, res[3] us merge (per-launch means, evented run)
+// res[1] us fold, res[2] us splits, res[3] us merge (per-launch means, evented run;
+//        each includes the dispatch gap before its kernel)
 // res[4] us/step of the evented run
+// res[5] us per mla_absorbed_splits launch, launches back to back over the same
+//        rotation of input sets (events only around the run)
 int mlab_absorbed_run(const mla_geom* g, int B, int L, int nsets, void* const* q_nope, void* const* q_pe,
                       void* const* c_kv, void* const* k_pe, void* const* w_uk, void* const* w_uv,
                       void* const* q_lat, float* const* out, const int32_t* off_h, const int32_t* off_d,
@@ -80,6 +83,20 @@ int mlab_absorbed_run(const mla_geom* g, int B, int L, int nsets, void* const* q
   hipEventElapsedTime(&whole, ev[0], ev[(size_t)(steps - 1) * 4 + 3]);
   for (int j = 0; j < 3; ++j) res[1 + j] = 1e3 * t[j] / steps;
   res[4] = 1e3 * whole / steps;
+
+  // split launches alone (q_lat of every set was written by the steps above)
+  hipStreamSynchronize(st);
+  hipEventRecord(a, st);
+  for (int i = 0; i < steps; ++i) {
+    const int k = i % nsets;
+    if ((rc = mla_absorbed_splits(g, MLA_BF16, B, L, s.q_lat[k], s.q_pe[k], s.c_kv[k], s.k_pe[k], off_h, off_d,
+                                  scale, ws, ws_bytes, st)))
+      return rc;
+  }
+  hipEventRecord(b, st);
+  hipStreamSynchronize(st);
+  hipEventElapsedTime(&ms, a, b);
+  res[5] = 1e3 * ms / steps;
   for (auto& e : ev) hipEventDestroy(e);
   hipEventDestroy(a);
   hipEventDestroy(b);
