@@ -21,10 +21,8 @@ LIB = os.path.join(HERE, "libmla.so")
 BENCH_LIB = os.path.join(HERE, "libmla_bench.so")   # timing loop used by bench.py only
 SOURCES = ["attn.hip", "gemm.hip", "api.cpp"]
 ARCH = "gfx950"
-# Per-file extra flags.  attn.hip: MFMA results in VGPRs (the split kernel's O
-# accumulators are rescaled by VALU; left in AGPRs, the compiler copies all of
-# them to VGPRs and back on every tile).
-EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file extra flags (none at present).
+EXTRA: dict = {}
 
 
 def hipcc() -> str:

@@ -64,6 +64,9 @@ struct AttnArgs {
 __device__ __forceinline__ int kt_phys(int key, int ch) { return ch ^ ((key & 7) ^ ((key >> 3) & 7)); }
 __device__ __forceinline__ int row_phys(int row, int ch) { return ch ^ (row & 7); }
 
+// Headroom of the fixed softmax reference (log2 units): P = 2^(s - m) <= 2^64.
+constexpr float kRefSlack = 64.f;
+
 // DA: width of query part a (= width of the V source when VK); DR: query part
 // b width; DV: value width; VK: values are the first DA key columns (absorbed).
 //
@@ -101,17 +104,18 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
   __shared__ __attribute__((aligned(16))) uint8_t pl[BM * PRB];
+  __shared__ uint32_t pfd[kWave];   // landing slot of the L2 prefetch (never read)
   __shared__ __attribute__((aligned(16))) float red[BM * 4];   // per row: 4 partial values (2 key halves x 2 lane halves)
-  __shared__ __attribute__((aligned(16))) float al[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int item = xcd_item(blockIdx.x, p.n_items);
+  // work-item decode, kept in scalar registers (uniform over the workgroup)
+  const int item = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, p.n_items));
   if (item >= p.n_items) return;
-  const int rt = item % p.row_tiles;
-  const int tmp = item / p.row_tiles;
-  const int hs = tmp % p.head_slots;
-  const int g = tmp / p.head_slots;
+  const int rt = __builtin_amdgcn_readfirstlane(item % p.row_tiles);
+  const int tmp = __builtin_amdgcn_readfirstlane(item / p.row_tiles);
+  const int hs = __builtin_amdgcn_readfirstlane(tmp % p.head_slots);
+  const int g = __builtin_amdgcn_readfirstlane(tmp / p.head_slots);
   // the split is the same for the whole workgroup: keep its bounds in scalar registers
   // (one sequence: its start and length come from the host, no load of the offsets)
   int b = 0, ps = g, off_b = p.off0, Kv = p.kv1;
@@ -123,8 +127,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     Kv = __builtin_amdgcn_readfirstlane(p.off[b + 1]) - off_b;
   }
   const long long p0 = off_b;
-  const int k0 = ps * p.chunk;
-  const int k1 = min(Kv, k0 + p.chunk);
+  const int k0 = __builtin_amdgcn_readfirstlane(ps * p.chunk);
+  const int k1 = __builtin_amdgcn_readfirstlane(min(Kv, k0 + p.chunk));
   const int idx0 = rt * BM;
   const int nrows = min(BM, p.rows_slot - idx0);
 
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       static_assert(!VK || DA == 512, "absorbed path loads 1 KB latent rows");
       // one latent row per instruction: uniform row address + constant lane offset
       const int key = wu + 4 * x;
-      const int kr = min(t0 + key, k1 - 1);
+      const int kr = __builtin_amdgcn_readfirstlane(min(t0 + key, k1 - 1));
       __builtin_amdgcn_global_load_lds(lbase + kr * DA + 8 * lane,
                                        (__attribute__((address_space(3))) void*)(kdst + key * KRB), 16, 0, 0);
     } else if (x < NLW_K) {
@@ -247,6 +251,22 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         qst[x] = ld16(p.qb + (qflat0 + min(row, nrows - 1)) * DR + 8 * ch);
       }
     }
+    // This workgroup's share of the split's cache lines -> L2: positions
+    // k0 + rt + row_tiles * j, one 4-byte load per 128-byte line (8 latent lines,
+    // 1 rope line per position) into a dummy LDS slot.  The row tiles of a split
+    // run on one XCD, so the tile copies of the loop then hit L2.
+    {
+      constexpr int LPP = DA / 64 + (DR > 0 ? 1 : 0);   // 128-byte lines per position
+      const int cnt = max(0, (k1 - k0 - rt + p.row_tiles - 1) / p.row_tiles);
+      const int nl = cnt * LPP;
+      for (int e0 = 0; e0 < nl; e0 += 256) {
+        const int e = min(e0 + tid, nl - 1);
+        const int j = e / LPP, ln = e - (e / LPP) * LPP;
+        const long long pos = p0 + k0 + rt + (long long)p.row_tiles * j;
+        const uint16_t* src = ln < DA / 64 ? vvb + pos * p.vv_ks + 64 * ln : kab + pos * p.ka_ks;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)pfd, 4, 0, 0);
+      }
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int x = 0; x < QP_T; ++x) {
@@ -282,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
 
   // ---- running state ------------------------------------------------------
   float m_run = -INFINITY, l_run = 0.f;   // score layout: row rq, this wave's key half
-  float m_all = -INFINITY;                 // reference maximum of row `lane` (same in every wave)
+  float m_all = -INFINITY;                 // reference of row `lane` (the same in every wave)
   f32x16 O[2][NCB];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -299,7 +319,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   const int pa_off = l32 * PRB + 16 * half;                               // + rb*32*PRB + 32 kc
 
   // one 64-position tile: scores from `cur`, copy of the next tile into `nxt`
-  auto step = [&](int t0, const uint8_t* cur, uint8_t* nxt, bool pf) {
+  // one 64-position tile: scores from `cur`, copy of the next tile into `nxt`;
+  // returns true (uniformly) when the split must restart with raised references
+  auto step = [&](int t0, const uint8_t* cur, uint8_t* nxt, bool pf) -> bool {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // (A) tile t visible; PV(t-1) done, so the other buffer and pl are free
     // The next tile is copied unconditionally (branch-free code keeps the LDS
@@ -352,12 +374,15 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     float pmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     pmax = fmaxf(pmax, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])), fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
     pmax *= p.sl2;   // base-2 logits: scale * log2(e) * q.k
-    // Lazy rescaling: the reference maximum of a row only moves when a tile
-    // raises it by more than 2^8 (or on its first finite score), so P <= 256
-    // and the O accumulators are rescaled rarely.  P is computed here against
-    // the current reference and published with the partial maxima; a tile that
-    // raises some row recomputes it below.  A row without a finite reference
-    // uses 0: its masked keys give 2^-inf = 0, and its finite scores raise it.
+    // Fixed reference per row: P = 2^(s - m) with m the row's maximum over the
+    // first tile that gives it finite scores.  P (bf16) and O, l (fp32) keep
+    // their relative precision at any magnitude, so later scores may exceed m
+    // by up to kRefSlack (P <= 2^64) and O is never rescaled inside the loop;
+    // a tile that exceeds that restarts the split with the larger reference.
+    // P is computed here against the current reference and published with the
+    // partial maxima; a tile that sets some row's first reference recomputes
+    // it below.  A row without a finite reference uses 0: its masked keys give
+    // 2^-inf = 0.
     uint8_t* prow = pl + rq * PRB + 64 * wk + 8 * half;
     auto write_p = [&](float mref, float* psum) {
       const float mb = mref == -INFINITY ? 0.f : mref;
@@ -391,36 +416,25 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
     };
     const float tm_all = row_max(lane);
-    const bool raise_all = tm_all > m_all + 8.f;
-    // O needs rescaling only where a row with a finite reference was raised
-    const bool resc = __ballot(raise_all && m_all != -INFINITY) != 0;
-    if (__ballot(raise_all) != 0) {
-      m_all = raise_all ? tm_all : m_all;
-      const float tmax = row_max(rq);
-      const bool raise = tmax > m_run + 8.f;
-      const float m_new = raise ? tmax : m_run;
-      const float alpha = (raise && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      write_p(m_new, &psum);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (wk == 0 && half == 0) al[rq] = alpha;
-      lds_barrier();  // (C) recomputed P and the rescale factors visible
-    } else {
-      l_run += psum;
+    if (__ballot(m_all != -INFINITY && tm_all > m_all + kRefSlack) != 0) {
+      // some row exceeds its reference by more than 2^kRefSlack: raise the
+      // references (this tile's maxima bound every earlier score) and restart
+      m_all = fmaxf(m_all, tm_all);
+      m_run = fmaxf(m_run, row_max(rq));
+      return true;
     }
+    if (__ballot(m_all == -INFINITY && tm_all != -INFINITY) != 0) {
+      // first finite scores of some rows (O is still 0 there): their reference
+      // is this tile's maximum; the other rows recompute the same P
+      m_all = (m_all == -INFINITY) ? tm_all : m_all;
+      if (m_run == -INFINITY) m_run = row_max(rq);
+      write_p(m_run, &psum);
+      lds_barrier();  // (C) recomputed P visible
+    }
+    l_run += psum;
 
     // ---- PV: O[64 rows x CPW] for this wave's columns ----------------------
     {
-      if (resc) {   // lane holds row 32 rb + l32 of O
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const float ar = al[32 * rb + l32];
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) O[rb][cb][i] *= ar;
-        }
-      }
       const uint8_t* pa = pl + pa_off;
       const uint8_t* vb = vt + tr_off;
       // V^T fragment for step (kc, cb): two transposing reads of 4 keys each
@@ -473,14 +487,31 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       }
     }
     if (VK && pf) store_rope(nxt);   // the other buffer is not read until barrier (A)
+    return false;
   };
   // Tiles go in pairs (one per buffer) with no branch between them, so the
   // accumulators flow straight through the loop; an odd tile count ends with
   // a tile past the split (a clamped copy of the last position), whose keys
   // all fail key < kend and add nothing.  No copy follows the last pair.
   for (int t0 = k0; t0 < k1; t0 += 2 * BN) {
-    step(t0, buf0, buf1, true);
-    step(t0 + BN, buf1, buf0, t0 + 2 * BN < k1);
+    if (step(t0, buf0, buf1, true) || step(t0 + BN, buf1, buf0, t0 + 2 * BN < k1)) {
+      // restart (rare, uniform): drop the partial sums, reload the first tile.  Each
+      // restart is triggered by a tile past every tile already processed, so the
+      // number of restarts is bounded by the number of tiles.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();   // every wave is done with the tile buffers and pl
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) O[rb][cb][i] = 0.f;
+      l_run = 0.f;
+      issue_tile(k0, buf0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (VK) store_rope(buf0);
+      t0 = k0 - 2 * BN;   // the loop increment brings it back to the first tile
+    }
   }
 
   // ---- epilogue: row sums, partial results ---------------------------------

@@ -28,7 +28,8 @@ def host64(t) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "", rel: float = BF16_REL_TOL):
+def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "", rel: float = BF16_REL_TOL,
+                abs_cap: bool = True):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -39,7 +40,8 @@ def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "", re
         return err, None
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
     assert err <= rel * max(rms, 1e-30), f"{what}: max err {err:.3e} > {rel} * rms {rms:.3e}"
-    assert err <= 2e-2
+    if abs_cap:   # outputs of unit-scale inputs: also inside an absolute 2e-2
+        assert err <= 2e-2, f"{what}: max err {err:.3e} > 2e-2"
     return err, err / rms
 
 

@@ -212,3 +212,60 @@ def test_select_path_through_binding():
     assert mla.select_path(g, 379, 8192) == (mla.MLA_ABSORBED, 379)
     assert mla.select_path(g, 380, 8192) == (mla.MLA_MATERIALIZED, 379)
     assert mla.select_path(g, 398, 0) == (mla.MLA_ABSORBED, 398)
+
+
+
+def _ramp(T: int, kind: str) -> np.ndarray:
+    """Per-position factors on the keys that spread the logits of a row over a
+    wide range: a sawtooth of period 256 positions rising from 1 to 81 (within
+    each period the last tiles exceed the first by far more than 2^64), the
+    falling sawtooth, and one late key scaled by 80."""
+    t = (np.arange(T) % 256) / 255.0
+    if kind == "rising":
+        f = 1.0 + 80.0 * t
+    elif kind == "falling":
+        f = 81.0 - 80.0 * t
+    else:
+        f = np.ones(T)
+        f[(T * 7) // 8] = 80.0
+    return f.astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["rising", "falling", "spike"])
+def test_wide_score_range(kind):
+    """Logits of one row spread over hundreds of log2 units (keys scaled by
+    position) on both attention kernels.  At these shapes the plans cut the
+    4096 positions into splits of 256 (absorbed: 16 row tiles of 64; materialised:
+    16 heads x 1 row tile), so every split holds one rise of the sawtooth: the
+    fixed per-row reference of the kernels must be raised inside a split."""
+    r, n, v, rope, L, kv = 512, 128, 128, 64, 8, 4096
+    H = 128
+    x = _inputs(("wide", r, n, v, rope, H, L, [kv], "bf16"))
+    f = _ramp(kv, kind)
+    c_kv = synth.round_bf16(x.c_kv * f[:, None])
+    k_pe = synth.round_bf16(x.k_pe * f[:, None])
+    q_lat = synth.draw_like((1, L, H, r), math.sqrt(n / r), "bf16", seed=78)
+    offs = x.offsets.astype(np.int32)
+    if kind == "rising":
+        # precondition: in some split of 256 positions a row's later tile exceeds its
+        # first tile's maximum by more than 64 (log2 units)
+        s = (q_lat.reshape(-1, r).astype(np.float64) @ c_kv[:512].astype(np.float64).T
+             + x.q_pe.reshape(-1, rope).astype(np.float64) @ k_pe[:512].astype(np.float64).T) * x.scale / math.log(2)
+        assert np.max(s[:, 192:256].max(1) - s[:, 0:64].max(1)) > 64
+    d = _dev_all(x, "bf16")
+    out = mla.absorbed_attention(dev(q_lat, "bf16"), d["q_pe"], dev(c_kv, "bf16"), dev(k_pe, "bf16"), d["w_uv"],
+                                 offs, scale=x.scale)
+    torch.cuda.synchronize()
+    ref = oracle.latent_attention(q_lat, x.q_pe, c_kv, k_pe, x.w_uv, x.offsets, L, x.scale)
+    # keys scaled up to 81x give outputs of rms up to ~50: the bar is relative only
+    check_close(host64(out).reshape(-1, v), ref, "bf16", f"absorbed_attention {kind}", abs_cap=False)
+
+    Hm = 16
+    xm = _inputs(("wide_m", r, n, v, rope, Hm, L, [kv], "bf16"))
+    K = synth.round_bf16(synth.draw_like((kv, Hm, n + rope), 1.0, "bf16", seed=33) * f[:, None, None])
+    V = synth.draw_like((kv, Hm, v), 1.0, "bf16", seed=34)
+    dm = _dev_all(xm, "bf16")
+    outm = mla.materialized_attention(dm["q_nope"], dm["q_pe"], dev(K, "bf16"), dev(V, "bf16"), offs, scale=xm.scale)
+    torch.cuda.synchronize()
+    refm = oracle.attention(xm.q_nope, xm.q_pe, K, V, xm.offsets, L, xm.scale, n=n)
+    check_close(host64(outm).reshape(refm.shape), refm, "bf16", f"materialized_attention {kind}", abs_cap=False)
