@@ -4,6 +4,7 @@ latent-cache bandwidth, with the roofline of the dominant kernel and the
 float64 CPU oracle timed beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --crossover        # forced-path sweep over L (GLM-4.7-Flash-like geometry)
 
 A step is one whole absorbed verify call over one batch of synthetic inputs
 already resident in device memory: mla_fold_query (q_lat = q_nope . W_UK),
@@ -15,6 +16,12 @@ cache of 8192 positions, L = 8 query rows, bf16 storage, fp32 accumulation.
 Input sets are cloned on the device and rotated step by step so that the
 data of a step has been evicted from L2 and the 256 MB Infinity Cache before
 it is reused (cold); a warm variant reuses one set.  Prints one JSON line.
+
+Other workloads (``--workload``, e.g. the 16-head share of the benchmark
+workload, where HBM rather than MFMA bounds the split kernel) print the same
+line with their own metric name.  ``--crossover`` times the absorbed call
+(fold + attention) against the materialised call (expand + attention) at each
+L of the sweep, arms interleaved sample by sample, and prints one line per L.
 """
 
 from __future__ import annotations
@@ -35,6 +42,8 @@ sys.path.insert(0, ROOT)
 METRIC = "absorbed MLA verify µs/call + latent-cache HBM GB/s (L=8, Kv=8192, H=128)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)   # FLOP per byte where the two bounds meet
+HEADLINE = "dsv3_h128_kv8192_l8_bf16"
 
 # HBM traffic of the split kernel per launch, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
 # (KiB per dispatch) scaled by what the same counters read for a plain 256 MiB device copy
@@ -66,6 +75,9 @@ def parse():
                     help="total bytes of rotated input sets (cold protocol); 0 = warm only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--crossover", action="store_true",
+                    help="forced-path sweep: absorbed vs materialised call at each L of the sweep")
+    ap.add_argument("--samples", type=int, default=15, help="samples per arm and L (--crossover)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -93,6 +105,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
+        return
+    if args.crossover:
+        crossover(args)
         return
     lib = _lib.load()
     blib = ctypes.CDLL(os.path.join(ROOT, "mla_speculative_decode_amd", "libmla_bench.so"))
@@ -126,7 +141,7 @@ def main():
         return arr
 
     def run(idx, steps, warmup):
-        res = (ctypes.c_double * 6)()
+        res = (ctypes.c_double * 8)()
         torch.cuda.synchronize()
         rc = blib.mlab_absorbed_run(
             ctypes.byref(geom), B, L, len(idx), ptrs("q_nope", idx), ptrs("q_pe", idx), ptrs("c_kv", idx),
@@ -149,14 +164,25 @@ def main():
     vis = sum(int(H * (kv * L - L * (L - 1) // 2)) for kv in lens)          # sum over rows of visible positions
     attn_flop = 2.0 * (2 * w.r + w.rope) * vis                            # scores (r+rope) + latent PV (r)
     cache_bytes = float(lens.sum() * (w.r + w.rope) * 2)
+    q_bytes = float(B * L * H * (w.r + w.rope) * 2)                       # q_lat + q_pe read by the split kernel
     weight_bytes = float(2 * H * w.n * w.r * 2)                            # W_UK + W_UV, bf16
-    us_step, us_fold, us_split, us_merge, us_evented, us_split_b2b = cold
+    us_step, us_fold, us_split, us_merge, us_evented, us_split_b2b, us_merge_b2b, us_fold_b2b = cold
     # roofline of the split kernel: its launches back to back (per-launch duration
     # without the dispatch gap that an event pair around one launch also measures)
-    achieved_tflops = attn_flop / (us_split_b2b * 1e-6) / 1e12
+    intensity = attn_flop / cache_bytes
+    if intensity >= RIDGE:
+        achieved = attn_flop / (us_split_b2b * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = (cache_bytes + q_bytes) / (us_split_b2b * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    roof = {"kernel": "attn_bf16_kernel (mla_absorbed_splits)", **roof, "duration_us": round(us_split_b2b, 3),
+            "traffic": split_traffic_bytes() if w.name == HEADLINE else None}
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == HEADLINE else f"absorbed MLA verify µs/call + latent-cache HBM GB/s ({w.name})",
         "value": round(us_step, 3),
         "unit": "us/call",
         "n_gpus": 1,
@@ -169,23 +195,112 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/r) weights)",
         "config": {"workload": w.name, "r": w.r, "n": w.n, "v": w.v, "rope": w.rope, "heads": H, "batch": B,
-                   "kv": int(lens.max()), "L": L, "cache_state": f"cold ({nsets} rotated input sets)"},
+                   "kv": int(lens.max()), "kv_total": int(lens.sum()), "L": L,
+                   "cache_state": f"cold ({nsets} rotated input sets)"},
         "latent_cache_GBps": round(cache_bytes / (us_split_b2b * 1e-6) / 1e9, 1),
+        "latent_cache_GBps_split_merge": round(cache_bytes / ((us_split_b2b + us_merge_b2b) * 1e-6) / 1e9, 1),
         "step_GBps": round((cache_bytes + weight_bytes) / (us_step * 1e-6) / 1e9, 1),
+        "flop_per_cache_byte": round(intensity, 1),
         "per_launch_us": {"fold": round(us_fold, 3), "splits": round(us_split, 3), "merge": round(us_merge, 3),
-                          "splits_back_to_back": round(us_split_b2b, 3)},
+                          "splits_back_to_back": round(us_split_b2b, 3),
+                          "merge_back_to_back": round(us_merge_b2b, 3), "fold_back_to_back": round(us_fold_b2b, 3)},
         "warm_us_per_call": round(warm[0], 3),
-        "warm_per_launch_us": {"fold": round(warm[1], 3), "splits": round(warm[2], 3), "merge": round(warm[3], 3)},
-        "roofline": {"kernel": "attn_bf16_kernel (mla_absorbed_splits)", "bound": "mfma",
-                     "duration_us": round(us_split_b2b, 3),
-                     "achieved": round(achieved_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4), "traffic": split_traffic_bytes()},
+        "warm_per_launch_us": {"fold": round(warm[1], 3), "splits": round(warm[2], 3), "merge": round(warm[3], 3),
+                               "splits_back_to_back": round(warm[5], 3)},
+        "roofline": roof,
         "wall_s": round(wall, 3),
     }
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def crossover(args):
+    """Forced-path sweep on the GLM-4.7-Flash-like workload (r 512, n 192, v 256,
+    rope 64, 32 heads, one sequence of 8192 positions): at each L, the absorbed
+    call (fold + attention) and the materialised call (expand K/V + attention),
+    interleaved sample by sample.  Each sample starts after a 512 MiB scrub write
+    (inputs evicted from L2 and the Infinity Cache) and a device-side delay, so
+    that the host has enqueued the whole call before the first event is passed:
+    the event pair then measures device time only."""
+    import torch
+    import mla_speculative_decode_amd as mla
+    from mla_speculative_decode_amd import synth
+
+    w = synth.WORKLOADS["glm47_h32_kv8192_bf16"]
+    dev = torch.device("cuda:0")
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # device delay of about 2 ms (torch's spin kernel, calibrated here)
+    torch.cuda._sleep(1000)
+    e0.record()
+    torch.cuda._sleep(1_000_000)
+    e1.record()
+    torch.cuda.synchronize()
+    spin = int(1_000_000 * 2.0 / max(e0.elapsed_time(e1), 1e-3))
+    geom = mla.Geom(w.r, w.n, w.v, w.rope, w.heads)
+    rows = []
+    for L in synth.SWEEP_L:
+        x = synth.make_inputs(w, L=L)
+        d = {k: torch.from_numpy(getattr(x, k)).to(torch.bfloat16).to(dev).contiguous()
+             for k in ("q_nope", "q_pe", "c_kv", "k_pe", "w_uk", "w_uv")}
+        offs = mla.Offsets(x.offsets.astype(np.int32), dev)
+        T = int(x.offsets[-1])
+        q_lat = torch.empty((1, L, w.heads, w.r), dtype=torch.bfloat16, device=dev)
+        out_a = torch.empty((1, L, w.heads, w.v), dtype=torch.float32, device=dev)
+        out_m = torch.empty_like(out_a)
+        ws_a = torch.empty(max(256, mla.absorbed_workspace_size(geom, 1, L, offs)), dtype=torch.uint8, device=dev)
+        gm = mla.Geom(1, w.n, w.v, w.rope, w.heads)
+        ws_m = torch.empty(max(256, mla.materialized_workspace_size(gm, 1, L, offs)), dtype=torch.uint8, device=dev)
+        K = torch.empty((T, w.heads, w.n + w.rope), dtype=torch.bfloat16, device=dev)
+        V = torch.empty((T, w.heads, w.v), dtype=torch.bfloat16, device=dev)
+
+        def absorbed():
+            mla.fold_query(d["q_nope"], d["w_uk"], out=q_lat)
+            mla.absorbed_attention(q_lat, d["q_pe"], d["c_kv"], d["k_pe"], d["w_uv"], offs, scale=x.scale,
+                                   out=out_a, workspace=ws_a)
+
+        def materialized():
+            mla.materialize_kv(d["c_kv"], d["k_pe"], d["w_uk"], d["w_uv"], k=K, v=V)
+            mla.materialized_attention(d["q_nope"], d["q_pe"], K, V, offs, scale=x.scale, out=out_m, workspace=ws_m)
+
+        arms = {"absorbed": absorbed, "materialized": materialized}
+        for f in arms.values():
+            f()
+            f()
+        times = {a: [] for a in arms}
+        for i in range(args.samples):
+            order = ("absorbed", "materialized") if i % 2 == 0 else ("materialized", "absorbed")
+            for a in order:
+                scrub.fill_(i & 255)
+                torch.cuda._sleep(spin)
+                e0.record()
+                arms[a]()
+                e1.record()
+                torch.cuda.synchronize()
+                times[a].append(e0.elapsed_time(e1) * 1e3)
+        diff = float(torch.max(torch.abs(out_a - out_m)))
+        path, max_abs = mla.select_path(geom, L, T)
+        med = {a: float(np.median(t)) for a, t in times.items()}
+        row = {"crossover": w.name, "L": L, "T": T,
+               "absorbed_us": round(med["absorbed"], 2), "materialized_us": round(med["materialized"], 2),
+               "absorbed_us_min": round(min(times["absorbed"]), 2),
+               "materialized_us_min": round(min(times["materialized"]), 2),
+               "faster": min(med, key=med.get), "ratio_mat_over_abs": round(med["materialized"] / med["absorbed"], 3),
+               "formula_path": "absorbed" if path == mla.MLA_ABSORBED else "materialized",
+               "formula_max_absorbed": max_abs, "max_abs_diff_paths": diff, "samples": args.samples,
+               "cache_state": "cold (512 MiB scrub before each sample)"}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del d, q_lat, out_a, out_m, ws_a, ws_m, K, V
+        torch.cuda.empty_cache()
+    # measured crossover: between the last L where absorbed is faster and the first where it is not
+    last_abs = max([r["L"] for r in rows if r["faster"] == "absorbed"], default=None)
+    first_mat = min([r["L"] for r in rows if r["faster"] == "materialized"], default=None)
+    print(json.dumps({"crossover_summary": w.name, "absorbed_faster_up_to_L": last_abs,
+                      "materialized_faster_from_L": first_mat, "formula_max_absorbed": rows[0]["formula_max_absorbed"]}),
+          flush=True)
 
 
 def cpu_baseline(x, target_s: float):

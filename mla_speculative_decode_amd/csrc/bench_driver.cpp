@@ -43,6 +43,8 @@ extern "C" {
 // res[4] us/step of the evented run
 // res[5] us per mla_absorbed_splits launch, launches back to back over the same
 //        rotation of input sets (events only around the run)
+// res[6] us per mla_absorbed_merge launch, back to back (same rotation)
+// res[7] us per mla_fold_query launch, back to back (same rotation)
 int mlab_absorbed_run(const mla_geom* g, int B, int L, int nsets, void* const* q_nope, void* const* q_pe,
                       void* const* c_kv, void* const* k_pe, void* const* w_uk, void* const* w_uv,
                       void* const* q_lat, float* const* out, const int32_t* off_h, const int32_t* off_d,
@@ -97,6 +99,26 @@ int mlab_absorbed_run(const mla_geom* g, int B, int L, int nsets, void* const* q
   hipStreamSynchronize(st);
   hipEventElapsedTime(&ms, a, b);
   res[5] = 1e3 * ms / steps;
+
+  hipEventRecord(a, st);
+  for (int i = 0; i < steps; ++i) {
+    const int k = i % nsets;
+    if ((rc = mla_absorbed_merge(g, MLA_BF16, B, L, off_h, off_d, s.w_uv[k], s.out[k], ws, ws_bytes, st))) return rc;
+  }
+  hipEventRecord(b, st);
+  hipStreamSynchronize(st);
+  hipEventElapsedTime(&ms, a, b);
+  res[6] = 1e3 * ms / steps;
+
+  hipEventRecord(a, st);
+  for (int i = 0; i < steps; ++i) {
+    const int k = i % nsets;
+    if ((rc = mla_fold_query(g, MLA_BF16, (int64_t)B * L, s.q_nope[k], s.w_uk[k], s.q_lat[k], st))) return rc;
+  }
+  hipEventRecord(b, st);
+  hipStreamSynchronize(st);
+  hipEventElapsedTime(&ms, a, b);
+  res[7] = 1e3 * ms / steps;
   for (auto& e : ev) hipEventDestroy(e);
   hipEventDestroy(a);
   hipEventDestroy(b);

@@ -9,10 +9,9 @@
 //
 // bf16 uses MFMA with fp32 accumulation.  MFMA operands need the contraction
 // index contiguous per lane; W_UK [H, n, r] (fold contracts over n) and W_UV
-// [H, r, v] (the expand contracts over r) store it strided: the fold's
-// small-M GEMM reads those fragments transposed from LDS (ds_read_b64_tr_b16),
-// the expand transposes its W_UV tiles in registers (8x8 bf16 blocks) on the
-// way into LDS.  The fold is a small-M product (M = B*L rows per head): each
+// [H, r, v] (the expand contracts over r) store it strided: both the fold's
+// small-M GEMM and the expand read those fragments transposed from LDS
+// (ds_read_b64_tr_b16).  The fold is a small-M product (M = B*L rows per head): each
 // workgroup reads its weight tile once for up to 64 rows, the weight stream
 // being the cost.  float32 uses plain VALU loops.
 
@@ -171,147 +170,182 @@ hipError_t fold_query(mla_dtype_t dt, int rows, int H, int n, int r, const void*
 }
 
 // ---------------------------------------------------------------------------
-// expand, bf16: C[T x H(n+v)] = c_kv[T x r] . [W_UK[h]^T | W_UV[h]]_h.
-// Workgroup tile 128 positions x 128 columns, as two 64-column halves that
-// each lie inside one head's K part or V part; k steps of 32.  Wave (wm, wn)
-// computes rows 64wm.., half wn as 2x2 blocks of 32x32.
+// expand, bf16: two plain GEMMs over the cached latent A = c_kv [T x r]
+// (contraction over r, fp32 accumulation, bf16 results):
+//   K part (NN = false): C[t, q] = sum_c A[t, c] W_UK[q, c] with W_UK viewed
+//       as [(H n) x r], q = h n + j; C[t, q] is stored at K[t, q / n, q % n];
+//   V part (NN = true):  C[t, q] = sum_c A[t, c] W_UV[q / v, c, q % v], and C
+//       is V viewed as [T x (H v)].
+// Workgroup tile 128 positions x 128 columns; k steps of 64, double-buffered
+// in LDS and filled by direct-to-LDS loads (each wave instruction writes 1 KB,
+// lane l at bytes 16l..16l+15).  Which global 16-byte chunk a lane fetches
+// sets an XOR swizzle of the chunks inside an LDS row, so the fragment reads
+// are free of bank conflicts without padding.  The product is computed
+// transposed, C^T = B^T A^T, in 32x32x16 MFMAs (wave (wm, wn) owns 64 x 64),
+// so a lane holds 4 consecutive output columns of one position; the tile is
+// staged through LDS and leaves with 16-byte row-contiguous stores.  Items
+// are ordered so that each XCD takes one contiguous range of column tiles for
+// all row tiles: its weight tiles stay in its L2 while the latent rows pass.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int ab_phys(int row, int ch) { return ch ^ ((row >> 1) & 3); }
+struct ExpandArgs {
+  const uint16_t* a;   // c_kv [T, r]
+  const uint16_t* w;   // W_UK [H, n, r] (K part) or W_UV [H, r, v] (V part)
+  uint16_t* out;       // K [T, H, n + rope] or V [T, H, v]
+  long long T;
+  int H, r, n, v, rope;
+  int ncols;           // H n (K part) or H v (V part)
+  int MT, NTX;         // row tiles; column tiles per XCD
+  int n_items;         // kXcds * MT * NTX
+};
 
-__global__ __launch_bounds__(256) void expand_bf16_kernel(const uint16_t* __restrict__ c_kv,
-                                                          const uint16_t* __restrict__ w_uk,
-                                                          const uint16_t* __restrict__ w_uv,
-                                                          uint16_t* __restrict__ Kout, uint16_t* __restrict__ Vout,
-                                                          long long T, int H, int r, int n, int v, int rope,
-                                                          int CT, int n_items) {
-  __shared__ __attribute__((aligned(16))) uint8_t as_[128 * 64];
-  __shared__ __attribute__((aligned(16))) uint8_t bs_[128 * 64];
+template <bool NN>
+__global__ __launch_bounds__(256, 2) void expand_gemm_kernel(ExpandArgs p) {
+  constexpr int BM = 128, BN = 128, BK = 64;
+  constexpr int ABYTES = BM * BK * 2;     // rows of 128 B (8 chunks)
+  constexpr int BBYTES = BN * BK * 2;     // NT: rows of 128 B per column; NN: rows of 256 B per k
+  constexpr int STAGE = ABYTES + BBYTES;
+  constexpr int CP = BN * 2 + 16;         // staging row pitch of the output tile (bytes)
+  static_assert(BM * CP <= 2 * STAGE, "output staging fits in the stage buffers");
+  __shared__ __attribute__((aligned(1024))) uint8_t sm[2 * STAGE];
+
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
-  const int item = xcd_item(blockIdx.x, n_items);
-  if (item >= n_items) return;
-  const int ct = item % CT;
-  const long long t0 = (long long)(item / CT) * 128;
-  const int NC = n + v;
-  const int ncols = H * NC;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int item = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, p.n_items));
+  if (item >= p.n_items) return;
+  const int per = p.MT * p.NTX;
+  const int xb = item / per, rem = item - xb * per;
+  const int mt = rem / p.NTX;
+  const int nt = __builtin_amdgcn_readfirstlane(xb * p.NTX + (rem - mt * p.NTX));
+  if (nt * BN >= p.ncols) return;
+  const long long t0 = (long long)mt * BM;
+  const int q0 = nt * BN;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
 
-  int hh[2], j0[2];
-  bool isK[2], act[2];
+  // per-lane source offsets (elements) that do not change with the k step
+  long long a_src[4];
+  long long b_src[4];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int col0 = ct * 128 + 64 * hf;
-    act[hf] = col0 < ncols;
-    const int cc = act[hf] ? col0 : 0;
-    hh[hf] = cc / NC;
-    const int x = cc % NC;
-    isK[hf] = x < n;
-    j0[hf] = isK[hf] ? x : x - n;
+  for (int i = 0; i < 4; ++i) {
+    const int x = w + 4 * i;                       // instruction slot: 1 KB of the tile
+    const int row = 8 * x + (lane >> 3);           // A: 8 rows of 8 chunks per instruction
+    const int c = (lane & 7) ^ (lane >> 3);        // logical chunk landing in physical slot lane & 7
+    long long t = t0 + row;
+    t = t < p.T ? t : p.T - 1;
+    a_src[i] = t * p.r + 8 * c;
+    if (!NN) {
+      int q = q0 + row;                            // weight row = output column
+      q = q < p.ncols ? q : p.ncols - 1;
+      b_src[i] = (long long)q * p.r + 8 * c;
+    } else {
+      const int krow = 4 * x + (lane >> 4);         // 4 k rows of 16 chunks per instruction
+      const int cb = (lane & 15) ^ (2 * (lane >> 4));
+      const int q = min(q0 + 8 * cb, p.ncols - 8);  // 8 columns, inside one head (v % 8 == 0)
+      const int h = q / p.v;
+      b_src[i] = ((long long)h * p.r + krow) * p.v + (q - h * p.v);
+    }
   }
-
-  u32x4 ast[2];
-  u32x4 bst[2][8];
-  auto load = [&](int k0) {
+  auto issue = [&](int k0, uint8_t* dst) {
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int C = tid + 256 * y;
-      const int row = C >> 2, ch = C & 3;
-      long long t = t0 + row;
-      if (t >= T) t = T - 1;
-      ast[y] = ld16(c_kv + t * r + k0 + 8 * ch);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(p.a + a_src[i] + k0, (lds_ptr)(dst + 1024 * (w + 4 * i)), 16, 0, 0);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      if (!act[hf]) continue;
-      if (isK[hf]) {
-        const int col = tid >> 2, ch = tid & 3;
-        bst[hf][0] = ld16(w_uk + ((long long)hh[hf] * n + j0[hf] + col) * r + k0 + 8 * ch);
-      } else if (tid < 32) {
-        const int kg = tid & 3, cc = tid >> 2;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          bst[hf][jj] = ld16(w_uv + ((long long)hh[hf] * r + k0 + 8 * kg + jj) * v + j0[hf] + 8 * cc);
-      }
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int C = tid + 256 * y;
-      const int row = C >> 2, ch = C & 3;
-      st16(as_ + row * 64 + ab_phys(row, ch) * 16, ast[y]);
-    }
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      if (!act[hf]) continue;
-      if (isK[hf]) {
-        const int row = 64 * hf + (tid >> 2), ch = tid & 3;
-        st16(bs_ + row * 64 + ab_phys(row, ch) * 16, bst[hf][0]);
-      } else if (tid < 32) {
-        const int kg = tid & 3, cc = tid >> 2;
-        u32x4 tr[8];
-        transpose8x8_bf16(bst[hf], tr);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int row = 64 * hf + 8 * cc + e;
-          st16(bs_ + row * 64 + ab_phys(row, kg) * 16, tr[e]);
-        }
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(p.w + b_src[i] + (NN ? (long long)k0 * p.v : (long long)k0),
+                                       (lds_ptr)(dst + ABYTES + 1024 * (w + 4 * i)), 16, 0, 0);
   };
 
   const int wm = w >> 1, wn = w & 1;
+  // A / NT-B fragment: row l32 of a 32-row block, logical chunk 2 kc + half
+  const int a_off = (64 * wm + l32) * 128;
+  const int b_off = (64 * wn + l32) * 128;
+  const int sw = lane & 7;                         // row % 8 of every fragment row
+  // NN-B fragment (B^T [32 columns x 16 k] from the [k][column] tile): two
+  // transposing 8-byte reads of 4 k rows each per 16-lane group
+  const int G = lane >> 4, s16 = lane & 15;
+  int tr_off[2];
+#pragma unroll
+  for (int bn = 0; bn < 2; ++bn) {
+    const int krow = 8 * (G >> 1) + (s16 >> 2);
+    const int chunk = 8 * wn + 4 * bn + 2 * (G & 1) + ((s16 & 3) >> 1);
+    tr_off[bn] = krow * 256 + 16 * (chunk ^ (2 * (s16 >> 2))) + 8 * (s16 & 1);
+  }
+
   f32x16 acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int bn = 0; bn < 2; ++bn)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[bn][bm][i] = 0.f;
 
-  const int nks = r / 32;
-  load(0);
-  for (int ks = 0; ks < nks; ++ks) {
-    store();
-    __syncthreads();
-    if (ks + 1 < nks) load(32 * (ks + 1));
-    if (act[wn]) {
+  const int nk = p.r / BK;
+  issue(0, sm);
+  for (int ks = 0; ks < nk; ++ks) {
+    const uint8_t* cur = sm + (ks & 1) * STAGE;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // stage ks landed; every wave is done with the other stage
+    if (ks + 1 < nk) issue(BK * (ks + 1), sm + ((ks + 1) & 1) * STAGE);
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        u32x4 a[2], bv[2];
+    for (int kc = 0; kc < BK / 16; ++kc) {
+      const int ch = 16 * ((2 * kc + half) ^ sw);
+      u32x4 af[2], bf[2];
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm) {
-          const int row = 64 * wm + 32 * bm + l32;
-          a[bm] = *reinterpret_cast<const u32x4*>(as_ + row * 64 + ab_phys(row, 2 * kc + half) * 16);
-        }
-#pragma unroll
-        for (int bn = 0; bn < 2; ++bn) {
-          const int row = 64 * wn + 32 * bn + l32;
-          bv[bn] = *reinterpret_cast<const u32x4*>(bs_ + row * 64 + ab_phys(row, 2 * kc + half) * 16);
-        }
-#pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-          for (int bn = 0; bn < 2; ++bn) acc[bm][bn] = mfma32(a[bm], bv[bn], acc[bm][bn]);
-      }
-    }
-    __syncthreads();
-  }
-  if (!act[wn]) return;
-  const int h = hh[wn];
-#pragma unroll
-  for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const long long t = t0 + 64 * wm + 32 * bm + 8 * (i >> 2) + 4 * half + (i & 3);
-      if (t >= T) continue;
+      for (int bm = 0; bm < 2; ++bm) af[bm] = *reinterpret_cast<const u32x4*>(cur + a_off + bm * 32 * 128 + ch);
 #pragma unroll
       for (int bn = 0; bn < 2; ++bn) {
-        const int j = j0[wn] + 32 * bn + l32;
-        const uint16_t o = __builtin_bit_cast(uint16_t, (__bf16)acc[bm][bn][i]);
-        if (isK[wn]) Kout[(t * H + h) * (n + rope) + j] = o;
-        else Vout[(t * H + h) * v + j] = o;
+        if (!NN) {
+          bf[bn] = *reinterpret_cast<const u32x4*>(cur + ABYTES + b_off + bn * 32 * 128 + ch);
+        } else {
+#pragma unroll
+          for (int ld = 0; ld < 2; ++ld) {
+            const uint8_t* src = cur + ABYTES + tr_off[bn] + (16 * kc + 4 * ld) * 256;
+            const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src));
+            const u32x2 rr = __builtin_bit_cast(u32x2, r);
+            bf[bn][2 * ld] = rr[0];
+            bf[bn][2 * ld + 1] = rr[1];
+          }
+        }
+      }
+#pragma unroll
+      for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm) acc[bn][bm] = mfma32(bf[bn], af[bm], acc[bn][bm]);   // C^T += B^T A^T
+    }
+  }
+
+  // epilogue: C^T block (bn, bm), lane: position 32 bm + l32, columns
+  // 32 bn + 8 (i / 4) + 4 half + (i % 4) -> bf16 staging [128 positions][128 columns]
+  __syncthreads();   // every wave is done with the stage buffers
+#pragma unroll
+  for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int m = 64 * wm + 32 * bm + l32;
+        const int nn = 64 * wn + 32 * bn + 8 * qd + 4 * half;
+        u32x2 v;
+        v[0] = pack_bf16(acc[bn][bm][4 * qd], acc[bn][bm][4 * qd + 1]);
+        v[1] = pack_bf16(acc[bn][bm][4 * qd + 2], acc[bn][bm][4 * qd + 3]);
+        *reinterpret_cast<u32x2*>(sm + m * CP + nn * 2) = v;
+      }
+  __syncthreads();
+#pragma unroll
+  for (int rd = 0; rd < BM * BN / 8 / 256; ++rd) {
+    const int e = tid + 256 * rd;
+    const int row = e >> 4, ch = e & 15;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(sm + row * CP + 16 * ch);
+    const long long t = t0 + row;
+    const int q = q0 + 8 * ch;
+    if (t < p.T && q < p.ncols) {
+      if (NN) {
+        st16(p.out + t * p.ncols + q, val);
+      } else {
+        const int h = q / p.n, j = q - h * p.n;     // n % 8 == 0: the 8 columns share a head
+        st16(p.out + (t * p.H + h) * (p.n + p.rope) + j, val);
       }
     }
+  }
 }
 
 // K[t, h, n:n+rope] = k_pe[t, :], 16 bytes per thread.
@@ -361,14 +395,25 @@ hipError_t materialize_kv(mla_dtype_t dt, long long T, int H, int r, int n, int 
                           hipStream_t st) {
   if (dt == kBF16) {
     if (r % 64 != 0 || n % 64 != 0 || v % 64 != 0 || rope % 8 != 0) return hipErrorInvalidValue;
-    const int CT = (H * (n + v) + 127) / 128;
-    const long long TT = (T + 127) / 128;
-    const long long n_items = TT * CT;
-    if (n_items > (1LL << 30)) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)(((n_items + kXcds - 1) / kXcds) * kXcds);
-    hipLaunchKernelGGL(expand_bf16_kernel, dim3(grid), dim3(256), 0, st, (const uint16_t*)c_kv,
-                       (const uint16_t*)w_uk, (const uint16_t*)w_uv, (uint16_t*)k, (uint16_t*)vout, T, H, r, n, v,
-                       rope, CT, (int)n_items);
+    ExpandArgs a{};
+    a.a = (const uint16_t*)c_kv;
+    a.T = T;
+    a.H = H; a.r = r; a.n = n; a.v = v; a.rope = rope;
+    a.MT = (int)((T + 127) / 128);
+    for (int part = 0; part < 2; ++part) {
+      a.w = (const uint16_t*)(part == 0 ? w_uk : w_uv);
+      a.out = (uint16_t*)(part == 0 ? k : vout);
+      a.ncols = H * (part == 0 ? n : v);
+      const int nt = (a.ncols + 127) / 128;
+      a.NTX = (nt + kXcds - 1) / kXcds;
+      const long long n_items = (long long)kXcds * a.MT * a.NTX;
+      if (n_items > (1LL << 30)) return hipErrorInvalidValue;
+      a.n_items = (int)n_items;
+      if (part == 0)
+        hipLaunchKernelGGL(expand_gemm_kernel<false>, dim3((unsigned)n_items), dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL(expand_gemm_kernel<true>, dim3((unsigned)n_items), dim3(256), 0, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || rope == 0) return e;
     const long long tot = T * H * (rope / 8);

@@ -75,6 +75,13 @@ WORKLOADS = {
     # DeepSeek-V3 geometry, 128 heads, 32 sequences with Kv ~ U[1024, 32768], 8 rows each.
     "dsv3_h128_b32_varlen_l8_bf16": Workload("dsv3_h128_b32_varlen_l8_bf16", 512, 128, 128, 64, 128, 32, 8,
                                              kv_range=(1024, 32768), dtype="bf16", seed=5),
+    # 16-head shares of the two DeepSeek-V3 workloads above (one GPU's heads when 8 GPUs
+    # split the 128 heads): the latent cache is the same size, the rows 8x fewer, so HBM
+    # rather than MFMA bounds the attention.  Same seeds, so the batch draws the same lengths.
+    "dsv3_h16_kv8192_l8_bf16": Workload("dsv3_h16_kv8192_l8_bf16", 512, 128, 128, 64, 16, 1, 8,
+                                        kv=8192, dtype="bf16", seed=2),
+    "dsv3_h16_b32_varlen_l8_bf16": Workload("dsv3_h16_b32_varlen_l8_bf16", 512, 128, 128, 64, 16, 32, 8,
+                                            kv_range=(1024, 32768), dtype="bf16", seed=5),
 }
 
 # Query-row counts of the forced-path sweep on the GLM-4.7-Flash-like workload.
