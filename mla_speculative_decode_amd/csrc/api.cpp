@@ -43,7 +43,10 @@ int check_offsets(int32_t B, int32_t L, const int32_t* off) {
 
 // Split-KV plan: aim for about one workgroup per compute unit on a single
 // sequence and about four per unit across a batch (variable lengths need the
-// slack to balance), never splitting finer than one 64-position tile.
+// slack to balance).  Splits hold an even number of 64-position tiles (the
+// split kernel takes tiles in pairs, one per LDS buffer), at least two: with
+// few query rows a finer cut would only multiply the partial sums that the
+// merge has to read back.
 int make_plan(int32_t B, int32_t L, int32_t H, const int32_t* off, int rows_slot, int head_slots, int DV,
               int o_elem_bytes, SplitPlan* p) {
   const int64_t row_tiles = (rows_slot + kTile - 1) / kTile;
@@ -51,7 +54,7 @@ int make_plan(int32_t B, int32_t L, int32_t H, const int32_t* off, int rows_slot
   for (int32_t b = 0; b < B; ++b) total_tiles += (off[b + 1] - off[b] + kTile - 1) / kTile;
   const int64_t units = row_tiles * head_slots * total_tiles;
   const int64_t target = (int64_t)kCUs * (B > 1 ? 4 : 1);
-  const int64_t chunk_tiles = std::max<int64_t>(1, (units + target - 1) / target);
+  const int64_t chunk_tiles = std::max<int64_t>(2, ((units + target - 1) / target + 1) / 2 * 2);
   if (chunk_tiles * kTile > INT32_MAX) return MLA_E_SHAPE;
   const int chunk = (int)(chunk_tiles * kTile);
   int64_t splits = 0;

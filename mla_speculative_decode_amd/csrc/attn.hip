@@ -387,20 +387,21 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     auto write_p = [&](float mref, float* psum) {
       const float mb = mref == -INFINITY ? 0.f : mref;
       float e[16];
-      float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(fmaf(s[i], p.sl2, -mb));
-        ps += e[i];
-      }
+      for (int i = 0; i < 16; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[i], p.sl2, -mb));
+      // the row sum adds the bf16 weights that PV uses, so that numerator and
+      // denominator carry the same rounding (exact for a row led by one key)
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         u32x2 v;
         v[0] = pack_bf16(e[4 * q + 0], e[4 * q + 1]);
         v[1] = pack_bf16(e[4 * q + 2], e[4 * q + 3]);
         *reinterpret_cast<u32x2*>(prow + 16 * q) = v;
+        ps0 = add_bf16x2(v[0], ps0);
+        ps1 = add_bf16x2(v[1], ps1);
       }
-      *psum = ps;
+      *psum = ps0 + ps1;
     };
     float psum;
     write_p(m_run, &psum);
@@ -489,12 +490,10 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     if (VK && pf) store_rope(nxt);   // the other buffer is not read until barrier (A)
     return false;
   };
-  // Tiles go in pairs (one per buffer) with no branch between them, so the
-  // accumulators flow straight through the loop; an odd tile count ends with
-  // a tile past the split (a clamped copy of the last position), whose keys
-  // all fail key < kend and add nothing.  No copy follows the last pair.
+  // Tiles go in pairs (one per buffer); an odd tile count skips the second
+  // step of the last pair.  No copy follows the last tile.
   for (int t0 = k0; t0 < k1; t0 += 2 * BN) {
-    if (step(t0, buf0, buf1, true) || step(t0 + BN, buf1, buf0, t0 + 2 * BN < k1)) {
+    if (step(t0, buf0, buf1, t0 + BN < k1) || (t0 + BN < k1 && step(t0 + BN, buf1, buf0, t0 + 2 * BN < k1))) {
       // restart (rare, uniform): drop the partial sums, reload the first tile.  Each
       // restart is triggered by a tile past every tile already processed, so the
       // number of restarts is bounded by the number of tiles.

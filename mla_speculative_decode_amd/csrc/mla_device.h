@@ -37,6 +37,12 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 // ---- bfloat16 ----------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// acc + lo + hi of a packed bf16 pair, in one dot-product instruction (weights 1, 1)
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Round-to-nearest-even pack of two floats: one v_cvt_pk_bf16_f32 on gfx950.
