@@ -41,20 +41,38 @@ int check_offsets(int32_t B, int32_t L, const int32_t* off) {
   return MLA_OK;
 }
 
-// Split-KV plan: aim for about one workgroup per compute unit on a single
-// sequence and about four per unit across a batch (variable lengths need the
-// slack to balance).  Splits hold an even number of 64-position tiles (the
-// split kernel takes tiles in pairs, one per LDS buffer), at least two: with
-// few query rows a finer cut would only multiply the partial sums that the
-// merge has to read back.
+// Split-KV plan.  A workgroup of the bf16 kernels takes 64 query rows x one
+// split; splits hold an even number of 64-position tiles (the kernel takes
+// tiles in pairs, one per LDS buffer), at least two.
+//   B == 1, bf16: the split count minimises a model of the kernel pair in
+//     units of one tile's time: rounds of workgroups over the CUs x (tiles per
+//     split + 2 for the prologue and epilogue), plus the merge's read-back of
+//     the partial sums (8 MiB per unit).  Rounds matter: 398 workgroups on 256
+//     CUs take two full rounds.
+//   otherwise: about one workgroup per CU for one sequence, four per CU for a
+//     batch (variable lengths need the slack to balance).
 int make_plan(int32_t B, int32_t L, int32_t H, const int32_t* off, int rows_slot, int head_slots, int DV,
-              int o_elem_bytes, SplitPlan* p) {
+              int o_elem_bytes, bool bf16, SplitPlan* p) {
   const int64_t row_tiles = (rows_slot + kTile - 1) / kTile;
   int64_t total_tiles = 0;
   for (int32_t b = 0; b < B; ++b) total_tiles += (off[b + 1] - off[b] + kTile - 1) / kTile;
   const int64_t units = row_tiles * head_slots * total_tiles;
   const int64_t target = (int64_t)kCUs * (B > 1 ? 4 : 1);
-  const int64_t chunk_tiles = std::max<int64_t>(2, ((units + target - 1) / target + 1) / 2 * 2);
+  auto even = [](int64_t t) { return std::max<int64_t>(2, (t + 1) / 2 * 2); };
+  int64_t chunk_tiles = even((units + target - 1) / target);
+  if (B == 1 && bf16) {
+    const int64_t wg_per_split = row_tiles * head_slots;
+    const double merge_unit = (double)rows_slot * head_slots * DV * o_elem_bytes / (8.0 * 1024 * 1024);
+    double best = -1.0;
+    const int64_t smax = std::min<int64_t>(total_tiles, 8 * kCUs);
+    for (int64_t s = 1; s <= smax; ++s) {
+      const int64_t ct = even((total_tiles + s - 1) / s);
+      const int64_t ns = (total_tiles + ct - 1) / ct;
+      const int64_t rounds = (ns * wg_per_split + kCUs - 1) / kCUs;
+      const double cost = (double)rounds * (double)(ct + 2) + merge_unit * (double)ns;
+      if (best < 0.0 || cost < best) { best = cost; chunk_tiles = ct; }
+    }
+  }
   if (chunk_tiles * kTile > INT32_MAX) return MLA_E_SHAPE;
   const int chunk = (int)(chunk_tiles * kTile);
   int64_t splits = 0;
@@ -156,7 +174,8 @@ int mla_absorbed_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int3
   if ((int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
   if ((st = absorbed_supported(g, dt))) return st;
   SplitPlan p{};
-  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L * g->heads, 1, g->r, dt == MLA_BF16 ? 2 : 4, &p))) return st;
+  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L * g->heads, 1, g->r, dt == MLA_BF16 ? 2 : 4, dt == MLA_BF16, &p)))
+    return st;
   *bytes_out = p.ws_bytes;
   return MLA_OK;
 }
@@ -183,7 +202,8 @@ int absorbed_prepare(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, cons
   if (need_merge && (!w_uv || !out)) return MLA_E_NULL;
   if ((st = absorbed_supported(g, dt))) return st;
   SplitPlan p{};
-  if ((st = make_plan(B, L, g->heads, off_h, L * g->heads, 1, g->r, dt == MLA_BF16 ? 2 : 4, &p))) return st;
+  if ((st = make_plan(B, L, g->heads, off_h, L * g->heads, 1, g->r, dt == MLA_BF16 ? 2 : 4, dt == MLA_BF16, &p)))
+    return st;
   if (!workspace || workspace_bytes < p.ws_bytes) return MLA_E_WORKSPACE;
   q->r = g->r; q->rope = g->rope; q->v_dim = g->v; q->H = g->heads; q->B = B; q->L = L;
   q->q_lat = q_lat; q->q_pe = q_pe; q->c_kv = c_kv; q->k_pe = k_pe; q->w_uv = w_uv;
@@ -259,7 +279,7 @@ int mla_materialized_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, 
   if ((int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
   if ((st = materialized_supported(g, dt))) return st;
   SplitPlan p{};
-  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L, g->heads, g->v, 4, &p))) return st;
+  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L, g->heads, g->v, 4, dt == MLA_BF16, &p))) return st;
   *bytes_out = p.ws_bytes;
   return MLA_OK;
 }
@@ -278,7 +298,7 @@ int mla_materialized_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32
   if (g->n < 1) return MLA_E_SHAPE;
   if ((st = materialized_supported(g, dt))) return st;
   SplitPlan p{};
-  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L, g->heads, g->v, 4, &p))) return st;
+  if ((st = make_plan(B, L, g->heads, kv_offsets_host, L, g->heads, g->v, 4, dt == MLA_BF16, &p))) return st;
   if (!workspace || workspace_bytes < p.ws_bytes) return MLA_E_WORKSPACE;
   MaterializedLaunch q{};
   q.n = g->n; q.rope = g->rope; q.v_dim = g->v; q.H = g->heads; q.B = B; q.L = L;
