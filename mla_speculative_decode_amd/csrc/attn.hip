@@ -302,6 +302,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
 
   // ---- running state ------------------------------------------------------
   float m_run = -INFINITY, l_run = 0.f;   // score layout: row rq, this wave's key half
+  float t_max = -INFINITY;                 // this lane's largest logit of row rq in the split
   float m_all = -INFINITY;                 // reference of row `lane` (the same in every wave)
   f32x16 O[2][NCB];
 #pragma unroll
@@ -318,10 +319,12 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
                      + (w * CPW + 16 * (G & 1) + 4 * (s16 & 3)) * 2;      // column part
   const int pa_off = l32 * PRB + 16 * half;                               // + rb*32*PRB + 32 kc
 
+  auto row_max_all = [&](int row) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(&red[row * 4]);
+    return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+  };
   // one 64-position tile: scores from `cur`, copy of the next tile into `nxt`
-  // one 64-position tile: scores from `cur`, copy of the next tile into `nxt`;
-  // returns true (uniformly) when the split must restart with raised references
-  auto step = [&](int t0, const uint8_t* cur, uint8_t* nxt, bool pf) -> bool {
+  auto step = [&](int t0, const uint8_t* cur, uint8_t* nxt, bool pf) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // (A) tile t visible; PV(t-1) done, so the other buffer and pl are free
     // The next tile is copied unconditionally (branch-free code keeps the LDS
@@ -378,10 +381,10 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     // first tile that gives it finite scores.  P (bf16) and O, l (fp32) keep
     // their relative precision at any magnitude, so later scores may exceed m
     // by up to kRefSlack (P <= 2^64) and O is never rescaled inside the loop;
-    // a tile that exceeds that restarts the split with the larger reference.
-    // P is computed here against the current reference and published with the
-    // partial maxima; a tile that sets some row's first reference recomputes
-    // it below.  A row without a finite reference uses 0: its masked keys give
+    // a split in which some row exceeds that runs again with raised references
+    // (checked after its last tile).  P is computed here against the current
+    // reference; the first tile, which sets the references, recomputes it
+    // below.  A row without a finite reference uses 0: its masked keys give
     // 2^-inf = 0.
     uint8_t* prow = pl + rq * PRB + 64 * wk + 8 * half;
     auto write_p = [&](float mref, float* psum) {
@@ -405,32 +408,32 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     };
     float psum;
     write_p(m_run, &psum);
-    red[rq * 4 + wk * 2 + half] = pmax;   // maximum over this lane's 16 keys
-    lds_barrier();  // (B) P and partial maxima visible (the next tile's copy stays in flight)
-
-    // Every wave decides for all 64 rows (lane = row) from the same partial
-    // maxima with the same arithmetic, so the decision is uniform over the
-    // workgroup and the branch below (with its barrier) is taken by all waves
-    // or by none.
+    t_max = fmaxf(t_max, pmax);
+    // A row sees a prefix of the split's positions, so every row with finite
+    // scores in the split has them in its first tile: the references are set
+    // there from the tile's row maxima.  Later tiles publish only P; whether
+    // some row outgrew its reference is decided once, after the last tile.
     auto row_max = [&](int row) {
       const f32x4 a = *reinterpret_cast<const f32x4*>(&red[row * 4]);
       return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
     };
-    const float tm_all = row_max(lane);
-    if (__ballot(m_all != -INFINITY && tm_all > m_all + kRefSlack) != 0) {
-      // some row exceeds its reference by more than 2^kRefSlack: raise the
-      // references (this tile's maxima bound every earlier score) and restart
-      m_all = fmaxf(m_all, tm_all);
-      m_run = fmaxf(m_run, row_max(rq));
-      return true;
-    }
-    if (__ballot(m_all == -INFINITY && tm_all != -INFINITY) != 0) {
-      // first finite scores of some rows (O is still 0 there): their reference
-      // is this tile's maximum; the other rows recompute the same P
-      m_all = (m_all == -INFINITY) ? tm_all : m_all;
-      if (m_run == -INFINITY) m_run = row_max(rq);
-      write_p(m_run, &psum);
-      lds_barrier();  // (C) recomputed P visible
+    if (t0 == k0) {
+      red[rq * 4 + wk * 2 + half] = pmax;   // maximum over this lane's 16 keys
+      lds_barrier();  // (B) P and partial maxima visible (the next tile's copy stays in flight)
+      // Every wave decides for all 64 rows (lane = row) from the same partial
+      // maxima with the same arithmetic, so the decision is uniform over the
+      // workgroup and the branch (with its barrier) is taken by all waves or by none.
+      const float tm_all = row_max(lane);
+      if (__ballot(m_all == -INFINITY && tm_all != -INFINITY) != 0) {
+        // first finite scores of some rows (O is still 0 there): their reference
+        // is this tile's maximum; the other rows recompute the same P
+        m_all = (m_all == -INFINITY) ? tm_all : m_all;
+        if (m_run == -INFINITY) m_run = row_max(rq);
+        write_p(m_run, &psum);
+        lds_barrier();  // (C) recomputed P visible
+      }
+    } else {
+      lds_barrier();  // (B) P visible
     }
     l_run += psum;
 
@@ -488,29 +491,39 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       }
     }
     if (VK && pf) store_rope(nxt);   // the other buffer is not read until barrier (A)
-    return false;
   };
   // Tiles go in pairs (one per buffer); an odd tile count skips the second
   // step of the last pair.  No copy follows the last tile.
-  for (int t0 = k0; t0 < k1; t0 += 2 * BN) {
-    if (step(t0, buf0, buf1, t0 + BN < k1) || (t0 + BN < k1 && step(t0 + BN, buf1, buf0, t0 + 2 * BN < k1))) {
-      // restart (rare, uniform): drop the partial sums, reload the first tile.  Each
-      // restart is triggered by a tile past every tile already processed, so the
-      // number of restarts is bounded by the number of tiles.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();   // every wave is done with the tile buffers and pl
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) O[rb][cb][i] = 0.f;
-      l_run = 0.f;
-      issue_tile(k0, buf0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (VK) store_rope(buf0);
-      t0 = k0 - 2 * BN;   // the loop increment brings it back to the first tile
+  for (;;) {
+    for (int t0 = k0; t0 < k1; t0 += 2 * BN) {
+      step(t0, buf0, buf1, t0 + BN < k1);
+      if (t0 + BN < k1) step(t0 + BN, buf1, buf0, t0 + 2 * BN < k1);
     }
+    // Did some row's scores exceed its reference by more than 2^kRefSlack (P up
+    // to 2^kRefSlack keeps fp32 and bf16 exact in relative terms)?  Then its
+    // P, O and l may have overflowed: raise every reference to the row's
+    // maximum over the whole split and run the split again.  The second pass
+    // cannot trigger another, since its references bound every score.
+    __syncthreads();   // every wave is done with red and the tile buffers
+    red[rq * 4 + wk * 2 + half] = t_max;
+    lds_barrier();
+    const float tm_all = row_max_all(lane);
+    if (__ballot(m_all != -INFINITY && tm_all > m_all + kRefSlack) == 0) break;
+    m_all = fmaxf(m_all, tm_all);
+    m_run = fmaxf(m_run, row_max_all(rq));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // the maxima are read before red is written again
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[rb][cb][i] = 0.f;
+    l_run = 0.f;
+    t_max = -INFINITY;
+    issue_tile(k0, buf0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (VK) store_rope(buf0);
   }
 
   // ---- epilogue: row sums, partial results ---------------------------------
