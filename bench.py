@@ -5,6 +5,7 @@ float64 CPU oracle timed beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --crossover        # forced-path sweep over L (GLM-4.7-Flash-like geometry)
+    python bench.py --verify-curve     # verify cost at L = 1..16 and the derived draft cap
 
 A step is one whole absorbed verify call over one batch of synthetic inputs
 already resident in device memory: mla_fold_query (q_lat = q_nope . W_UK),
@@ -78,6 +79,9 @@ def parse():
     ap.add_argument("--crossover", action="store_true",
                     help="forced-path sweep: absorbed vs materialised call at each L of the sweep")
     ap.add_argument("--samples", type=int, default=15, help="samples per arm and L (--crossover)")
+    ap.add_argument("--verify-curve", action="store_true",
+                    help="time the verify call at L = 1..max-width and derive the draft cap from the curve")
+    ap.add_argument("--max-width", type=int, default=16, help="largest L of --verify-curve")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -109,55 +113,17 @@ def main():
     if args.crossover:
         crossover(args)
         return
-    lib = _lib.load()
-    blib = ctypes.CDLL(os.path.join(ROOT, "mla_speculative_decode_amd", "libmla_bench.so"))
-    blib.mlab_absorbed_run.restype = ctypes.c_int
-
+    if args.verify_curve:
+        verify_curve(args)
+        return
     w = synth.WORKLOADS[args.workload]
     if w.dtype != "bf16":
         raise SystemExit("bench.py times the bf16 path")
     x = synth.make_inputs(w)
     B, L, H = w.batch, x.L, w.heads
-    dev = torch.device("cuda:0")
-
-    def up(a):
-        return torch.from_numpy(a).to(torch.bfloat16).to(dev).contiguous()
-
-    base = {k: up(getattr(x, k)) for k in ("q_nope", "q_pe", "c_kv", "k_pe", "w_uk", "w_uv")}
-    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
-    nsets = max(1, int(math.ceil(args.cold_bytes / set_bytes))) if args.cold_bytes > 0 else 1
-    sets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(nsets - 1)]
-    for s in sets:
-        s["q_lat"] = torch.empty((B, L, H, w.r), dtype=torch.bfloat16, device=dev)
-        s["out"] = torch.empty((B, L, H, w.v), dtype=torch.float32, device=dev)
-    offs = mla.Offsets(x.offsets.astype(np.int32), dev)
-    geom = mla.Geom(w.r, w.n, w.v, w.rope, H)
-    ws_bytes = mla.absorbed_workspace_size(geom, _lib.MLA_BF16, L, offs)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.Stream()
-
-    def ptrs(key, idx):
-        arr = (ctypes.c_void_p * len(idx))(*[sets[i][key].data_ptr() for i in idx])
-        return arr
-
-    def run(idx, steps, warmup):
-        res = (ctypes.c_double * 8)()
-        torch.cuda.synchronize()
-        rc = blib.mlab_absorbed_run(
-            ctypes.byref(geom), B, L, len(idx), ptrs("q_nope", idx), ptrs("q_pe", idx), ptrs("c_kv", idx),
-            ptrs("k_pe", idx), ptrs("w_uk", idx), ptrs("w_uv", idx), ptrs("q_lat", idx), ptrs("out", idx),
-            offs.host_ptr(), offs.dev_ptr(), ctypes.c_float(x.scale), ctypes.c_void_p(ws.data_ptr()),
-            ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream), warmup, steps, res)
-        torch.cuda.synchronize()
-        if rc != 0:
-            raise RuntimeError(f"bench step failed: {lib.mla_status_string(rc).decode()}")
-        return list(res)
-
-    # timed region: W untimed steps, then K steps between synchronisations
     t0 = time.perf_counter()
-    cold = run(list(range(nsets)), args.steps, args.warmup)
+    cold, warm, nsets = absorbed_timing(w, x, args.cold_bytes, args.steps, args.warmup)
     wall = time.perf_counter() - t0
-    warm = run([0], args.steps, args.warmup)
 
     # algorithmic work of one call
     lens = np.diff(x.offsets)
@@ -214,6 +180,86 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def absorbed_timing(w, x, cold_bytes, steps, warmup):
+    """Time the absorbed verify call on inputs x through the native loop: the
+    cold rotation of cloned input sets, then one warm set.  Returns the result
+    arrays of both runs (see bench_driver.cpp) and the number of sets."""
+    import torch
+    import mla_speculative_decode_amd as mla
+    from mla_speculative_decode_amd import _lib
+
+    lib = _lib.load()
+    blib = ctypes.CDLL(os.path.join(ROOT, "mla_speculative_decode_amd", "libmla_bench.so"))
+    blib.mlab_absorbed_run.restype = ctypes.c_int
+    B, L, H = w.batch, x.L, w.heads
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(a).to(torch.bfloat16).to(dev).contiguous()
+
+    base = {k: up(getattr(x, k)) for k in ("q_nope", "q_pe", "c_kv", "k_pe", "w_uk", "w_uv")}
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    nsets = max(1, int(math.ceil(cold_bytes / set_bytes))) if cold_bytes > 0 else 1
+    sets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(nsets - 1)]
+    for st in sets:
+        st["q_lat"] = torch.empty((B, L, H, w.r), dtype=torch.bfloat16, device=dev)
+        st["out"] = torch.empty((B, L, H, w.v), dtype=torch.float32, device=dev)
+    offs = mla.Offsets(x.offsets.astype(np.int32), dev)
+    geom = mla.Geom(w.r, w.n, w.v, w.rope, H)
+    ws_bytes = mla.absorbed_workspace_size(geom, _lib.MLA_BF16, L, offs)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+
+    def ptrs(key, idx):
+        return (ctypes.c_void_p * len(idx))(*[sets[i][key].data_ptr() for i in idx])
+
+    def run(idx):
+        res = (ctypes.c_double * 8)()
+        torch.cuda.synchronize()
+        rc = blib.mlab_absorbed_run(
+            ctypes.byref(geom), B, L, len(idx), ptrs("q_nope", idx), ptrs("q_pe", idx), ptrs("c_kv", idx),
+            ptrs("k_pe", idx), ptrs("w_uk", idx), ptrs("w_uv", idx), ptrs("q_lat", idx), ptrs("out", idx),
+            offs.host_ptr(), offs.dev_ptr(), ctypes.c_float(x.scale), ctypes.c_void_p(ws.data_ptr()),
+            ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream), warmup, steps, res)
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError(f"bench step failed: {lib.mla_status_string(rc).decode()}")
+        return list(res)
+
+    # timed region: W untimed steps, then K steps between synchronisations
+    cold = run(list(range(nsets)))
+    warm = run([0])
+    return cold, warm, nsets
+
+
+def verify_curve(args):
+    """Verify-width cost curve of the benchmark geometry (DeepSeek-V3 MLA, 128
+    heads, one cache of 8192 positions): the absorbed verify call timed at
+    L = 1..16 rows, cold, and the draft cap a speculative decoder would derive
+    from it (mla_draft_cap) for a few survival rates p and drafter costs.  The
+    curve covers the attention of the verify step only."""
+    import mla_speculative_decode_amd as mla
+    from mla_speculative_decode_amd import synth
+
+    w = synth.WORKLOADS[HEADLINE]
+    us = []
+    for L in range(1, args.max_width + 1):
+        x = synth.make_inputs(w, L=L)
+        cold, warm, nsets = absorbed_timing(w, x, args.cold_bytes, args.steps, args.warmup)
+        us.append(cold[0])
+        print(json.dumps({"verify_curve": w.name, "L": L, "us_per_call": round(cold[0], 3),
+                          "splits_us": round(cold[5], 3), "merge_us": round(cold[6], 3), "fold_us": round(cold[7], 3),
+                          "relative": round(cold[0] / us[0], 4), "cache_state": f"cold ({nsets} rotated input sets)"}),
+              flush=True)
+    caps = []
+    for drafter in (0.05, 0.2):
+        for p in (0.5, 0.6, 0.7, 0.8, 0.9):
+            cap, sp, by_cap = mla.draft_cap(us, p, drafter)
+            caps.append({"p": p, "drafter": drafter, "cap": cap, "speedup": round(sp, 4)})
+    print(json.dumps({"verify_curve_summary": w.name, "relative_cost": [round(u / us[0], 4) for u in us],
+                      "derived_caps": caps}), flush=True)
 
 
 def crossover(args):

@@ -111,6 +111,26 @@ int mla_select_path(const mla_geom* g, int64_t L, int64_t T, int32_t* path_out,
                     int64_t* max_absorbed_out);
 
 /*
+ * mla_draft_cap -- the draft cap a speculative decoder derives from a measured
+ * verify-cost curve ("Draft caps and calibration", sections "Play with it"
+ * and "How mlx-dspark picks it").  For caps C = 1 .. n_widths - 1:
+ *   speedup(C) = (1 + p + p^2 + ... + p^C) / (drafter + verify_cost[C] / verify_cost[0])
+ *   verify_cost[w - 1]  measured cost of one verify pass over w rows, any unit
+ *                       (dividing by the one-row cost gives single-token steps)
+ *   p                   probability that each drafted token survives, in [0, 1]
+ *   drafter             the drafter's cost per round, in single-token steps (>= 0)
+ * Writes the cap with the largest speedup (ties: the smaller cap) and its
+ * speedup, or cap 0 with speedup 1 when no cap beats plain decoding.  If
+ * speedup_by_cap is not null it receives n_widths values: 1 for C = 0 (no
+ * drafting), then speedup(C).  Host only; every pointer is host memory owned by
+ * the caller.  Returns MLA_E_NULL if verify_cost, cap_out or speedup_out is
+ * null; MLA_E_SHAPE if n_widths < 1, p is outside [0, 1], drafter is negative or
+ * not finite, or a cost is not finite and positive.
+ */
+int mla_draft_cap(const double* verify_cost, int32_t n_widths, double p, double drafter,
+                  int32_t* cap_out, double* speedup_out, double* speedup_by_cap);
+
+/*
  * mla_fold_query -- fold the key up-projection into the query ("One
  * guard...", section "The defect": the absorbed path folds the
  * up-projection into the query):

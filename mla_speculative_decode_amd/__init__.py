@@ -103,6 +103,20 @@ def select_path(geom: Geom, L: int, T: int = 0) -> tuple[int, int]:
     return int(path.value), int(m.value)
 
 
+def draft_cap(verify_cost, p: float, drafter: float) -> tuple[int, float, list[float]]:
+    """Derived draft cap from a verify-cost curve (verify_cost[w - 1] = cost of a
+    w-row pass, any unit): (cap, its speedup, speedup for caps 0..len - 1)."""
+    lib = _lib.load()
+    n = len(verify_cost)
+    vc = (ctypes.c_double * max(n, 1))(*[float(x) for x in verify_cost])
+    by_cap = (ctypes.c_double * max(n, 1))()
+    cap = ctypes.c_int32()
+    sp = ctypes.c_double()
+    _lib.check("mla_draft_cap", lib.mla_draft_cap(vc, n, float(p), float(drafter), ctypes.byref(cap),
+                                                  ctypes.byref(sp), by_cap))
+    return int(cap.value), float(sp.value), [float(by_cap[i]) for i in range(n)]
+
+
 def fold_query(q_nope, w_uk, out=None, stream=None):
     """q_lat[m, h, :] = q_nope[m, h, :] @ w_uk[h].  q_nope [..., H, n] -> [..., H, r]."""
     torch = _torch()

@@ -17,7 +17,7 @@ STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_UNSUPPORT
           -4: "MLA_E_WORKSPACE", -5: "MLA_E_HIP"}
 
 # Every symbol include/mla.h declares.
-EXPORTS = ("mla_status_string", "mla_version", "mla_select_path", "mla_fold_query",
+EXPORTS = ("mla_status_string", "mla_version", "mla_select_path", "mla_draft_cap", "mla_fold_query",
            "mla_absorbed_workspace_size", "mla_absorbed_attention", "mla_absorbed_splits",
            "mla_absorbed_merge", "mla_materialize_kv",
            "mla_materialized_workspace_size", "mla_materialized_attention")
@@ -63,6 +63,9 @@ def load() -> ctypes.CDLL:
     lib.mla_version.argtypes = []
     lib.mla_select_path.restype = ctypes.c_int
     lib.mla_select_path.argtypes = [GP, I64, I64, I32P, I64P]
+    lib.mla_draft_cap.restype = ctypes.c_int
+    lib.mla_draft_cap.argtypes = [ctypes.POINTER(ctypes.c_double), I32, ctypes.c_double, ctypes.c_double, I32P,
+                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     lib.mla_fold_query.restype = ctypes.c_int
     lib.mla_fold_query.argtypes = [GP, ctypes.c_int, I64, VP, VP, VP, VP]
     lib.mla_absorbed_workspace_size.restype = ctypes.c_int

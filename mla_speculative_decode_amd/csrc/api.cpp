@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 
 #include "internal.h"
@@ -149,6 +150,30 @@ int mla_select_path(const mla_geom* g, int64_t L, int64_t T, int32_t* path_out, 
   if (m > (__int128)INT64_MAX) m = INT64_MAX;
   *path_out = ((__int128)L <= m) ? MLA_ABSORBED : MLA_MATERIALIZED;
   if (max_absorbed_out) *max_absorbed_out = (int64_t)m;
+  return MLA_OK;
+}
+
+int mla_draft_cap(const double* verify_cost, int32_t n_widths, double p, double drafter, int32_t* cap_out,
+                  double* speedup_out, double* speedup_by_cap) {
+  if (!verify_cost || !cap_out || !speedup_out) return MLA_E_NULL;
+  if (n_widths < 1 || !(p >= 0.0 && p <= 1.0) || !(drafter >= 0.0) || !std::isfinite(drafter)) return MLA_E_SHAPE;
+  for (int32_t w = 0; w < n_widths; ++w)
+    if (!(verify_cost[w] > 0.0) || !std::isfinite(verify_cost[w])) return MLA_E_SHAPE;
+  int32_t cap = 0;
+  double best = 1.0, acc = 1.0, term = 1.0;
+  if (speedup_by_cap) speedup_by_cap[0] = 1.0;
+  for (int32_t c = 1; c < n_widths; ++c) {
+    term *= p;                 // p^c
+    acc += term;               // tokens committed per round with cap c
+    const double s = acc / (drafter + verify_cost[c] / verify_cost[0]);
+    if (speedup_by_cap) speedup_by_cap[c] = s;
+    if (s > best) {
+      best = s;
+      cap = c;
+    }
+  }
+  *cap_out = cap;
+  *speedup_out = best;
   return MLA_OK;
 }
 

@@ -6,7 +6,8 @@ code with the HIP library and imports nothing from it.
 
 The numerical functions live in ``mla_oracle.c`` (plain C loops in double,
 OpenMP over the outer independent loop); this module compiles it with gcc and
-calls it through ctypes.  The path threshold lives in ``threshold.py``.
+calls it through ctypes.  The path threshold lives in ``threshold.py``, the
+draft-cap cost model in ``draft_cap.py``.
 """
 
 from __future__ import annotations
@@ -18,6 +19,7 @@ import subprocess
 import numpy as np
 
 from . import threshold  # noqa: F401  (re-exported)
+from . import draft_cap  # noqa: F401  (re-exported)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mla_oracle.c")
