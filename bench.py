@@ -125,6 +125,8 @@ def main():
     cold, warm, nsets = absorbed_timing(w, x, args.cold_bytes, args.steps, args.warmup)
     wall = time.perf_counter() - t0
 
+    peaks = measured_peaks()
+
     # algorithmic work of one call
     lens = np.diff(x.offsets)
     vis = sum(int(H * (kv * L - L * (L - 1) // 2)) for kv in lens)          # sum over rows of visible positions
@@ -144,8 +146,10 @@ def main():
         achieved = (cache_bytes + q_bytes) / (us_split_b2b * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    measured = peaks["mfma_bf16_TFLOPs"] if roof["bound"] == "mfma" else peaks["hbm_read_GBps"]
     roof = {"kernel": "attn_bf16_kernel (mla_absorbed_splits)", **roof, "duration_us": round(us_split_b2b, 3),
-            "traffic": split_traffic_bytes() if w.name == HEADLINE else None}
+            "traffic": split_traffic_bytes() if w.name == HEADLINE else None,
+            "measured_peak": round(measured, 1), "frac_measured": round(roof["achieved"] / measured, 4)}
 
     line = {
         "metric": METRIC if w.name == HEADLINE else f"absorbed MLA verify µs/call + latent-cache HBM GB/s ({w.name})",
@@ -174,12 +178,35 @@ def main():
         "warm_per_launch_us": {"fold": round(warm[1], 3), "splits": round(warm[2], 3), "merge": round(warm[3], 3),
                                "splits_back_to_back": round(warm[5], 3)},
         "roofline": roof,
+        "peaks_measured": {k: round(v, 1) for k, v in peaks.items()},
         "wall_s": round(wall, 3),
     }
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def measured_peaks():
+    """Achievable peaks on this GPU (libmla_bench.so): a streaming read of 1 GiB
+    and a dense stream of independent bf16 32x32x16 MFMAs."""
+    import torch
+    blib = ctypes.CDLL(os.path.join(ROOT, "mla_speculative_decode_amd", "libmla_bench.so"))
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(16, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    gbps, tflops = ctypes.c_double(), ctypes.c_double()
+    for fn, args in ((blib.mlab_stream_read, (ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(buf.numel()),
+                                               ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream),
+                                               5, ctypes.byref(gbps))),
+                     (blib.mlab_mfma_peak, (ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream),
+                                            4096, ctypes.byref(tflops)))):
+        fn.restype = ctypes.c_int
+        if fn(*args) != 0:
+            raise RuntimeError("peak measurement failed")
+    torch.cuda.synchronize()
+    del buf
+    return {"hbm_read_GBps": gbps.value, "mfma_bf16_TFLOPs": tflops.value}
 
 
 def absorbed_timing(w, x, cold_bytes, steps, warmup):

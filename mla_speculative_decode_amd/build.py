@@ -65,6 +65,7 @@ def build(verbose: bool = False) -> str:
     # bench driver: links against libmla.so, found next to it at run time
     tmp = BENCH_LIB + ".tmp"
     r = subprocess.run([cc, *flags(), "-shared", "-o", tmp, os.path.join(CSRC, "bench_driver.cpp"),
+                        "-x", "hip", os.path.join(CSRC, "bench_peaks.hip"),
                         "-L", HERE, "-lmla", "-Wl,-rpath,$ORIGIN"], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"bench driver build failed:\n{r.stderr}")
