@@ -227,6 +227,46 @@ int mla_materialize_kv(const mla_geom* g, mla_dtype dt, int64_t T, const void* c
                        const void* k_pe, const void* w_uk, const void* w_uv, void* k, void* v,
                        void* stream);
 
+/*
+ * fp8 latent cache.  The pages test a "quantised latent form" of the cache
+ * without defining it (mlx-lm PR #1817, section "Tests"); the form built here:
+ * each cached position's row [c_kv[t] | k_pe[t]] (r + rope values) is stored as
+ * OCP E4M3 codes (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals m x 2^-9, no infinities, largest finite value 448) with one scale
+ * per position, the smallest power of two 2^k with max|row| <= 448 x 2^k
+ * (k in [-126, 127]; 2^0 for an all-zero row).  Codes are the nearest E4M3
+ * value of row / 2^k, ties to the even code (a negative value that rounds to
+ * zero gets code 0x00).  Every dequantised value code x 2^k is exact in bf16,
+ * and the fp8 attention computes the absorbed attention over exactly those values.
+ *
+ * mla_quantize_latent_fp8 -- c_kv [T, r], k_pe [T, rope] (device, bf16) ->
+ *   codes [T, r + rope] (device, uint8; latent then rope per position) and
+ *   scales [T] (device, float32, powers of two).  Buffers are the caller's.
+ *   Errors: MLA_E_NULL, MLA_E_SHAPE (T < 1 or > INT32_MAX), MLA_E_UNSUPPORTED
+ *   (r or rope not a multiple of 8, r + rope > 1024), MLA_E_HIP.
+ */
+int mla_quantize_latent_fp8(const mla_geom* g, int64_t T, const void* c_kv, const void* k_pe, void* codes,
+                            float* scales, void* stream);
+
+/*
+ * mla_absorbed_attention_fp8 -- mla_absorbed_attention (bf16 queries q_lat, q_pe
+ * and W_UV; float32 out) with the latent cache given as (codes, scales) from
+ * mla_quantize_latent_fp8 instead of c_kv and k_pe: the split kernel reads the
+ * codes (half the bytes of the bf16 cache) and expands each tile to bf16 in LDS.
+ * Workspace: mla_absorbed_workspace_size with MLA_BF16.  mla_absorbed_splits_fp8
+ * is its split pass alone; mla_absorbed_merge (MLA_BF16) completes it.
+ * Supported: r = 512, rope in {0, 64}; otherwise MLA_E_UNSUPPORTED.  Other
+ * errors as for mla_absorbed_attention.
+ */
+int mla_absorbed_attention_fp8(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                               const void* codes, const float* scales, const int32_t* kv_offsets_host,
+                               const int32_t* kv_offsets_dev, const void* w_uv, float scale, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+int mla_absorbed_splits_fp8(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                            const void* codes, const float* scales, const int32_t* kv_offsets_host,
+                            const int32_t* kv_offsets_dev, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Bytes of workspace mla_materialized_attention needs (split-KV partials). */
 int mla_materialized_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
                                     const int32_t* kv_offsets_host, size_t* bytes_out);

@@ -19,7 +19,7 @@ import math
 from typing import Sequence
 
 from . import _lib
-from ._lib import Geom, MlaError, MLA_ABSORBED, MLA_MATERIALIZED  # noqa: F401
+from ._lib import Geom, MlaError, MLA_ABSORBED, MLA_MATERIALIZED, MLA_BF16, MLA_F32  # noqa: F401
 
 __all__ = ["Geom", "MlaError", "MLA_ABSORBED", "MLA_MATERIALIZED", "Offsets", "select_path",
            "fold_query", "absorbed_workspace_size", "absorbed_attention", "absorbed_splits",
@@ -248,6 +248,56 @@ def materialized_attention(q_nope, q_pe, k, v, kv_offsets, scale=None, out=None,
         ctypes.byref(g), dt, B, L, _ptr(_dev(q_nope, "q_nope")), _ptr(q_pe) if rope else None,
         _ptr(_dev(k, "k")), _ptr(_dev(v, "v")), offs.host_ptr(), offs.dev_ptr(), ctypes.c_float(scale),
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def quantize_latent_fp8(c_kv, k_pe, codes=None, scales=None, stream=None):
+    """bf16 latent cache -> (codes uint8 [T, r + rope], scales float32 [T], powers of two)."""
+    torch = _torch()
+    lib = _lib.load()
+    T, r = c_kv.shape
+    rope = k_pe.shape[-1] if k_pe is not None else 0
+    if codes is None:
+        codes = torch.empty((T, r + rope), dtype=torch.uint8, device=c_kv.device)
+    if scales is None:
+        scales = torch.empty((T,), dtype=torch.float32, device=c_kv.device)
+    if _dtype_code(c_kv) != MLA_BF16 or (rope and _dtype_code(k_pe) != MLA_BF16):
+        raise TypeError("the fp8 cache is quantised from a bf16 cache")
+    g = Geom(r, 0, 1, rope, 1)
+    _lib.check("mla_quantize_latent_fp8", lib.mla_quantize_latent_fp8(
+        ctypes.byref(g), T, _ptr(_dev(c_kv, "c_kv")), _ptr(k_pe) if rope else None, _ptr(_dev(codes, "codes")),
+        _ptr(_dev(scales, "scales")), _stream(stream)))
+    return codes, scales
+
+
+def absorbed_attention_fp8(q_lat, q_pe, codes, scales, w_uv, kv_offsets, scale=None, out=None, workspace=None,
+                           stream=None, n=None):
+    """absorbed_attention over the fp8 cache (codes, scales) from quantize_latent_fp8."""
+    torch = _torch()
+    lib = _lib.load()
+    B, L, H, r = q_lat.shape
+    rope = q_pe.shape[-1] if q_pe is not None else 0
+    v = w_uv.shape[-1]
+    if codes.shape[-1] != r + rope:
+        raise ValueError("codes rows must hold r + rope values")
+    offs = _as_offsets(kv_offsets, q_lat.device)
+    if offs.B != B:
+        raise ValueError("offsets do not match the batch")
+    if scale is None:
+        if n is None:
+            raise ValueError("give scale, or n to default it to 1/sqrt(n + rope)")
+        scale = 1.0 / math.sqrt(n + rope)
+    g = Geom(r, int(n) if n is not None else 0, v, rope, H)
+    need = absorbed_workspace_size(g, MLA_BF16, L, offs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q_lat.device)
+    if out is None:
+        out = torch.empty((B, L, H, v), dtype=torch.float32, device=q_lat.device)
+    _lib.check("mla_absorbed_attention_fp8", lib.mla_absorbed_attention_fp8(
+        ctypes.byref(g), B, L, _ptr(_dev(q_lat, "q_lat")), _ptr(q_pe) if rope else None,
+        _ptr(_dev(codes, "codes")), _ptr(_dev(scales, "scales")), offs.host_ptr(), offs.dev_ptr(),
+        _ptr(_dev(w_uv, "w_uv")), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

@@ -280,6 +280,54 @@ int mla_absorbed_merge(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, co
   return hip_status(combine_upproj(q, dt == MLA_BF16 ? kBF16 : kF32, out, (hipStream_t)stream));
 }
 
+int mla_quantize_latent_fp8(const mla_geom* g, int64_t T, const void* c_kv, const void* k_pe, void* codes,
+                            float* scales, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (T < 1 || T > INT32_MAX) return MLA_E_SHAPE;
+  if (!c_kv || !codes || !scales) return MLA_E_NULL;
+  if (g->rope > 0 && !k_pe) return MLA_E_NULL;
+  if (g->r % 8 != 0 || g->rope % 8 != 0 || (g->r + g->rope) / 8 > 128) return MLA_E_UNSUPPORTED;
+  return hip_status(quantize_latent_fp8(T, g->r, g->rope, c_kv, k_pe, codes, scales, (hipStream_t)stream));
+}
+
+namespace {
+int absorbed_prepare_fp8(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                         const void* codes, const float* scales, const int32_t* off_h, const int32_t* off_d,
+                         const void* w_uv, const float* out, void* workspace, size_t workspace_bytes, float scale,
+                         bool need_merge, AbsorbedLaunch* q) {
+  if (!codes || !scales) return MLA_E_NULL;
+  if (!g) return MLA_E_NULL;
+  if (g->r != 512 || !(g->rope == 0 || g->rope == 64)) return MLA_E_UNSUPPORTED;
+  return absorbed_prepare(g, MLA_BF16, B, L, q_lat, q_pe, codes, g->rope > 0 ? codes : nullptr, off_h, off_d, w_uv,
+                          out, workspace, workspace_bytes, scale, true, need_merge, q);
+}
+}  // namespace
+
+int mla_absorbed_splits_fp8(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                            const void* codes, const float* scales, const int32_t* kv_offsets_host,
+                            const int32_t* kv_offsets_dev, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  AbsorbedLaunch q{};
+  int st = absorbed_prepare_fp8(g, B, L, q_lat, q_pe, codes, scales, kv_offsets_host, kv_offsets_dev, nullptr,
+                                nullptr, workspace, workspace_bytes, scale, false, &q);
+  if (st) return st;
+  return hip_status(absorbed_attn_fp8(q, codes, scales, (hipStream_t)stream));
+}
+
+int mla_absorbed_attention_fp8(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                               const void* codes, const float* scales, const int32_t* kv_offsets_host,
+                               const int32_t* kv_offsets_dev, const void* w_uv, float scale, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  AbsorbedLaunch q{};
+  int st = absorbed_prepare_fp8(g, B, L, q_lat, q_pe, codes, scales, kv_offsets_host, kv_offsets_dev, w_uv, out,
+                                workspace, workspace_bytes, scale, true, &q);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = hip_status(absorbed_attn_fp8(q, codes, scales, s)))) return st;
+  return hip_status(combine_upproj(q, kBF16, out, s));
+}
+
 int mla_materialize_kv(const mla_geom* g, mla_dtype dt, int64_t T, const void* c_kv, const void* k_pe,
                        const void* w_uk, const void* w_uv, void* k, void* v, void* stream) {
   int st = check_geom(g);

@@ -45,6 +45,8 @@ struct AttnArgs {
   const uint16_t* qb;   // query part b: [B, L, H, DR]
   const uint16_t* ka;   // key-only source (see KW), row for position p at ka + p*ka_ks + head*ka_hs
   const uint16_t* vv;   // value source, row for position p at vv + p*vv_ks + head*vv_hs
+  const uint8_t* c8;    // fp8 latent cache (F8): E4M3 codes [T, DA + DR] (latent | rope) ...
+  const float* c8s;     // ... and one power-of-two scale per position [T]
   long long ka_ks, ka_hs, vv_ks, vv_hs;
   const int32_t* off;   // [B+1] device offsets
   int off0, kv1;        // B == 1: off[0] and off[1] - off[0]
@@ -79,7 +81,7 @@ constexpr float kRefSlack = 64.f;
 // fragments straight from the row-major tile with ds_read_b64_tr_b16 (lane l
 // of each 16-lane group receives column l%16 of the 4 rows its group
 // addressed), so there is no transposed copy of V.
-template <int DA, int DR, int DV, bool VK>
+template <int DA, int DR, int DV, bool VK, bool F8 = false>
 __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   constexpr int D = DA + DR;
   constexpr int BM = 64, BN = 64;
@@ -197,7 +199,49 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       }
     }
   };
+  // F8: the tile's code rows (DA + DR bytes each) come into registers, four
+  // threads per position (thread t: position t / 4, 16-code chunks t % 4 + 4 x),
+  // and are expanded into the same bf16 tile layout after the tile's PV:
+  // code x 2^k is exact in bf16, so the tile holds the dequantised cache.
+  constexpr int F8C = F8 ? (DA + DR) / 16 : 4;           // 16-code chunks per position
+  constexpr int F8X = (F8C + 3) / 4;                      // chunks per thread
+  static_assert(!F8 || (VK && (DA + DR) % 64 == 0 && BN * 4 == 256), "fp8 rows: four threads per position");
+  u32x4 f8r[F8 ? F8X : 1];
+  float f8s = 0.f;
+  auto issue_f8 = [&](int t0, int x) {
+    const int key = tid >> 2, j = (tid & 3) + 4 * x;
+    const long long kr = p0 + min(t0 + key, k1 - 1);
+    f8r[x] = ld16(p.c8 + kr * (DA + DR) + 16 * j);
+    if (x == 0) f8s = p.c8s[kr];
+  };
+  auto store_f8 = [&](uint8_t* kdst) {
+    const int key = tid >> 2;
+#pragma unroll
+    for (int x = 0; x < F8X; ++x) {
+      const int j = (tid & 3) + 4 * x;
+      u32x4 lo, hi;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8r[x][q], f8s, false);   // codes 4q, 4q+1
+        const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8r[x][q], f8s, true);    // codes 4q+2, 4q+3
+        if (q < 2) {
+          lo[2 * q] = __builtin_bit_cast(uint32_t, a);
+          lo[2 * q + 1] = __builtin_bit_cast(uint32_t, b);
+        } else {
+          hi[2 * q - 4] = __builtin_bit_cast(uint32_t, a);
+          hi[2 * q - 3] = __builtin_bit_cast(uint32_t, b);
+        }
+      }
+      st16(kdst + key * KRB + 32 * j, lo);
+      st16(kdst + key * KRB + 32 * j + 16, hi);
+    }
+  };
   auto issue_tile = [&](int t0, uint8_t* kdst) {
+    if (F8) {
+#pragma unroll
+      for (int x = 0; x < F8X; ++x) issue_f8(t0, x);
+      return;
+    }
     if (VK) issue_rope(t0);
 #pragma unroll
     for (int x = 0; x < NLW; ++x) issue_part(t0, kdst, x);
@@ -255,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     // k0 + rt + row_tiles * j, one 4-byte load per 128-byte line (8 latent lines,
     // 1 rope line per position) into a dummy LDS slot.  The row tiles of a split
     // run on one XCD, so the tile copies of the loop then hit L2.
-    {
+    if (!F8) {
       constexpr int LPP = DA / 64 + (DR > 0 ? 1 : 0);   // 128-byte lines per position
       const int cnt = max(0, (k1 - k0 - rt + p.row_tiles - 1) / p.row_tiles);
       const int nl = cnt * LPP;
@@ -276,7 +320,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         st16(buf1 + row * KRB + (DA / 8 + ch) * 16, qst[x]);
       }
     }
-    store_rope(buf0);
+    if (F8) store_f8(buf0); else store_rope(buf0);
     __syncthreads();   // query block (and tile 0) in LDS
     const uint8_t* qrow = buf1 + rq * KRB + 16 * half;
 #pragma unroll
@@ -330,7 +374,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     // The next tile is copied unconditionally (branch-free code keeps the LDS
     // wait counts exact): past the end of the split every row clamps to the
     // last position and lands in the idle buffer, which nothing reads again.
-    if (VK && pf) issue_rope(t0 + BN);
+    if (VK && !F8 && pf) issue_rope(t0 + BN);
     const uint8_t* kt = cur;
     const uint8_t* vt = VK ? kt : kt + KBYTES;
 
@@ -354,8 +398,13 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         acc = mfma32(a, qf[c], acc);
         // next tile's copy, spread over the score MFMAs (NLW instructions)
         if (pf) {
+          if (F8) {
 #pragma unroll
-          for (int x = (c * NLW) / DCH; x < ((c + 1) * NLW) / DCH; ++x) issue_part(t0 + BN, nxt, x);
+            for (int x = (c * F8X) / DCH; x < ((c + 1) * F8X) / DCH; ++x) issue_f8(t0 + BN, x);
+          } else {
+#pragma unroll
+            for (int x = (c * NLW) / DCH; x < ((c + 1) * NLW) / DCH; ++x) issue_part(t0 + BN, nxt, x);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the read of step c+PF ahead of MFMA c
       }
@@ -490,7 +539,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         __builtin_amdgcn_sched_barrier(0);   // later steps' reads stay ahead of this step's MFMAs
       }
     }
-    if (VK && pf) store_rope(nxt);   // the other buffer is not read until barrier (A)
+    if (pf) {   // the other buffer is not read until barrier (A)
+      if (F8) store_f8(nxt); else if (VK) store_rope(nxt);
+    }
   };
   // Tiles go in pairs (one per buffer); an odd tile count skips the second
   // step of the last pair.  No copy follows the last tile.
@@ -523,7 +574,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     t_max = -INFINITY;
     issue_tile(k0, buf0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (VK) store_rope(buf0);
+    if (F8) store_f8(buf0); else if (VK) store_rope(buf0);
   }
 
   // ---- epilogue: row sums, partial results ---------------------------------
@@ -991,6 +1042,24 @@ hipError_t absorbed_attn_bf16(const AbsorbedLaunch& q, hipStream_t st) {
     case 64: return launch_attn<512, 64, 512, true>(a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t absorbed_attn_fp8(const AbsorbedLaunch& q, const void* codes, const float* scales, hipStream_t st) {
+  AttnArgs a{};
+  a.qa = (const uint16_t*)q.q_lat; a.qb = (const uint16_t*)q.q_pe;
+  a.c8 = (const uint8_t*)codes; a.c8s = scales;
+  a.off = q.off_dev; a.off0 = q.off0; a.kv1 = q.kv1; a.ws_o = q.ws_o; a.ws_ml = q.ws_ml;
+  a.B = q.B; a.L = q.L; a.H = q.H; a.hpr = q.H; a.rows_slot = q.L * q.H; a.head_slots = 1;
+  a.row_tiles = q.plan.row_tiles; a.chunk = q.plan.chunk; a.n_items = q.plan.n_items;
+  a.rows_total = q.L * q.H; a.sl2 = q.scale * 1.4426950408889634f;
+  if (q.r != 512) return hipErrorInvalidValue;
+  const dim3 grid(grid_xcd(a.n_items));
+  switch (q.rope) {
+    case 0:  hipLaunchKernelGGL((attn_bf16_kernel<512, 0, 512, true, true>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((attn_bf16_kernel<512, 64, 512, true, true>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t materialized_attn_bf16(const MaterializedLaunch& q, hipStream_t st) {

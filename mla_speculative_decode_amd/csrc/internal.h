@@ -44,11 +44,16 @@ struct MaterializedLaunch {
 
 // attn.hip
 hipError_t absorbed_attn_bf16(const AbsorbedLaunch& q, hipStream_t st);
+hipError_t absorbed_attn_fp8(const AbsorbedLaunch& q, const void* codes, const float* scales, hipStream_t st);
 hipError_t materialized_attn_bf16(const MaterializedLaunch& q, hipStream_t st);
 bool materialized_bf16_supported(int n, int rope, int v);
 hipError_t attn_f32(const AbsorbedLaunch* qa, const MaterializedLaunch* qm, hipStream_t st);
 hipError_t combine_materialized(const MaterializedLaunch& q, mla_dtype_t dt, float* out, hipStream_t st);
 hipError_t combine_upproj(const AbsorbedLaunch& q, mla_dtype_t dt, float* out, hipStream_t st);
+
+// quant.hip
+hipError_t quantize_latent_fp8(long long T, int r, int rope, const void* c_kv, const void* k_pe, void* codes,
+                               float* scales, hipStream_t st);
 
 // gemm.hip
 struct GemmArgs {

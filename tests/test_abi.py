@@ -18,7 +18,7 @@ from tests.conftest import ROOT
 def _header_symbols():
     with open(os.path.join(ROOT, "include", "mla.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\S.*?\b(mla_[a-z_]+)\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\S.*?\b(mla_[a-z0-9_]+)\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
