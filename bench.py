@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv3_h128_kv8192_l8_bf16")
+    ap.add_argument("--cache", choices=("bf16", "fp8"), default="bf16",
+                    help="latent cache form: bf16, or fp8 (E4M3 codes + power-of-two scale per position)")
     ap.add_argument("--cold-bytes", type=float, default=768e6,
                     help="total bytes of rotated input sets (cold protocol); 0 = warm only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -122,7 +124,8 @@ def main():
     x = synth.make_inputs(w)
     B, L, H = w.batch, x.L, w.heads
     t0 = time.perf_counter()
-    cold, warm, nsets = absorbed_timing(w, x, args.cold_bytes, args.steps, args.warmup)
+    fp8 = args.cache == "fp8"
+    cold, warm, nsets = absorbed_timing(w, x, args.cold_bytes, args.steps, args.warmup, fp8=fp8)
     wall = time.perf_counter() - t0
 
     peaks = measured_peaks()
@@ -131,7 +134,8 @@ def main():
     lens = np.diff(x.offsets)
     vis = sum(int(H * (kv * L - L * (L - 1) // 2)) for kv in lens)          # sum over rows of visible positions
     attn_flop = 2.0 * (2 * w.r + w.rope) * vis                            # scores (r+rope) + latent PV (r)
-    cache_bytes = float(lens.sum() * (w.r + w.rope) * 2)
+    # bf16 cache: 2 bytes per value; fp8 cache: 1 byte per value + a float32 scale per position
+    cache_bytes = float(lens.sum() * ((w.r + w.rope) + 4)) if fp8 else float(lens.sum() * (w.r + w.rope) * 2)
     q_bytes = float(B * L * H * (w.r + w.rope) * 2)                       # q_lat + q_pe read by the split kernel
     weight_bytes = float(2 * H * w.n * w.r * 2)                            # W_UK + W_UV, bf16
     us_step, us_fold, us_split, us_merge, us_evented, us_split_b2b, us_merge_b2b, us_fold_b2b = cold
@@ -148,11 +152,12 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBPS, 4)}
     measured = peaks["mfma_bf16_TFLOPs"] if roof["bound"] == "mfma" else peaks["hbm_read_GBps"]
     roof = {"kernel": "attn_bf16_kernel (mla_absorbed_splits)", **roof, "duration_us": round(us_split_b2b, 3),
-            "traffic": split_traffic_bytes() if w.name == HEADLINE else None,
+            "traffic": split_traffic_bytes() if (w.name == HEADLINE and not fp8) else None,
             "measured_peak": round(measured, 1), "frac_measured": round(roof["achieved"] / measured, 4)}
 
     line = {
-        "metric": METRIC if w.name == HEADLINE else f"absorbed MLA verify µs/call + latent-cache HBM GB/s ({w.name})",
+        "metric": METRIC if (w.name == HEADLINE and not fp8) else
+                  f"absorbed MLA verify µs/call + latent-cache HBM GB/s ({w.name}{', fp8 cache' if fp8 else ''})",
         "value": round(us_step, 3),
         "unit": "us/call",
         "n_gpus": 1,
@@ -165,7 +170,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/r) weights)",
         "config": {"workload": w.name, "r": w.r, "n": w.n, "v": w.v, "rope": w.rope, "heads": H, "batch": B,
-                   "kv": int(lens.max()), "kv_total": int(lens.sum()), "L": L,
+                   "kv": int(lens.max()), "kv_total": int(lens.sum()), "L": L, "cache": args.cache,
                    "cache_state": f"cold ({nsets} rotated input sets)"},
         "latent_cache_GBps": round(cache_bytes / (us_split_b2b * 1e-6) / 1e9, 1),
         "latent_cache_GBps_split_merge": round(cache_bytes / ((us_split_b2b + us_merge_b2b) * 1e-6) / 1e9, 1),
@@ -209,7 +214,7 @@ def measured_peaks():
     return {"hbm_read_GBps": gbps.value, "mfma_bf16_TFLOPs": tflops.value}
 
 
-def absorbed_timing(w, x, cold_bytes, steps, warmup):
+def absorbed_timing(w, x, cold_bytes, steps, warmup, fp8=False):
     """Time the absorbed verify call on inputs x through the native loop: the
     cold rotation of cloned input sets, then one warm set.  Returns the result
     arrays of both runs (see bench_driver.cpp) and the number of sets."""
@@ -227,9 +232,16 @@ def absorbed_timing(w, x, cold_bytes, steps, warmup):
         return torch.from_numpy(a).to(torch.bfloat16).to(dev).contiguous()
 
     base = {k: up(getattr(x, k)) for k in ("q_nope", "q_pe", "c_kv", "k_pe", "w_uk", "w_uv")}
-    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    if fp8:   # the cache in its fp8 form (quantised once, outside the timed region)
+        base["codes"], base["scales"] = mla.quantize_latent_fp8(base["c_kv"], base["k_pe"])
+        del base["c_kv"], base["k_pe"]
+        base["c_kv"], base["k_pe"] = base["codes"], base["codes"]   # placeholders, not read
+    set_bytes = sum(t.numel() * t.element_size() for k, t in base.items() if k not in ("c_kv", "k_pe") or not fp8)
     nsets = max(1, int(math.ceil(cold_bytes / set_bytes))) if cold_bytes > 0 else 1
     sets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(nsets - 1)]
+    if fp8:
+        for st in sets:
+            st["c_kv"], st["k_pe"] = st["codes"], st["codes"]
     for st in sets:
         st["q_lat"] = torch.empty((B, L, H, w.r), dtype=torch.bfloat16, device=dev)
         st["out"] = torch.empty((B, L, H, w.v), dtype=torch.float32, device=dev)
@@ -249,7 +261,8 @@ def absorbed_timing(w, x, cold_bytes, steps, warmup):
             ctypes.byref(geom), B, L, len(idx), ptrs("q_nope", idx), ptrs("q_pe", idx), ptrs("c_kv", idx),
             ptrs("k_pe", idx), ptrs("w_uk", idx), ptrs("w_uv", idx), ptrs("q_lat", idx), ptrs("out", idx),
             offs.host_ptr(), offs.dev_ptr(), ctypes.c_float(x.scale), ctypes.c_void_p(ws.data_ptr()),
-            ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream), warmup, steps, res)
+            ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream), warmup, steps, res,
+            ptrs("codes", idx) if fp8 else None, ptrs("scales", idx) if fp8 else None)
         torch.cuda.synchronize()
         if rc != 0:
             raise RuntimeError(f"bench step failed: {lib.mla_status_string(rc).decode()}")

@@ -16,7 +16,17 @@ namespace {
 struct Sets {
   void* const* q_nope; void* const* q_pe; void* const* c_kv; void* const* k_pe;
   void* const* w_uk; void* const* w_uv; void* const* q_lat; float* const* out;
+  void* const* codes; float* const* scales;   // fp8 cache (null: the bf16 cache)
 };
+
+int splits(const mla_geom* g, int B, int L, const Sets& s, int k, const int32_t* off_h, const int32_t* off_d,
+           float scale, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (s.codes)
+    return mla_absorbed_splits_fp8(g, B, L, s.q_lat[k], s.q_pe[k], s.codes[k], s.scales[k], off_h, off_d, scale, ws,
+                                   ws_bytes, st);
+  return mla_absorbed_splits(g, MLA_BF16, B, L, s.q_lat[k], s.q_pe[k], s.c_kv[k], s.k_pe[k], off_h, off_d, scale,
+                             ws, ws_bytes, st);
+}
 
 int step(const mla_geom* g, int B, int L, const Sets& s, int k, const int32_t* off_h, const int32_t* off_d,
          float scale, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev) {
@@ -24,9 +34,7 @@ int step(const mla_geom* g, int B, int L, const Sets& s, int k, const int32_t* o
   if (ev) hipEventRecord(ev[0], st);
   if ((rc = mla_fold_query(g, MLA_BF16, (int64_t)B * L, s.q_nope[k], s.w_uk[k], s.q_lat[k], st))) return rc;
   if (ev) hipEventRecord(ev[1], st);
-  if ((rc = mla_absorbed_splits(g, MLA_BF16, B, L, s.q_lat[k], s.q_pe[k], s.c_kv[k], s.k_pe[k], off_h, off_d, scale,
-                                ws, ws_bytes, st)))
-    return rc;
+  if ((rc = splits(g, B, L, s, k, off_h, off_d, scale, ws, ws_bytes, st))) return rc;
   if (ev) hipEventRecord(ev[2], st);
   if ((rc = mla_absorbed_merge(g, MLA_BF16, B, L, off_h, off_d, s.w_uv[k], s.out[k], ws, ws_bytes, st))) return rc;
   if (ev) hipEventRecord(ev[3], st);
@@ -45,12 +53,15 @@ extern "C" {
 //        rotation of input sets (events only around the run)
 // res[6] us per mla_absorbed_merge launch, back to back (same rotation)
 // res[7] us per mla_fold_query launch, back to back (same rotation)
+// codes / scales: per input set, the fp8 cache (mla_quantize_latent_fp8) to use
+// instead of c_kv / k_pe (mla_absorbed_splits_fp8), or null
 int mlab_absorbed_run(const mla_geom* g, int B, int L, int nsets, void* const* q_nope, void* const* q_pe,
                       void* const* c_kv, void* const* k_pe, void* const* w_uk, void* const* w_uv,
                       void* const* q_lat, float* const* out, const int32_t* off_h, const int32_t* off_d,
-                      float scale, void* ws, size_t ws_bytes, void* stream, int warmup, int steps, double* res) {
+                      float scale, void* ws, size_t ws_bytes, void* stream, int warmup, int steps, double* res,
+                      void* const* codes, float* const* scales) {
   hipStream_t st = (hipStream_t)stream;
-  Sets s{q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, q_lat, out};
+  Sets s{q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, q_lat, out, codes, scales};
   int rc;
   for (int i = 0; i < warmup; ++i)
     if ((rc = step(g, B, L, s, i % nsets, off_h, off_d, scale, ws, ws_bytes, st, nullptr))) return rc;
@@ -91,9 +102,7 @@ int mlab_absorbed_run(const mla_geom* g, int B, int L, int nsets, void* const* q
   hipEventRecord(a, st);
   for (int i = 0; i < steps; ++i) {
     const int k = i % nsets;
-    if ((rc = mla_absorbed_splits(g, MLA_BF16, B, L, s.q_lat[k], s.q_pe[k], s.c_kv[k], s.k_pe[k], off_h, off_d,
-                                  scale, ws, ws_bytes, st)))
-      return rc;
+    if ((rc = splits(g, B, L, s, k, off_h, off_d, scale, ws, ws_bytes, st))) return rc;
   }
   hipEventRecord(b, st);
   hipStreamSynchronize(st);
