@@ -267,6 +267,31 @@ int mla_absorbed_splits_fp8(const mla_geom* g, int32_t B, int32_t L, const void*
                             const int32_t* kv_offsets_dev, float scale, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/*
+ * mla_absorbed_attention_sparse -- absorbed attention over selected cache
+ * positions ("One guard, 110x off the verify step", section "The sparse model
+ * is different": an indexer selects the top 2048 cached positions and attention
+ * runs only over those).  Sequence b's selection is sel[sel_offsets[b] ..
+ * sel_offsets[b+1]): positions relative to the sequence start, strictly
+ * increasing, shared by the sequence's L rows and all heads; row i attends to
+ * the selected positions p < Kv_b - L + i + 1 (the causal rule of the dense
+ * call), and a row that sees none of them gets a zero output.  Everything else
+ * as mla_absorbed_attention with MLA_BF16 (q_lat, q_pe, c_kv, k_pe, W_UV bf16;
+ * out float32).  sel (int32) and sel_offsets_dev live on the device,
+ * sel_offsets_host on the host.  Selection entries outside [0, Kv_b) are clamped
+ * into it (no access leaves the cache).  Workspace:
+ * mla_absorbed_sparse_workspace_size.  Errors: MLA_E_NULL, MLA_E_SHAPE (offsets
+ * as for the dense call; 1 <= selection length <= Kv_b), MLA_E_UNSUPPORTED
+ * (r != 512 or rope not in {0, 64}), MLA_E_WORKSPACE, MLA_E_HIP.
+ */
+int mla_absorbed_sparse_workspace_size(const mla_geom* g, int32_t B, int32_t L, const int32_t* kv_offsets_host,
+                                       const int32_t* sel_offsets_host, size_t* bytes_out);
+int mla_absorbed_attention_sparse(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                                  const void* c_kv, const void* k_pe, const int32_t* kv_offsets_host,
+                                  const int32_t* kv_offsets_dev, const int32_t* sel, const int32_t* sel_offsets_host,
+                                  const int32_t* sel_offsets_dev, const void* w_uv, float scale, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace mla_materialized_attention needs (split-KV partials). */
 int mla_materialized_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
                                     const int32_t* kv_offsets_host, size_t* bytes_out);

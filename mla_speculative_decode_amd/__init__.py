@@ -301,6 +301,42 @@ def absorbed_attention_fp8(q_lat, q_pe, codes, scales, w_uv, kv_offsets, scale=N
     return out
 
 
+def absorbed_attention_sparse(q_lat, q_pe, c_kv, k_pe, w_uv, kv_offsets, sel, sel_offsets, scale=None, out=None,
+                              workspace=None, stream=None, n=None):
+    """Absorbed attention over selected positions: sequence b attends to
+    sel[sel_offsets[b]:sel_offsets[b+1]] (positions from its start, increasing),
+    row i to those below Kv_b - L + i + 1.  sel: int32 device tensor."""
+    torch = _torch()
+    lib = _lib.load()
+    B, L, H, r = q_lat.shape
+    rope = q_pe.shape[-1] if q_pe is not None else 0
+    v = w_uv.shape[-1]
+    offs = _as_offsets(kv_offsets, q_lat.device)
+    soffs = _as_offsets(sel_offsets, q_lat.device)
+    if offs.B != B or soffs.B != B:
+        raise ValueError("offsets do not match the batch")
+    if sel.dtype != torch.int32:
+        raise TypeError("sel must be int32")
+    if scale is None:
+        if n is None:
+            raise ValueError("give scale, or n to default it to 1/sqrt(n + rope)")
+        scale = 1.0 / math.sqrt(n + rope)
+    g = Geom(r, int(n) if n is not None else 0, v, rope, H)
+    sz = ctypes.c_size_t()
+    _lib.check("mla_absorbed_sparse_workspace_size", lib.mla_absorbed_sparse_workspace_size(
+        ctypes.byref(g), B, L, offs.host_ptr(), soffs.host_ptr(), ctypes.byref(sz)))
+    if workspace is None:
+        workspace = torch.empty(max(int(sz.value), 256), dtype=torch.uint8, device=q_lat.device)
+    if out is None:
+        out = torch.empty((B, L, H, v), dtype=torch.float32, device=q_lat.device)
+    _lib.check("mla_absorbed_attention_sparse", lib.mla_absorbed_attention_sparse(
+        ctypes.byref(g), B, L, _ptr(_dev(q_lat, "q_lat")), _ptr(q_pe) if rope else None, _ptr(_dev(c_kv, "c_kv")),
+        _ptr(k_pe) if rope else None, offs.host_ptr(), offs.dev_ptr(), _ptr(_dev(sel, "sel")), soffs.host_ptr(),
+        soffs.dev_ptr(), _ptr(_dev(w_uv, "w_uv")), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def absorbed(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, kv_offsets, scale=None, stream=None, q_lat=None,
              out=None, workspace=None):
     """Whole absorbed path: fold_query then absorbed_attention."""

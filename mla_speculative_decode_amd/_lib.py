@@ -21,7 +21,8 @@ EXPORTS = ("mla_status_string", "mla_version", "mla_select_path", "mla_draft_cap
            "mla_absorbed_workspace_size", "mla_absorbed_attention", "mla_absorbed_splits",
            "mla_absorbed_merge", "mla_materialize_kv",
            "mla_materialized_workspace_size", "mla_materialized_attention", "mla_quantize_latent_fp8",
-           "mla_absorbed_attention_fp8", "mla_absorbed_splits_fp8")
+           "mla_absorbed_attention_fp8", "mla_absorbed_splits_fp8", "mla_absorbed_sparse_workspace_size",
+           "mla_absorbed_attention_sparse")
 
 
 class Geom(ctypes.Structure):
@@ -94,6 +95,11 @@ def load() -> ctypes.CDLL:
     lib.mla_absorbed_splits_fp8.restype = ctypes.c_int
     lib.mla_absorbed_splits_fp8.argtypes = [GP, I32, I32, VP, VP, VP, VP, VP, VP, ctypes.c_float, VP,
                                             ctypes.c_size_t, VP]
+    lib.mla_absorbed_sparse_workspace_size.restype = ctypes.c_int
+    lib.mla_absorbed_sparse_workspace_size.argtypes = [GP, I32, I32, VP, VP, SZP]
+    lib.mla_absorbed_attention_sparse.restype = ctypes.c_int
+    lib.mla_absorbed_attention_sparse.argtypes = [GP, I32, I32, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
+                                                  ctypes.c_float, VP, VP, ctypes.c_size_t, VP]
     _lib = lib
     return lib
 

@@ -328,6 +328,64 @@ int mla_absorbed_attention_fp8(const mla_geom* g, int32_t B, int32_t L, const vo
   return hip_status(combine_upproj(q, kBF16, out, s));
 }
 
+namespace {
+// Selections: B >= 1, sel_off[0] >= 0, 1 <= k_b <= Kv_b for every sequence.
+int check_selection(int32_t B, const int32_t* kv_off, const int32_t* sel_off) {
+  if (!sel_off) return MLA_E_NULL;
+  if (sel_off[0] < 0) return MLA_E_SHAPE;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t k = (int64_t)sel_off[b + 1] - sel_off[b];
+    if (k < 1 || k > (int64_t)kv_off[b + 1] - kv_off[b]) return MLA_E_SHAPE;
+  }
+  return MLA_OK;
+}
+}  // namespace
+
+int mla_absorbed_sparse_workspace_size(const mla_geom* g, int32_t B, int32_t L, const int32_t* kv_offsets_host,
+                                       const int32_t* sel_offsets_host, size_t* bytes_out) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!bytes_out) return MLA_E_NULL;
+  if ((st = check_offsets(B, L, kv_offsets_host))) return st;
+  if ((st = check_selection(B, kv_offsets_host, sel_offsets_host))) return st;
+  if ((int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
+  SplitPlan p{};
+  if ((st = make_plan(B, L, g->heads, sel_offsets_host, L * g->heads, 1, g->r, 2, true, &p))) return st;
+  *bytes_out = p.ws_bytes;
+  return MLA_OK;
+}
+
+int mla_absorbed_attention_sparse(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                                  const void* c_kv, const void* k_pe, const int32_t* kv_offsets_host,
+                                  const int32_t* kv_offsets_dev, const int32_t* sel, const int32_t* sel_offsets_host,
+                                  const int32_t* sel_offsets_dev, const void* w_uv, float scale, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if ((st = check_offsets(B, L, kv_offsets_host))) return st;
+  if ((st = check_selection(B, kv_offsets_host, sel_offsets_host))) return st;
+  if ((int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
+  if (!kv_offsets_dev || !sel || !sel_offsets_dev || !q_lat || !c_kv || !w_uv || !out) return MLA_E_NULL;
+  if (g->rope > 0 && (!q_pe || !k_pe)) return MLA_E_NULL;
+  if ((st = absorbed_supported(g, MLA_BF16))) return st;
+  SplitPlan p{};
+  if ((st = make_plan(B, L, g->heads, sel_offsets_host, L * g->heads, 1, g->r, 2, true, &p))) return st;
+  if (!workspace || workspace_bytes < p.ws_bytes) return MLA_E_WORKSPACE;
+  AbsorbedLaunch q{};
+  q.r = g->r; q.rope = g->rope; q.v_dim = g->v; q.H = g->heads; q.B = B; q.L = L;
+  q.q_lat = q_lat; q.q_pe = q_pe; q.c_kv = c_kv; q.k_pe = k_pe; q.w_uv = w_uv;
+  q.off_dev = sel_offsets_dev; q.scale = scale;   // splits and merge run over the selections
+  q.off0 = sel_offsets_host[0]; q.kv1 = sel_offsets_host[1] - sel_offsets_host[0];
+  q.ws_o = workspace;
+  q.ws_ml = (float*)((char*)workspace + align_up(p.ws_o_bytes));
+  q.plan = p;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = hip_status(absorbed_attn_sparse(q, sel, kv_offsets_dev, kv_offsets_host[0],
+                                            kv_offsets_host[1] - kv_offsets_host[0], s))))
+    return st;
+  return hip_status(combine_upproj(q, kBF16, out, s));
+}
+
 int mla_materialize_kv(const mla_geom* g, mla_dtype dt, int64_t T, const void* c_kv, const void* k_pe,
                        const void* w_uk, const void* w_uv, void* k, void* v, void* stream) {
   int st = check_geom(g);

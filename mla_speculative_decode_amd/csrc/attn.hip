@@ -47,6 +47,9 @@ struct AttnArgs {
   const uint16_t* vv;   // value source, row for position p at vv + p*vv_ks + head*vv_hs
   const uint8_t* c8;    // fp8 latent cache (F8): E4M3 codes [T, DA + DR] (latent | rope) ...
   const float* c8s;     // ... and one power-of-two scale per position [T]
+  const int32_t* sel;   // SEL: selected positions per sequence (packed by off; relative, increasing)
+  const int32_t* koff;  // SEL: cache offsets [B+1] (off then indexes the selection)
+  int koff0, kvt1;      // SEL, B == 1: koff[0] and koff[1] - koff[0]
   long long ka_ks, ka_hs, vv_ks, vv_hs;
   const int32_t* off;   // [B+1] device offsets
   int off0, kv1;        // B == 1: off[0] and off[1] - off[0]
@@ -81,7 +84,7 @@ constexpr float kRefSlack = 64.f;
 // fragments straight from the row-major tile with ds_read_b64_tr_b16 (lane l
 // of each 16-lane group receives column l%16 of the 4 rows its group
 // addressed), so there is no transposed copy of V.
-template <int DA, int DR, int DV, bool VK, bool F8 = false>
+template <int DA, int DR, int DV, bool VK, bool F8 = false, bool SEL = false>
 __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   constexpr int D = DA + DR;
   constexpr int BM = 64, BN = 64;
@@ -128,7 +131,31 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     off_b = __builtin_amdgcn_readfirstlane(p.off[b]);
     Kv = __builtin_amdgcn_readfirstlane(p.off[b + 1]) - off_b;
   }
-  const long long p0 = off_b;
+  // SEL: the split runs over the sequence's selected positions: off_b / Kv index
+  // the packed selection, the cache rows start at koff[b], and the causal bound
+  // comes from the cache length Kt.  Selected entries are clamped into the cache.
+  long long pcache = off_b;
+  int Kt = Kv;
+  if (SEL) {
+    pcache = p.B > 1 ? (long long)__builtin_amdgcn_readfirstlane(p.koff[b]) : (long long)p.koff0;
+    Kt = p.B > 1 ? __builtin_amdgcn_readfirstlane(p.koff[b + 1]) - (int)pcache : p.kvt1;
+  }
+  const long long p0 = pcache;
+  const int sel0 = off_b;
+  auto kpos = [&](int j) -> int {   // cache position (from the sequence start) of split index j
+    if (!SEL) return j;
+    return min(max(p.sel[sel0 + j], 0), Kt - 1);
+  };
+  auto visible = [&](int i) -> int {   // split indices query row i may see: positions < Kt - L + i + 1
+    const int bound = Kt - p.L + i + 1;
+    if (!SEL) return bound;
+    int lo = 0, hi = Kv;               // the selection is increasing: count its entries below bound
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.sel[sel0 + mid] < bound) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
   const int k0 = __builtin_amdgcn_readfirstlane(ps * p.chunk);
   const int k1 = __builtin_amdgcn_readfirstlane(min(Kv, k0 + p.chunk));
   const int idx0 = rt * BM;
@@ -159,7 +186,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       static_assert(!VK || DA == 512, "absorbed path loads 1 KB latent rows");
       // one latent row per instruction: uniform row address + constant lane offset
       const int key = wu + 4 * x;
-      const int kr = __builtin_amdgcn_readfirstlane(min(t0 + key, k1 - 1));
+      const int kr = __builtin_amdgcn_readfirstlane(kpos(min(t0 + key, k1 - 1)));
       __builtin_amdgcn_global_load_lds(lbase + kr * DA + 8 * lane,
                                        (__attribute__((address_space(3))) void*)(kdst + key * KRB), 16, 0, 0);
     } else if (x < NLW_K) {
@@ -194,7 +221,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       const int C = tid + 256 * x;
       if (C < BN * RCH) {
         const int key = C / RCH, ch = C % RCH;
-        const unsigned kr = (unsigned)min(t0 + key, k1 - 1);
+        const unsigned kr = (unsigned)kpos(min(t0 + key, k1 - 1));
         rst[x] = ld16(rseq + kr * (unsigned)DR + 8 * ch);
       }
     }
@@ -206,6 +233,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   constexpr int F8C = F8 ? (DA + DR) / 16 : 4;           // 16-code chunks per position
   constexpr int F8X = (F8C + 3) / 4;                      // chunks per thread
   static_assert(!F8 || (VK && (DA + DR) % 64 == 0 && BN * 4 == 256), "fp8 rows: four threads per position");
+  static_assert(!SEL || (VK && !F8), "selection only on the absorbed bf16 route");
   u32x4 f8r[F8 ? F8X : 1];
   float f8s = 0.f;
   auto issue_f8 = [&](int t0, int x) {
@@ -268,10 +296,10 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   {
     const int idx = idx0 + rq;
     const int i = idx / p.hpr;
-    kend = min(k1, Kv - p.L + i + 1);
+    kend = min(k1, visible(i));
   }
   // positions every row of the tile may see (rows are in increasing query order)
-  const int kfull = min(k1, Kv - p.L + idx0 / p.hpr + 1);
+  const int kfull = __builtin_amdgcn_readfirstlane(min(k1, visible(idx0 / p.hpr)));
   if (VK) {
     // absorbed: the rows of the tile are consecutive in q_lat / q_pe.  The query
     // block goes to the idle tile buffer once (q_lat row = one 1 KB direct load,
@@ -299,7 +327,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     // k0 + rt + row_tiles * j, one 4-byte load per 128-byte line (8 latent lines,
     // 1 rope line per position) into a dummy LDS slot.  The row tiles of a split
     // run on one XCD, so the tile copies of the loop then hit L2.
-    if (!F8) {
+    if (!F8 && !SEL) {
       constexpr int LPP = DA / 64 + (DR > 0 ? 1 : 0);   // 128-byte lines per position
       const int cnt = max(0, (k1 - k0 - rt + p.row_tiles - 1) / p.row_tiles);
       const int nl = cnt * LPP;
@@ -1057,6 +1085,27 @@ hipError_t absorbed_attn_fp8(const AbsorbedLaunch& q, const void* codes, const f
   switch (q.rope) {
     case 0:  hipLaunchKernelGGL((attn_bf16_kernel<512, 0, 512, true, true>), grid, dim3(256), 0, st, a); break;
     case 64: hipLaunchKernelGGL((attn_bf16_kernel<512, 64, 512, true, true>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t absorbed_attn_sparse(const AbsorbedLaunch& q, const int32_t* sel, const int32_t* koff_dev, int koff0,
+                                int kvt1, hipStream_t st) {
+  AttnArgs a{};
+  a.qa = (const uint16_t*)q.q_lat; a.qb = (const uint16_t*)q.q_pe;
+  a.ka = (const uint16_t*)q.k_pe; a.ka_ks = q.rope; a.ka_hs = 0;
+  a.vv = (const uint16_t*)q.c_kv; a.vv_ks = q.r; a.vv_hs = 0;
+  a.sel = sel; a.koff = koff_dev; a.koff0 = koff0; a.kvt1 = kvt1;
+  a.off = q.off_dev; a.off0 = q.off0; a.kv1 = q.kv1; a.ws_o = q.ws_o; a.ws_ml = q.ws_ml;
+  a.B = q.B; a.L = q.L; a.H = q.H; a.hpr = q.H; a.rows_slot = q.L * q.H; a.head_slots = 1;
+  a.row_tiles = q.plan.row_tiles; a.chunk = q.plan.chunk; a.n_items = q.plan.n_items;
+  a.rows_total = q.L * q.H; a.sl2 = q.scale * 1.4426950408889634f;
+  if (q.r != 512) return hipErrorInvalidValue;
+  const dim3 grid(grid_xcd(a.n_items));
+  switch (q.rope) {
+    case 0:  hipLaunchKernelGGL((attn_bf16_kernel<512, 0, 512, true, false, true>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((attn_bf16_kernel<512, 64, 512, true, false, true>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,0 +1,83 @@
+"""GPU parity of the absorbed attention over selected positions
+(mla_absorbed_attention_sparse) against the float64 oracle, and bit-identity
+with the dense path when every position is selected."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import sparse
+from mla_speculative_decode_amd import synth
+from tests.helpers import check_close, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+import mla_speculative_decode_amd as mla  # noqa: E402
+from tests.test_parity_gpu import _inputs  # noqa: E402
+
+
+def _sel_dev(sels):
+    sel = np.concatenate(sels).astype(np.int32)
+    soff = np.concatenate([[0], np.cumsum([s.size for s in sels])]).astype(np.int32)
+    return sel, soff, torch.from_numpy(sel).cuda()
+
+
+def _run(case, sels, seed=77):
+    name, r, n, v, rope, H, L, lens, dt = case
+    x = _inputs(case)
+    q_lat = synth.draw_like((len(lens), L, H, r), math.sqrt(n / r), dt, seed=seed)
+    sel, soff, sel_d = _sel_dev(sels)
+    out = mla.absorbed_attention_sparse(dev(q_lat, dt), dev(x.q_pe, dt) if rope else None, dev(x.c_kv, dt),
+                                        dev(x.k_pe, dt) if rope else None, dev(x.w_uv, dt),
+                                        x.offsets.astype(np.int32), sel_d, soff, scale=x.scale)
+    torch.cuda.synchronize()
+    ref = sparse.sparse_latent_attention(q_lat, x.q_pe, x.c_kv, x.k_pe, x.w_uv, x.offsets, sel, soff, L, x.scale)
+    return x, q_lat, out, ref
+
+
+def test_full_selection_equals_dense_path():
+    case = ("full", 512, 128, 128, 64, 16, 4, [300, 77], "bf16")
+    name, r, n, v, rope, H, L, lens, dt = case
+    x, q_lat, out, ref = _run(case, [np.arange(k) for k in lens])
+    dense = mla.absorbed_attention(dev(q_lat, dt), dev(x.q_pe, dt), dev(x.c_kv, dt), dev(x.k_pe, dt),
+                                   dev(x.w_uv, dt), x.offsets.astype(np.int32), scale=x.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dense)
+    check_close(host64(out).reshape(-1, v), ref, "bf16", "sparse full selection")
+
+
+@pytest.mark.parametrize("case,budgets", [
+    (("dsv3_sel", 512, 128, 128, 64, 8, 8, [3000, 700], "bf16"), (512, 300)),
+    (("glm53_sel", 512, 256, 256, 64, 4, 16, [4000], "bf16"), (2048,)),
+    (("norope_sel", 512, 128, 128, 0, 8, 4, [1000, 90, 400], "bf16"), (100, 90, 257)),
+])
+def test_random_selections(case, budgets):
+    name, r, n, v, rope, H, L, lens, dt = case
+    rng = np.random.default_rng(len(name))
+    sels = []
+    for k, m in zip(lens, budgets):
+        s = rng.choice(k - 4, size=m - 4, replace=False)
+        s = np.concatenate([s, np.arange(k - 4, k)])     # the newest positions are selected too
+        sels.append(np.sort(s))
+    x, q_lat, out, ref = _run(case, sels)
+    check_close(host64(out).reshape(-1, v), ref, "bf16", f"sparse {name}")
+
+
+def test_rows_that_see_nothing_output_zero():
+    case = ("late_sel", 512, 128, 128, 64, 4, 8, [200], "bf16")
+    name, r, n, v, rope, H, L, lens, dt = case
+    x, q_lat, out, ref = _run(case, [np.array([195, 197, 199])])
+    got = host64(out).reshape(L, H, v)
+    assert np.all(got[:3] == 0)       # row i sees positions < 193 + i: rows 0..2 see none of 195, 197, 199
+    assert np.all(np.any(got[3:] != 0, axis=-1))
+    check_close(got.reshape(-1, v), ref, "bf16", "sparse late selection")
