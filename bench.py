@@ -6,6 +6,7 @@ float64 CPU oracle timed beside it.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --crossover        # forced-path sweep over L (GLM-4.7-Flash-like geometry)
     python bench.py --verify-curve     # verify cost at L = 1..16 and the derived draft cap
+    python bench.py --sparse 2048      # attention over 2048 selected positions vs dense
 
 A step is one whole absorbed verify call over one batch of synthetic inputs
 already resident in device memory: mla_fold_query (q_lat = q_nope . W_UK),
@@ -84,6 +85,9 @@ def parse():
     ap.add_argument("--verify-curve", action="store_true",
                     help="time the verify call at L = 1..max-width and derive the draft cap from the curve")
     ap.add_argument("--max-width", type=int, default=16, help="largest L of --verify-curve")
+    ap.add_argument("--sparse", type=int, default=0, metavar="BUDGET",
+                    help="time attention over BUDGET selected positions against dense attention, GLM-5.3-like "
+                         "geometry, caches of 2048..32768")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -117,6 +121,9 @@ def main():
         return
     if args.verify_curve:
         verify_curve(args)
+        return
+    if args.sparse:
+        sparse_sweep(args)
         return
     w = synth.WORKLOADS[args.workload]
     if w.dtype != "bf16":
@@ -300,6 +307,69 @@ def verify_curve(args):
             caps.append({"p": p, "drafter": drafter, "cap": cap, "speedup": round(sp, 4)})
     print(json.dumps({"verify_curve_summary": w.name, "relative_cost": [round(u / us[0], 4) for u in us],
                       "derived_caps": caps}), flush=True)
+
+
+def sparse_sweep(args):
+    """Absorbed attention (after the fold) over a selection of `budget` cached
+    positions against dense attention over the whole cache: GLM-5.3-Flash-like
+    geometry (r 512, n 256, v 256, rope 64), 64 heads, L = 16, one sequence, caches
+    of 2048, 8192 and 32768 positions.  The selection is seeded random positions
+    plus the newest L (an indexer's top-k stands in; its scoring is not part of
+    this path).  Cold: a 512 MiB scrub write before every sample; events around
+    the call, median of `samples`."""
+    import torch
+    import mla_speculative_decode_amd as mla
+    from mla_speculative_decode_amd import synth
+
+    budget = args.sparse
+    dev = torch.device("cuda:0")
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    e0.record()
+    torch.cuda._sleep(1_000_000)
+    e1.record()
+    torch.cuda.synchronize()
+    spin = int(1_000_000 * 2.0 / max(e0.elapsed_time(e1), 1e-3))
+    for kv in (2048, 8192, 32768):
+        w = synth.custom(512, 256, 256, 64, 64, 1, 16, kv=kv, dtype="bf16", seed=9, name=f"glm53_h64_kv{kv}_l16")
+        x = synth.make_inputs(w)
+        rng = np.random.default_rng(kv)
+        k = min(budget, kv)
+        sel = np.sort(np.concatenate([rng.choice(kv - w.L, size=k - w.L, replace=False),
+                                      np.arange(kv - w.L, kv)])).astype(np.int32)
+        d = {n: torch.from_numpy(getattr(x, n)).to(torch.bfloat16).to(dev).contiguous()
+             for n in ("q_nope", "q_pe", "c_kv", "k_pe", "w_uk", "w_uv")}
+        q_lat = mla.fold_query(d["q_nope"], d["w_uk"])
+        offs = mla.Offsets(x.offsets.astype(np.int32), dev)
+        soffs = mla.Offsets(np.array([0, k], dtype=np.int32), dev)
+        sel_d = torch.from_numpy(sel).to(dev)
+        out = torch.empty((1, w.L, w.heads, w.v), dtype=torch.float32, device=dev)
+        arms = {
+            "sparse": lambda: mla.absorbed_attention_sparse(q_lat, d["q_pe"], d["c_kv"], d["k_pe"], d["w_uv"], offs,
+                                                            sel_d, soffs, scale=x.scale, out=out),
+            "dense": lambda: mla.absorbed_attention(q_lat, d["q_pe"], d["c_kv"], d["k_pe"], d["w_uv"], offs,
+                                                    scale=x.scale, out=out),
+        }
+        for f in arms.values():
+            f()
+        times = {a: [] for a in arms}
+        for i in range(args.samples):
+            for a in (("sparse", "dense") if i % 2 == 0 else ("dense", "sparse")):
+                scrub.fill_(i & 255)
+                torch.cuda._sleep(spin)
+                e0.record()
+                arms[a]()
+                e1.record()
+                torch.cuda.synchronize()
+                times[a].append(e0.elapsed_time(e1) * 1e3)
+        print(json.dumps({"sparse_attention": w.name, "kv": kv, "budget": k,
+                          "sparse_us": round(float(np.median(times["sparse"])), 2),
+                          "dense_us": round(float(np.median(times["dense"])), 2),
+                          "samples": args.samples, "cache_state": "cold (512 MiB scrub before each sample)"}),
+              flush=True)
+        del d, q_lat, out, sel_d
+        torch.cuda.empty_cache()
 
 
 def crossover(args):

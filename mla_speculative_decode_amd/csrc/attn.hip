@@ -146,18 +146,35 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     if (!SEL) return j;
     return min(max(p.sel[sel0 + j], 0), Kt - 1);
   };
+  const int k0 = __builtin_amdgcn_readfirstlane(ps * p.chunk);
+  const int k1 = __builtin_amdgcn_readfirstlane(min(Kv, k0 + p.chunk));
+  // SEL: the entries at or above a row's bound Kt - L + i + 1 are among the
+  // selection's last L - 1 (they are distinct positions above Kt - L): count them
+  // from a register holding that tail (lane j: the j-th entry from the end).
+  const int ntail = min(p.L - 1, Kv);
+  int tailv = -1;
+  if (SEL && ntail <= kWave && lane < ntail) tailv = p.sel[sel0 + Kv - 1 - lane];
   auto visible = [&](int i) -> int {   // split indices query row i may see: positions < Kt - L + i + 1
     const int bound = Kt - p.L + i + 1;
     if (!SEL) return bound;
-    int lo = 0, hi = Kv;               // the selection is increasing: count its entries below bound
+    if (ntail <= kWave) {
+      int above = 0;
+      for (int j = 0; j < ntail; ++j) above += __builtin_amdgcn_readlane(tailv, j) >= bound ? 1 : 0;
+      return Kv - above;
+    }
+    int lo = 0, hi = Kv;               // long blocks: binary search of the increasing selection
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (p.sel[sel0 + mid] < bound) lo = mid + 1; else hi = mid;
     }
     return lo;
   };
-  const int k0 = __builtin_amdgcn_readfirstlane(ps * p.chunk);
-  const int k1 = __builtin_amdgcn_readfirstlane(min(Kv, k0 + p.chunk));
+  // SEL: cache positions of the 64 keys of the next tile to copy, lane j -> key j;
+  // loaded one step ahead so the copy's row addresses wait for nothing
+  int sidx = 0;
+  auto load_idx = [&](int t0) {
+    if (SEL) sidx = kpos(min(t0 + lane, k1 - 1));
+  };
   const int idx0 = rt * BM;
   const int nrows = min(BM, p.rows_slot - idx0);
 
@@ -186,7 +203,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       static_assert(!VK || DA == 512, "absorbed path loads 1 KB latent rows");
       // one latent row per instruction: uniform row address + constant lane offset
       const int key = wu + 4 * x;
-      const int kr = __builtin_amdgcn_readfirstlane(kpos(min(t0 + key, k1 - 1)));
+      const int kr = SEL ? __builtin_amdgcn_readlane(sidx, key) : __builtin_amdgcn_readfirstlane(min(t0 + key, k1 - 1));
       __builtin_amdgcn_global_load_lds(lbase + kr * DA + 8 * lane,
                                        (__attribute__((address_space(3))) void*)(kdst + key * KRB), 16, 0, 0);
     } else if (x < NLW_K) {
@@ -221,7 +238,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       const int C = tid + 256 * x;
       if (C < BN * RCH) {
         const int key = C / RCH, ch = C % RCH;
-        const unsigned kr = (unsigned)kpos(min(t0 + key, k1 - 1));
+        const unsigned kr = SEL ? (unsigned)__shfl(sidx, key, kWave) : (unsigned)min(t0 + key, k1 - 1);
         rst[x] = ld16(rseq + kr * (unsigned)DR + 8 * ch);
       }
     }
@@ -292,7 +309,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   int kend = 0;   // positions this row may see within the split (relative to sequence start)
   u32x4 qf[DCH];
 
+  load_idx(k0);
   issue_tile(k0, buf0);   // first tile in flight while the queries load
+  load_idx(k0 + BN);
   {
     const int idx = idx0 + rq;
     const int i = idx / p.hpr;
@@ -570,6 +589,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     if (pf) {   // the other buffer is not read until barrier (A)
       if (F8) store_f8(nxt); else if (VK) store_rope(nxt);
     }
+    load_idx(t0 + 2 * BN);   // keys of the tile the next step copies
   };
   // Tiles go in pairs (one per buffer); an odd tile count skips the second
   // step of the last pair.  No copy follows the last tile.
@@ -600,7 +620,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         for (int i = 0; i < 16; ++i) O[rb][cb][i] = 0.f;
     l_run = 0.f;
     t_max = -INFINITY;
+    load_idx(k0);
     issue_tile(k0, buf0);
+    load_idx(k0 + BN);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (F8) store_f8(buf0); else if (VK) store_rope(buf0);
   }
