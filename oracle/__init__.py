@@ -22,6 +22,7 @@ from . import threshold  # noqa: F401  (re-exported)
 from . import draft_cap  # noqa: F401  (re-exported)
 from . import fp8  # noqa: F401  (re-exported)
 from . import sparse  # noqa: F401  (re-exported)
+from . import indexer  # noqa: F401  (re-exported)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mla_oracle.c")
