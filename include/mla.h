@@ -292,6 +292,112 @@ int mla_absorbed_attention_sparse(const mla_geom* g, int32_t B, int32_t L, const
                                   const int32_t* sel_offsets_dev, const void* w_uv, float scale, float* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Pooled top-k indexer ("One guard, 110x off the verify step", sections "The
+ * sparse model is different" and "The same bug, one layer over").  The indexer
+ * pools the cached keys of each sequence into windows of four positions
+ * (window w = positions 4w .. 4w+3, the last one possibly partial), scores the
+ * windows, and picks the top `budget` positions for mla_absorbed_attention_sparse.
+ *
+ *   pooled key of window w = float32 mean of its bf16 key rows, summed in
+ *                            position order (so a window pools to the same bits
+ *                            however its positions arrived);
+ *   score of window w      = q_b . pooled[w] in float32 (the pages do not define
+ *                            the score; this is the library's reading);
+ *   selection              = the first min(budget, Kv_b) positions in the order
+ *                            (window score descending, position ascending),
+ *                            written in increasing position order.
+ *
+ * The pool caches completed windows.  A step that appended S positions to
+ * every sequence recomputes only the windows from floor((Kv_b - S) / 4) on if
+ * all four guards hold: the pool holds keys, the cache has no padding, the
+ * batch shape (sequence count, key width) is the one the pool was built for,
+ * and every cache is exactly as long (minus S) as the pool remembers.
+ * Otherwise every window is recomputed.  A wide step therefore pools exactly
+ * as the same positions fed one at a time.  A cache cut back after a
+ * speculative rejection either fails the last guard (full recompute) or is
+ * announced with mla_indexer_pool_trim, after which the windows wholly before
+ * the cut are kept.
+ *
+ * The pool's state lives in a caller-owned mla_pool on the host; its pooled
+ * keys in a caller-owned device buffer [batch_max][capacity][d] float32.
+ */
+typedef struct mla_pool {
+  float* pooled;        /* device [batch_max][capacity][d] float32 (caller-owned)        */
+  int32_t capacity;     /* windows per sequence the buffer holds                          */
+  int32_t batch_max;    /* sequences the buffer (and lengths) hold                        */
+  int32_t batch;        /* sequences the pool was last built for                          */
+  int32_t d;            /* key width the pool was last built for                          */
+  int32_t valid;        /* 1 once a step has pooled keys; 0 after init or a failed step   */
+  int32_t* lengths;     /* host [batch_max]: cache length per sequence the pool covers    */
+} mla_pool;
+
+/* Initialise *pool over caller-owned storage (nothing is launched).  Errors:
+ * MLA_E_NULL (pool, pooled or lengths NULL), MLA_E_SHAPE (capacity or
+ * batch_max < 1). */
+int mla_indexer_pool_init(mla_pool* pool, float* pooled, int32_t capacity, int32_t batch_max, int32_t* lengths);
+
+/* The guard decision alone (host only, nothing launched): *incremental_out = 1
+ * if a step of S new positions per sequence over caches with these offsets
+ * would recompute only the tail, 0 if it would recompute every window.
+ * padded != 0 declares that the cache rows of a sequence are not its positions
+ * from 0 (padding).  Errors: MLA_E_NULL, MLA_E_SHAPE (B < 1, S < 1, a Kv_b < S). */
+int mla_indexer_pool_plan(const mla_pool* pool, int32_t B, int32_t d, const int32_t* kv_offsets_host, int32_t S,
+                          int32_t padded, int32_t* incremental_out);
+
+/*
+ * mla_indexer_pool_step -- bring the pool up to date after a step that
+ * appended S positions to every sequence.
+ *   keys: device bf16, row of position p of sequence b at
+ *         keys + (kv_offsets[b] + p) * key_stride (elements), d columns used
+ *   kv_offsets_host / kv_offsets_dev: the cache offsets as everywhere else
+ *   incremental_out (may be NULL): which path ran (as mla_indexer_pool_plan)
+ * On success pool->lengths[b] = Kv_b, batch = B, d = d, valid = 1.
+ * Supported: d a multiple of 8, 8 <= d <= 1024.  Errors: MLA_E_NULL,
+ * MLA_E_SHAPE (B outside [1, batch_max], S < 1, a Kv_b < S, key_stride < d,
+ * ceil(Kv_b / 4) > capacity), MLA_E_UNSUPPORTED (d), MLA_E_HIP (the pool is then
+ * marked invalid, so the next step recomputes everything).
+ */
+int mla_indexer_pool_step(mla_pool* pool, int32_t B, int32_t d, const void* keys, int64_t key_stride,
+                          const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, int32_t S, int32_t padded,
+                          int32_t* incremental_out, void* stream);
+
+/* A speculative rejection cut sequence b's cache back to new_lengths[b]
+ * positions (host array [B]): the pool forgets what it covered past the cut
+ * (host only; the next step recomputes from the window holding the cut).
+ * Entries not below the remembered length change nothing.  Errors: MLA_E_NULL,
+ * MLA_E_SHAPE (pool not valid, B != pool->batch, a negative length). */
+int mla_indexer_pool_trim(mla_pool* pool, int32_t B, const int32_t* new_lengths);
+
+/*
+ * mla_indexer_scores -- scores[b * capacity + w] = q[b] . pooled key of window
+ * w, for w < ceil(Kv_b / 4) (the rest untouched).  q: device float32 [B][d].
+ * The pool must cover the caches as they are (pool->lengths[b] == Kv_b).
+ * Errors: MLA_E_NULL, MLA_E_SHAPE (pool not valid, B != pool->batch, a length
+ * not covered), MLA_E_HIP.
+ */
+int mla_indexer_scores(const mla_pool* pool, int32_t B, const float* q, const int32_t* kv_offsets_host,
+                       const int32_t* kv_offsets_dev, float* scores, void* stream);
+
+/* Offsets of the packed selection (host only): sel_offsets_out[0] = 0,
+ * sel_offsets_out[b+1] = sel_offsets_out[b] + min(budget, Kv_b).  Errors:
+ * MLA_E_NULL, MLA_E_SHAPE (B < 1, budget < 1, bad offsets). */
+int mla_indexer_selection_offsets(int32_t B, const int32_t* kv_offsets_host, int32_t budget,
+                                  int32_t* sel_offsets_out);
+
+/*
+ * mla_indexer_select -- the selection of sequence b into sel[sel_offsets[b] ..
+ * sel_offsets[b+1]) (device int32, positions from the sequence start,
+ * increasing), from window scores [B][capacity] (device float32, windows
+ * w < ceil(Kv_b / 4) read).  Scores must not be NaN (their order is then
+ * unspecified); -0 and +0 are equal.  sel_offsets_dev must hold what
+ * mla_indexer_selection_offsets gives.  Errors: MLA_E_NULL, MLA_E_SHAPE (B < 1,
+ * budget < 1, bad offsets, ceil(Kv_b / 4) > capacity), MLA_E_HIP.
+ */
+int mla_indexer_select(int32_t B, const float* scores, int32_t capacity, const int32_t* kv_offsets_host,
+                       const int32_t* kv_offsets_dev, int32_t budget, const int32_t* sel_offsets_dev, int32_t* sel,
+                       void* stream);
+
 /* Bytes of workspace mla_materialized_attention needs (split-KV partials). */
 int mla_materialized_workspace_size(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
                                     const int32_t* kv_offsets_host, size_t* bytes_out);

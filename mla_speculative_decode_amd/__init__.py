@@ -25,7 +25,7 @@ __all__ = ["Geom", "MlaError", "MLA_ABSORBED", "MLA_MATERIALIZED", "Offsets", "s
            "fold_query", "absorbed_workspace_size", "absorbed_attention", "absorbed_splits",
            "absorbed_merge", "materialize_kv",
            "materialized_workspace_size", "materialized_attention", "absorbed", "materialized",
-           "library_path"]
+           "library_path", "IndexerPool", "selection_offsets", "indexer_select"]
 
 
 def library_path() -> str:
@@ -335,6 +335,100 @@ def absorbed_attention_sparse(q_lat, q_pe, c_kv, k_pe, w_uv, kv_offsets, sel, se
         soffs.dev_ptr(), _ptr(_dev(w_uv, "w_uv")), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+class IndexerPool:
+    """Pooled keys of the top-k indexer (windows of four positions) for up to
+    batch_max sequences of up to 4 * capacity cached positions, key width d.
+    step() after every step that appended S positions per sequence: the tail
+    only when the four guards hold, every window otherwise."""
+
+    def __init__(self, capacity: int, batch_max: int, d: int, device=None):
+        torch = _torch()
+        self.pooled = torch.empty((batch_max, capacity, d), dtype=torch.float32,
+                                  device=device if device is not None else "cuda")
+        self.lengths = torch.zeros(batch_max, dtype=torch.int32)
+        self.d = d
+        self.state = _lib.Pool()
+        _lib.check("mla_indexer_pool_init", _lib.load().mla_indexer_pool_init(
+            ctypes.byref(self.state), ctypes.c_void_p(self.pooled.data_ptr()), capacity, batch_max,
+            ctypes.c_void_p(self.lengths.data_ptr())))
+
+    @property
+    def capacity(self) -> int:
+        return int(self.state.capacity)
+
+    @property
+    def valid(self) -> bool:
+        return bool(self.state.valid)
+
+    def plan(self, kv_offsets, S: int, padded: bool = False) -> bool:
+        """Would a step of S new positions recompute only the tail?"""
+        offs = kv_offsets if isinstance(kv_offsets, Offsets) else Offsets(kv_offsets, self.pooled.device)
+        inc = ctypes.c_int32()
+        _lib.check("mla_indexer_pool_plan", _lib.load().mla_indexer_pool_plan(
+            ctypes.byref(self.state), offs.B, self.d, offs.host_ptr(), S, int(padded), ctypes.byref(inc)))
+        return bool(inc.value)
+
+    def step(self, keys, kv_offsets, S: int, padded: bool = False, stream=None) -> bool:
+        """Pool after a step; keys: bf16 device tensor whose rows are the cached
+        positions (row stride keys.stride(0), first d columns).  Returns True if
+        only the tail was recomputed."""
+        torch = _torch()
+        if keys.dtype != torch.bfloat16 or keys.dim() != 2 or keys.stride(1) != 1 or keys.shape[1] < self.d:
+            raise ValueError("keys must be a bf16 [T, >= d] device tensor with unit column stride")
+        offs = kv_offsets if isinstance(kv_offsets, Offsets) else Offsets(kv_offsets, keys.device)
+        inc = ctypes.c_int32()
+        _lib.check("mla_indexer_pool_step", _lib.load().mla_indexer_pool_step(
+            ctypes.byref(self.state), offs.B, self.d, ctypes.c_void_p(_dev(keys, "keys").data_ptr()),
+            keys.stride(0), offs.host_ptr(), offs.dev_ptr(), S, int(padded), ctypes.byref(inc), _stream(stream)))
+        return bool(inc.value)
+
+    def trim(self, new_lengths) -> None:
+        torch = _torch()
+        nl = torch.as_tensor(new_lengths, dtype=torch.int32).contiguous()
+        _lib.check("mla_indexer_pool_trim", _lib.load().mla_indexer_pool_trim(
+            ctypes.byref(self.state), nl.numel(), ctypes.c_void_p(nl.data_ptr())))
+
+    def scores(self, q, kv_offsets, out=None, stream=None):
+        """Window scores [B, capacity] (float32; windows past a sequence's last untouched)."""
+        torch = _torch()
+        offs = kv_offsets if isinstance(kv_offsets, Offsets) else Offsets(kv_offsets, q.device)
+        if q.dtype != torch.float32 or tuple(q.shape) != (offs.B, self.d):
+            raise ValueError("q must be float32 [B, d]")
+        if out is None:
+            out = torch.zeros((offs.B, self.capacity), dtype=torch.float32, device=q.device)
+        _lib.check("mla_indexer_scores", _lib.load().mla_indexer_scores(
+            ctypes.byref(self.state), offs.B, _ptr(_dev(q, "q")), offs.host_ptr(), offs.dev_ptr(), _ptr(out),
+            _stream(stream)))
+        return out
+
+
+def selection_offsets(kv_offsets, budget: int, device=None) -> Offsets:
+    """Offsets of the packed selection: sequence b gets min(budget, Kv_b) positions."""
+    torch = _torch()
+    offs = kv_offsets if isinstance(kv_offsets, Offsets) else Offsets(kv_offsets, device)
+    so = torch.empty(offs.B + 1, dtype=torch.int32)
+    _lib.check("mla_indexer_selection_offsets", _lib.load().mla_indexer_selection_offsets(
+        offs.B, offs.host_ptr(), budget, ctypes.c_void_p(so.data_ptr())))
+    return Offsets(so, offs.dev.device if device is None else device)
+
+
+def indexer_select(scores, kv_offsets, budget: int, sel_offsets: Offsets | None = None, out=None, stream=None):
+    """Top-budget positions per sequence from window scores [B, capacity]:
+    returns (sel int32 device tensor, sel_offsets)."""
+    torch = _torch()
+    offs = kv_offsets if isinstance(kv_offsets, Offsets) else Offsets(kv_offsets, scores.device)
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.shape[0] != offs.B:
+        raise ValueError("scores must be float32 [B, capacity]")
+    if sel_offsets is None:
+        sel_offsets = selection_offsets(offs, budget)
+    if out is None:
+        out = torch.empty(max(int(sel_offsets.host[-1]), 1), dtype=torch.int32, device=scores.device)
+    _lib.check("mla_indexer_select", _lib.load().mla_indexer_select(
+        offs.B, _ptr(_dev(scores, "scores")), scores.shape[1], offs.host_ptr(), offs.dev_ptr(), budget,
+        sel_offsets.dev_ptr(), _ptr(out), _stream(stream)))
+    return out, sel_offsets
 
 
 def absorbed(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, kv_offsets, scale=None, stream=None, q_lat=None,

@@ -22,7 +22,9 @@ EXPORTS = ("mla_status_string", "mla_version", "mla_select_path", "mla_draft_cap
            "mla_absorbed_merge", "mla_materialize_kv",
            "mla_materialized_workspace_size", "mla_materialized_attention", "mla_quantize_latent_fp8",
            "mla_absorbed_attention_fp8", "mla_absorbed_splits_fp8", "mla_absorbed_sparse_workspace_size",
-           "mla_absorbed_attention_sparse")
+           "mla_absorbed_attention_sparse", "mla_indexer_pool_init", "mla_indexer_pool_plan",
+           "mla_indexer_pool_step", "mla_indexer_pool_trim", "mla_indexer_scores", "mla_indexer_selection_offsets",
+           "mla_indexer_select")
 
 
 class Geom(ctypes.Structure):
@@ -31,6 +33,13 @@ class Geom(ctypes.Structure):
 
     def __repr__(self):
         return f"Geom(r={self.r}, n={self.n}, v={self.v}, rope={self.rope}, heads={self.heads})"
+
+
+class Pool(ctypes.Structure):
+    """mla_pool: host-side state of the indexer's pooled keys."""
+    _fields_ = [("pooled", ctypes.c_void_p), ("capacity", ctypes.c_int32), ("batch_max", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("d", ctypes.c_int32), ("valid", ctypes.c_int32),
+                ("lengths", ctypes.POINTER(ctypes.c_int32))]
 
 
 class MlaError(RuntimeError):
@@ -100,6 +109,17 @@ def load() -> ctypes.CDLL:
     lib.mla_absorbed_attention_sparse.restype = ctypes.c_int
     lib.mla_absorbed_attention_sparse.argtypes = [GP, I32, I32, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
                                                   ctypes.c_float, VP, VP, ctypes.c_size_t, VP]
+    PP = ctypes.POINTER(Pool)
+    for name, args in (("mla_indexer_pool_init", [PP, VP, I32, I32, VP]),
+                       ("mla_indexer_pool_plan", [PP, I32, I32, VP, I32, I32, I32P]),
+                       ("mla_indexer_pool_step", [PP, I32, I32, VP, I64, VP, VP, I32, I32, I32P, VP]),
+                       ("mla_indexer_pool_trim", [PP, I32, VP]),
+                       ("mla_indexer_scores", [PP, I32, VP, VP, VP, VP, VP]),
+                       ("mla_indexer_selection_offsets", [I32, VP, I32, VP]),
+                       ("mla_indexer_select", [I32, VP, I32, VP, VP, I32, VP, VP, VP])):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = args
     _lib = lib
     return lib
 

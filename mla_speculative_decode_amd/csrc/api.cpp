@@ -445,4 +445,138 @@ int mla_materialized_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32
   return hip_status(combine_materialized(q, dt == MLA_BF16 ? kBF16 : kF32, out, s));
 }
 
+
+// ---- pooled top-k indexer ------------------------------------------------------
+namespace {
+constexpr int kPoolWindow = 4;
+int64_t pool_windows(int64_t T) { return (T + kPoolWindow - 1) / kPoolWindow; }
+
+// offsets: off[0] >= 0, non-decreasing, every Kv_b >= min_len
+int check_plain_offsets(int32_t B, const int32_t* off, int64_t min_len) {
+  if (!off) return MLA_E_NULL;
+  if (B < 1 || off[0] < 0) return MLA_E_SHAPE;
+  for (int32_t b = 0; b < B; ++b)
+    if ((int64_t)off[b + 1] - off[b] < min_len) return MLA_E_SHAPE;
+  return MLA_OK;
+}
+
+bool pool_guards_hold(const mla_pool* pool, int32_t B, int32_t d, const int32_t* off, int32_t S, int32_t padded) {
+  if (!pool->valid) return false;                              // the cache has a pool
+  if (padded) return false;                                    // there is no padding
+  if (pool->batch != B || pool->d != d) return false;          // the batch shape matches
+  for (int32_t b = 0; b < B; ++b)                              // the cache is as long as remembered
+    if ((int64_t)pool->lengths[b] != (int64_t)off[b + 1] - off[b] - S) return false;
+  return true;
+}
+}  // namespace
+
+int mla_indexer_pool_init(mla_pool* pool, float* pooled, int32_t capacity, int32_t batch_max, int32_t* lengths) {
+  if (!pool || !pooled || !lengths) return MLA_E_NULL;
+  if (capacity < 1 || batch_max < 1) return MLA_E_SHAPE;
+  pool->pooled = pooled;
+  pool->capacity = capacity;
+  pool->batch_max = batch_max;
+  pool->batch = 0;
+  pool->d = 0;
+  pool->valid = 0;
+  pool->lengths = lengths;
+  for (int32_t b = 0; b < batch_max; ++b) lengths[b] = 0;
+  return MLA_OK;
+}
+
+int mla_indexer_pool_plan(const mla_pool* pool, int32_t B, int32_t d, const int32_t* kv_offsets_host, int32_t S,
+                          int32_t padded, int32_t* incremental_out) {
+  if (!pool || !incremental_out || !pool->lengths) return MLA_E_NULL;
+  if (S < 1) return MLA_E_SHAPE;
+  int st = check_plain_offsets(B, kv_offsets_host, S);
+  if (st) return st;
+  if (B > pool->batch_max) return MLA_E_SHAPE;
+  *incremental_out = pool_guards_hold(pool, B, d, kv_offsets_host, S, padded) ? 1 : 0;
+  return MLA_OK;
+}
+
+int mla_indexer_pool_step(mla_pool* pool, int32_t B, int32_t d, const void* keys, int64_t key_stride,
+                          const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, int32_t S, int32_t padded,
+                          int32_t* incremental_out, void* stream) {
+  if (!pool || !pool->pooled || !pool->lengths || !keys || !kv_offsets_dev) return MLA_E_NULL;
+  if (S < 1 || key_stride < d) return MLA_E_SHAPE;
+  int st = check_plain_offsets(B, kv_offsets_host, S);
+  if (st) return st;
+  if (B > pool->batch_max) return MLA_E_SHAPE;
+  if (d < 8 || d > 1024 || d % 8 != 0) return MLA_E_UNSUPPORTED;
+  const bool inc = pool_guards_hold(pool, B, d, kv_offsets_host, S, padded);
+  int64_t wmax = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t kv = (int64_t)kv_offsets_host[b + 1] - kv_offsets_host[b];
+    if (pool_windows(kv) > pool->capacity) return MLA_E_SHAPE;
+    const int64_t first = inc ? (kv - S) / kPoolWindow : 0;
+    wmax = std::max(wmax, pool_windows(kv) - first);
+  }
+  if ((int64_t)kv_offsets_host[B] * key_stride > INT64_MAX / 2) return MLA_E_SHAPE;
+  pool->valid = 0;   // until the launch is known to be enqueued
+  st = hip_status(indexer_pool(keys, key_stride, kv_offsets_dev, B, d, S, !inc, (int)wmax, pool->pooled,
+                               pool->capacity, (hipStream_t)stream));
+  if (st) return st;
+  for (int32_t b = 0; b < B; ++b) pool->lengths[b] = kv_offsets_host[b + 1] - kv_offsets_host[b];
+  pool->batch = B;
+  pool->d = d;
+  pool->valid = 1;
+  if (incremental_out) *incremental_out = inc ? 1 : 0;
+  return MLA_OK;
+}
+
+int mla_indexer_pool_trim(mla_pool* pool, int32_t B, const int32_t* new_lengths) {
+  if (!pool || !new_lengths || !pool->lengths) return MLA_E_NULL;
+  if (!pool->valid || B != pool->batch) return MLA_E_SHAPE;
+  for (int32_t b = 0; b < B; ++b)
+    if (new_lengths[b] < 0) return MLA_E_SHAPE;
+  for (int32_t b = 0; b < B; ++b) pool->lengths[b] = std::min(pool->lengths[b], new_lengths[b]);
+  return MLA_OK;
+}
+
+int mla_indexer_scores(const mla_pool* pool, int32_t B, const float* q, const int32_t* kv_offsets_host,
+                       const int32_t* kv_offsets_dev, float* scores, void* stream) {
+  if (!pool || !pool->pooled || !pool->lengths || !q || !kv_offsets_dev || !scores) return MLA_E_NULL;
+  int st = check_plain_offsets(B, kv_offsets_host, 1);
+  if (st) return st;
+  if (!pool->valid || B != pool->batch) return MLA_E_SHAPE;
+  int64_t wmax = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t kv = (int64_t)kv_offsets_host[b + 1] - kv_offsets_host[b];
+    if (pool->lengths[b] != kv) return MLA_E_SHAPE;   // the pool must cover the cache as it is
+    wmax = std::max(wmax, pool_windows(kv));
+  }
+  return hip_status(indexer_scores(pool->pooled, pool->capacity, pool->d, q, kv_offsets_dev, B, (int)wmax, scores,
+                                   (hipStream_t)stream));
+}
+
+int mla_indexer_selection_offsets(int32_t B, const int32_t* kv_offsets_host, int32_t budget,
+                                  int32_t* sel_offsets_out) {
+  if (!sel_offsets_out) return MLA_E_NULL;
+  if (budget < 1) return MLA_E_SHAPE;
+  int st = check_plain_offsets(B, kv_offsets_host, 1);
+  if (st) return st;
+  int64_t acc = 0;
+  for (int32_t b = 0; b < B; ++b) acc += std::min<int64_t>(budget, (int64_t)kv_offsets_host[b + 1] - kv_offsets_host[b]);
+  if (acc > INT32_MAX) return MLA_E_SHAPE;
+  sel_offsets_out[0] = 0;
+  for (int32_t b = 0; b < B; ++b)
+    sel_offsets_out[b + 1] =
+        sel_offsets_out[b] + (int32_t)std::min<int64_t>(budget, (int64_t)kv_offsets_host[b + 1] - kv_offsets_host[b]);
+  return MLA_OK;
+}
+
+int mla_indexer_select(int32_t B, const float* scores, int32_t capacity, const int32_t* kv_offsets_host,
+                       const int32_t* kv_offsets_dev, int32_t budget, const int32_t* sel_offsets_dev, int32_t* sel,
+                       void* stream) {
+  if (!scores || !kv_offsets_dev || !sel_offsets_dev || !sel) return MLA_E_NULL;
+  if (budget < 1 || capacity < 1) return MLA_E_SHAPE;
+  int st = check_plain_offsets(B, kv_offsets_host, 1);
+  if (st) return st;
+  for (int32_t b = 0; b < B; ++b)
+    if (pool_windows((int64_t)kv_offsets_host[b + 1] - kv_offsets_host[b]) > capacity) return MLA_E_SHAPE;
+  return hip_status(indexer_select(scores, capacity, kv_offsets_dev, B, budget, sel_offsets_dev, sel,
+                                   (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1,5 +1,5 @@
 // internal.h -- launch descriptors shared between the C ABI layer (api.cpp)
-// and the kernel files (attn.hip, gemm.hip).  Not part of the public ABI.
+// and the kernel files (attn.hip, gemm.hip, quant.hip, indexer.hip).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -56,6 +56,14 @@ hipError_t combine_upproj(const AbsorbedLaunch& q, mla_dtype_t dt, float* out, h
 // quant.hip
 hipError_t quantize_latent_fp8(long long T, int r, int rope, const void* c_kv, const void* k_pe, void* codes,
                                float* scales, hipStream_t st);
+
+// indexer.hip
+hipError_t indexer_pool(const void* keys, long long ld, const int32_t* off_dev, int B, int d, int S, bool full,
+                        int wmax, float* pooled, int cap, hipStream_t st);
+hipError_t indexer_scores(const float* pooled, int cap, int d, const float* q, const int32_t* off_dev, int B,
+                          int wmax, float* scores, hipStream_t st);
+hipError_t indexer_select(const float* scores, int cap, const int32_t* off_dev, int B, int budget,
+                          const int32_t* sel_off_dev, int32_t* sel, hipStream_t st);
 
 // gemm.hip
 struct GemmArgs {

@@ -153,6 +153,30 @@ def draw_like(shape, std: float, dtype: str, seed: int) -> np.ndarray:
     return _draw(rng, shape, std, dtype)
 
 
+# Pooled-indexer workload: one sequence of 131072 cached positions (the longest
+# context the pages measure the indexer at), a verify step of 8 new positions,
+# keys = the bf16 latent rows (width 512), top-2048 budget.
+INDEXER_WORKLOAD = dict(name="indexer_kv131072_s8_d512_top2048", kv=131072, S=8, d=512, budget=2048, seed=6)
+
+
+@dataclass
+class IndexerInputs:
+    offsets: np.ndarray                     # int64 [B+1], cache lengths after the step
+    keys: np.ndarray                        # [sumKv, d] bf16-exact float32 ~ N(0, 1)
+    q: np.ndarray                           # [B, d] float32 ~ N(0, 1/d): the indexer query of the step
+
+
+def indexer_inputs(lengths, d: int, seed: int) -> IndexerInputs:
+    """Seeded keys and queries for the pooled indexer (draw order: keys, q)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = np.asarray(lengths, dtype=np.int64)
+    offsets = np.zeros(lens.size + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(lens)
+    keys = _draw(rng, (int(offsets[-1]), d), 1.0, "bf16")
+    q = _draw(rng, (lens.size, d), 1.0 / math.sqrt(d), "f32")
+    return IndexerInputs(offsets, keys, q)
+
+
 def custom(r: int, n: int, v: int, rope: int, heads: int, batch: int, L: int, kv: int | None = None,
            kv_range: tuple[int, int] | None = None, dtype: str = "bf16", seed: int = 0,
            name: str = "custom") -> Workload:
