@@ -7,6 +7,7 @@ float64 CPU oracle timed beside it.
     python bench.py --crossover        # forced-path sweep over L (GLM-4.7-Flash-like geometry)
     python bench.py --verify-curve     # verify cost at L = 1..16 and the derived draft cap
     python bench.py --sparse 2048      # attention over 2048 selected positions vs dense
+    python bench.py --indexer          # pooled top-k indexer step: incremental tail vs full pooling
 
 A step is one whole absorbed verify call over one batch of synthetic inputs
 already resident in device memory: mla_fold_query (q_lat = q_nope . W_UK),
@@ -88,6 +89,9 @@ def parse():
     ap.add_argument("--sparse", type=int, default=0, metavar="BUDGET",
                     help="time attention over BUDGET selected positions against dense attention, GLM-5.3-like "
                          "geometry, caches of 2048..32768")
+    ap.add_argument("--indexer", action="store_true",
+                    help="time the pooled top-k indexer step (tail vs full pooling, scores, selection) and the "
+                         "sparse attention it feeds, caches of 8192 and 131072")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -124,6 +128,9 @@ def main():
         return
     if args.sparse:
         sparse_sweep(args)
+        return
+    if args.indexer:
+        indexer_sweep(args)
         return
     w = synth.WORKLOADS[args.workload]
     if w.dtype != "bf16":
@@ -369,6 +376,108 @@ def sparse_sweep(args):
                           "samples": args.samples, "cache_state": "cold (512 MiB scrub before each sample)"}),
               flush=True)
         del d, q_lat, out, sel_d
+        torch.cuda.empty_cache()
+
+
+def indexer_sweep(args):
+    """The pooled top-k indexer of a sparse layer, one sequence, a verify step
+    of S = 8 new positions, keys = the bf16 latent rows (width 512), budget 2048:
+    the whole indexer step (pooling, scores, selection) with the incremental
+    tail (guards hold) against pooling the whole cache, each kernel on its own,
+    and the absorbed attention over the selected positions that follows
+    (GLM-5.3-Flash-like geometry, 64 heads, the step's 8 rows).  Cold: a 512 MiB
+    scrub write before every sample; the host queues a sample's launches behind
+    a 2 ms device spin, so they run back to back; events around each piece,
+    median of `samples`, arms interleaved."""
+    import torch
+    import mla_speculative_decode_amd as mla
+    from mla_speculative_decode_amd import synth
+
+    wl = synth.INDEXER_WORKLOAD
+    S, d, budget = wl["S"], wl["d"], wl["budget"]
+    dev = torch.device("cuda:0")
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    torch.cuda._sleep(1000)
+    ev[0].record()
+    torch.cuda._sleep(1_000_000)
+    ev[1].record()
+    torch.cuda.synchronize()
+    spin = int(1_000_000 * 2.0 / max(ev[0].elapsed_time(ev[1]), 1e-3))
+    for T in (8192, wl["kv"]):
+        x = synth.indexer_inputs([T], d, seed=wl["seed"])
+        keys = torch.from_numpy(x.keys).to(torch.bfloat16).to(dev)   # also the attention's c_kv
+        q = torch.from_numpy(x.q).to(dev)
+        offs = mla.Offsets(x.offsets.astype(np.int32), dev)
+        cap = (T + 3) // 4
+        pool = mla.IndexerPool(capacity=cap, batch_max=1, d=d, device=dev)
+        assert not pool.step(keys[:T - S], [0, T - S], S=T - S)
+        assert pool.step(keys, offs, S=S)
+        scores = torch.empty((1, cap), dtype=torch.float32, device=dev)
+        soffs = mla.selection_offsets(offs, budget, dev)
+        k = int(soffs.host[-1])
+        sel = torch.empty(k, dtype=torch.int32, device=dev)
+        # attention that follows: GLM-5.3-Flash-like heads over the same latent rows
+        H, L, n, v, rope = 64, S, 256, 256, 64
+        aw = synth.custom(512, n, v, rope, H, 1, L, kv=T, seed=wl["seed"] + 1)
+        q_nope = torch.from_numpy(synth.draw_like((1, L, H, n), 1.0, "bf16", 71)).to(torch.bfloat16).to(dev)
+        q_pe = torch.from_numpy(synth.draw_like((1, L, H, rope), 1.0, "bf16", 72)).to(torch.bfloat16).to(dev)
+        k_pe = torch.from_numpy(synth.draw_like((T, rope), 1.0, "bf16", 73)).to(torch.bfloat16).to(dev)
+        w_uk = torch.from_numpy(synth.draw_like((H, n, 512), 1 / math.sqrt(512), "bf16", 74)).to(torch.bfloat16).to(dev)
+        w_uv = torch.from_numpy(synth.draw_like((H, 512, v), 1 / math.sqrt(512), "bf16", 75)).to(torch.bfloat16).to(dev)
+        q_lat = torch.empty((1, L, H, 512), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((1, L, H, v), dtype=torch.float32, device=dev)
+
+        def pool_tail():
+            pool.trim([T - S])   # host only: the pool again covers T - S positions
+            assert pool.step(keys, offs, S=S)
+
+        def pool_full():
+            pool.state.valid = 0   # host only: no pool, so every window is pooled
+            assert not pool.step(keys, offs, S=S)
+
+        def score():
+            pool.scores(q, offs, out=scores)
+
+        def select():
+            mla.indexer_select(scores, offs, budget, sel_offsets=soffs, out=sel)
+
+        def attend():
+            mla.fold_query(q_nope, w_uk, out=q_lat)
+            mla.absorbed_attention_sparse(q_lat, q_pe, keys, k_pe, w_uv, offs, sel, soffs, scale=aw.scale, out=out)
+
+        arms = {"incremental": (pool_tail, score, select, attend), "full": (pool_full, score, select, attend)}
+        for parts in arms.values():
+            for f in parts:
+                f()
+        times = {a: [[] for _ in range(4)] for a in arms}
+        for i in range(args.samples):
+            for a in (("incremental", "full") if i % 2 == 0 else ("full", "incremental")):
+                scrub.fill_(i & 255)
+                torch.cuda._sleep(spin)
+                ev[0].record()
+                for j, f in enumerate(arms[a]):
+                    f()
+                    ev[j + 1].record()
+                torch.cuda.synchronize()
+                for j in range(4):
+                    times[a][j].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+        med = {a: [float(np.median(t)) for t in times[a]] for a in arms}
+        inc, full = med["incremental"], med["full"]
+        W = cap
+        print(json.dumps({
+            "indexer": wl["name"] if T == wl["kv"] else f"indexer_kv{T}_s{S}_d{d}_top{budget}", "kv": T, "S": S,
+            "d": d, "budget": budget, "windows": W,
+            "indexer_step_us": {"incremental": round(sum(inc[:3]), 2), "full": round(sum(full[:3]), 2)},
+            "pool_us": {"tail": round(inc[0], 2), "full": round(full[0], 2)},
+            "scores_us": round(inc[1], 2), "select_us": round(inc[2], 2),
+            "sparse_attention_us": round(inc[3], 2),
+            "layer_step_us": {"incremental": round(sum(inc), 2), "full": round(sum(full), 2)},
+            "scores_GBps": round(W * d * 4 / (inc[1] * 1e-6) / 1e9, 1),
+            "pool_full_GBps": round((T * d * 2 + W * d * 4) / (full[0] * 1e-6) / 1e9, 1),
+            "attention_geometry": "r 512, n 256, v 256, rope 64, 64 heads, L 8 (GLM-5.3-Flash-like)",
+            "samples": args.samples, "cache_state": "cold (512 MiB scrub before each sample)"}), flush=True)
+        del pool, keys, k_pe, scores, sel, q_lat, out
         torch.cuda.empty_cache()
 
 

@@ -149,7 +149,7 @@ def _given_scores(W, seed, decimals=1):
 
 
 def test_select_given_scores_is_exact():
-    lens = [1, 5, 6, 10, 2048, 2049, 2051, 700, 9000]
+    lens = [1, 5, 6, 10, 2048, 2049, 2051, 700, 9000, 20000]
     budgets = (1, 6, 7, 2048)
     cap = ix.n_windows(max(lens))
     sc = np.zeros((len(lens), cap), dtype=np.float32)
@@ -159,6 +159,7 @@ def test_select_given_scores_is_exact():
     sc[7, :] = 0.25                                   # all tied
     sc[8, 100:400] = np.float32(1e30)                 # a wide block of equal top scores
     sc[8, 500] = -np.float32(1e30)
+    sc[9, :] = 1.5                                    # all tied, more windows than the candidate list holds
     off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     scd = torch.from_numpy(sc).cuda()
     for budget in budgets:
