@@ -171,11 +171,15 @@ def test_select_given_scores_is_exact():
             assert np.array_equal(got[so[b]:so[b + 1]], ref), (budget, b, T)
 
 
-def test_select_large_given_scores_is_exact():
-    T, budget = 131072, 2048
+@pytest.mark.parametrize("T", [131072, 140001])
+def test_select_large_given_scores_is_exact(T):
+    # 131072: every window staged in LDS; 140001: 35001 windows, those past 32768 read from memory
+    budget = 2048
     W = ix.n_windows(T)
     for seed, dec in ((40, 2), (41, 6)):
         s = _given_scores(W, seed, dec)[None, :]
+        if T > 131072:
+            s[0, -200:] = np.float32(50.0)            # the best windows lie past the staged ones
         sel, _ = mla.indexer_select(torch.from_numpy(s).cuda(), [0, T], budget)
         assert np.array_equal(sel.cpu().numpy(), ix.select_positions(s[0], T, budget))
 
