@@ -51,7 +51,7 @@ HEADLINE = "dsv3_h128_kv8192_l8_bf16"
 # HBM traffic of the split kernel per launch, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
 # (KiB per dispatch) scaled by what the same counters read for a plain 256 MiB device copy
 # (FETCH x2.00, WRITE x1.00); valid only for the kernel source it was measured on.
-SPLIT_TRAFFIC = {"source_sha256": "a937c498336fe74a4877af67e3ae1e70d894dbe1fbb93f6a9f20cfd51b05262a",
+SPLIT_TRAFFIC = {"source_sha256": "326b24c97638b06ed9c898865d127ea9b114636232fadd55feb556bd422bf0a8",
                  "fetch_kib": 9373.6, "write_kib": 16512.0, "fetch_factor": 2.0, "write_factor": 1.0}
 KERNEL_SOURCES = ("mla_speculative_decode_amd/csrc/attn.hip", "mla_speculative_decode_amd/csrc/mla_device.h")
 

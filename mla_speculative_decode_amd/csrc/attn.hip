@@ -21,13 +21,18 @@
 //   scores  S^T[64 keys x 64 rows] as 2x2 blocks of 32x32; wave (wk, wr)
 //           computes keys 32wk.., rows 32wr.. with the query block held in
 //           registers (B operand) and keys streamed from LDS (A operand);
-//   softmax base-2 online softmax; each lane publishes the maximum of its
-//           16 scores of a row and every wave reads the 4 values of each row;
-//   PV      O[64 rows x DV]: wave w owns columns w*DV/4..; P (bf16) comes from
-//           LDS, V^T from an LDS copy transposed in registers on the way in.
-// LDS holds one key tile row-major (kt), one value tile transposed (vt), P,
-// and small exchange arrays; the next tile is prefetched into registers and
-// written to kt while PV runs, and to vt right after it.
+//   softmax base-2, against a fixed reference per row (the row's maximum
+//           over the first tile of the split that gives it finite scores);
+//           a split in which a later score exceeds its reference by more
+//           than 2^64 runs again with raised references, so O is never
+//           rescaled inside the tile loop;
+//   PV      O^T[DV x 64 rows]: wave w owns columns w*DV/4..; P (bf16) comes
+//           from LDS, V^T fragments are read transposed from the row-major
+//           tile with ds_read_b64_tr_b16.
+// LDS holds two tile buffers (tile t is computed while tile t+1 is copied in
+// by direct-to-LDS loads issued between the score MFMAs), P and small
+// exchange arrays.  Variants of the same template read an fp8 cache (codes
+// expanded to bf16 in LDS) or only selected cache positions.
 
 #include <algorithm>
 #include <type_traits>
@@ -65,9 +70,6 @@ struct AttnArgs {
   int rows_total;       // L*H
   float sl2;            // scale * log2(e)
 };
-
-__device__ __forceinline__ int kt_phys(int key, int ch) { return ch ^ ((key & 7) ^ ((key >> 3) & 7)); }
-__device__ __forceinline__ int row_phys(int row, int ch) { return ch ^ (row & 7); }
 
 // Headroom of the fixed softmax reference (log2 units): P = 2^(s - m) <= 2^64.
 constexpr float kRefSlack = 64.f;

@@ -1,7 +1,7 @@
 // mla_device.h -- device-side building blocks for the gfx950 (CDNA4) kernels
-// of libmla: vector types, MFMA wrappers, bfloat16 conversion, LDS swizzles,
-// an 8x8 bf16 register transpose, XCD-aware work mapping and the split-KV
-// plan decode shared by the attention and combine kernels.
+// of libmla: vector types, MFMA wrappers, bfloat16 conversion and packing, an
+// LDS-only workgroup barrier, XCD-aware work mapping and the split-KV plan
+// decode shared by the attention and merge kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -74,23 +74,6 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// 8x8 transpose of bf16 held as 8 rows of 16 bytes: in[r] holds elements
-// (r, 0..7); out[c] receives elements (0..7, c).  32 byte-permutes.
-__device__ __forceinline__ void transpose8x8_bf16(const u32x4 in[8], u32x4 out[8]) {
-  // out[c] dword q = (in[2q] element c, in[2q+1] element c); element c of a
-  // row sits in dword c/2, low half when c is even.
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t a = in[2 * q][c >> 1], b = in[2 * q + 1][c >> 1];
-      // v_perm_b32 selector: bytes of (b:a); pick the c-even/odd half of each.
-      out[c][q] = (c & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
-                          : __builtin_amdgcn_perm(b, a, 0x05040100u);
-    }
-  }
-}
-
 // ---- work mapping ----------------------------------------------------------
 // Workgroups are dispatched round-robin over the XCDs (block id b runs on XCD
 // b % 8).  Give each XCD a contiguous range of work items so that items that
@@ -149,15 +132,6 @@ __device__ __forceinline__ void seq_splits(int b, const int32_t* __restrict__ of
     for (int d = kWave / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d, kWave);
     acc += s;
   }
-  *g0 = acc;
-  *sb = (off[b + 1] - off[b] + chunk - 1) / chunk;
-}
-
-// Same as seq_splits, computed by one thread alone (no wave collectives), for
-// callers whose lanes belong to different sequences.
-__device__ __forceinline__ void seq_splits_lane(int b, const int32_t* __restrict__ off, int chunk, int* g0, int* sb) {
-  int acc = 0;
-  for (int bb = 0; bb < b; ++bb) acc += (off[bb + 1] - off[bb] + chunk - 1) / chunk;
   *g0 = acc;
   *sb = (off[b + 1] - off[b] + chunk - 1) / chunk;
 }
