@@ -92,8 +92,10 @@ def test_absorbed_fp8_matches_oracle_and_bf16_path(case):
     out8 = mla.absorbed_attention_fp8(ql, qp, c_dev, s_dev, wuv, offs, scale=x.scale)
     out16 = mla.absorbed_attention(ql, qp, dev(ch.astype(np.float32), "bf16"), dev(kh.astype(np.float32), "bf16"),
                                    wuv, offs, scale=x.scale)
+    again = mla.absorbed_attention_fp8(ql, qp, c_dev, s_dev, wuv, offs, scale=x.scale)
     torch.cuda.synchronize()
     assert torch.equal(out8, out16), "fp8 path differs from the bf16 path on the dequantised cache"
+    assert torch.equal(out8, again), "fp8 path is not deterministic"
     ref = oracle.latent_attention(q_lat, x.q_pe, ch, kh, x.w_uv, x.offsets, L, x.scale)
     check_close(host64(out8).reshape(-1, v), ref, "bf16", f"absorbed fp8 {name}")
 

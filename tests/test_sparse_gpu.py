@@ -71,6 +71,13 @@ def test_random_selections(case, budgets):
         sels.append(np.sort(s))
     x, q_lat, out, ref = _run(case, sels)
     check_close(host64(out).reshape(-1, v), ref, "bf16", f"sparse {name}")
+    # deterministic: a second call (fresh workspace) gives the same bits
+    sel, soff, sel_d = _sel_dev(sels)
+    again = mla.absorbed_attention_sparse(dev(q_lat, dt), dev(x.q_pe, dt) if rope else None, dev(x.c_kv, dt),
+                                          dev(x.k_pe, dt) if rope else None, dev(x.w_uv, dt),
+                                          x.offsets.astype(np.int32), sel_d, soff, scale=x.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
 
 
 def test_rows_that_see_nothing_output_zero():
