@@ -51,7 +51,7 @@ HEADLINE = "dsv3_h128_kv8192_l8_bf16"
 # HBM traffic of the split kernel per launch, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
 # (KiB per dispatch) scaled by what the same counters read for a plain 256 MiB device copy
 # (FETCH x2.00, WRITE x1.00); valid only for the kernel source it was measured on.
-SPLIT_TRAFFIC = {"source_sha256": "326b24c97638b06ed9c898865d127ea9b114636232fadd55feb556bd422bf0a8",
+SPLIT_TRAFFIC = {"source_sha256": "6108d7700fddea7e7762fcc7e8937d3c5a43beb1f3e56433f3cfbcce49b01c0b",
                  "fetch_kib": 9373.6, "write_kib": 16512.0, "fetch_factor": 2.0, "write_factor": 1.0}
 KERNEL_SOURCES = ("mla_speculative_decode_amd/csrc/attn.hip", "mla_speculative_decode_amd/csrc/mla_device.h")
 
@@ -358,6 +358,14 @@ def sparse_sweep(args):
             "dense": lambda: mla.absorbed_attention(q_lat, d["q_pe"], d["c_kv"], d["k_pe"], d["w_uv"], offs,
                                                     scale=x.scale, out=out),
         }
+        if args.cache == "fp8":   # the same two calls over the fp8 form of the cache
+            codes, scales = mla.quantize_latent_fp8(d["c_kv"], d["k_pe"])
+            arms = {
+                "sparse": lambda: mla.absorbed_attention_sparse_fp8(q_lat, d["q_pe"], codes, scales, d["w_uv"], offs,
+                                                                    sel_d, soffs, scale=x.scale, out=out),
+                "dense": lambda: mla.absorbed_attention_fp8(q_lat, d["q_pe"], codes, scales, d["w_uv"], offs,
+                                                            scale=x.scale, out=out),
+            }
         for f in arms.values():
             f()
         times = {a: [] for a in arms}
@@ -370,7 +378,7 @@ def sparse_sweep(args):
                 e1.record()
                 torch.cuda.synchronize()
                 times[a].append(e0.elapsed_time(e1) * 1e3)
-        print(json.dumps({"sparse_attention": w.name, "kv": kv, "budget": k,
+        print(json.dumps({"sparse_attention": w.name, "kv": kv, "budget": k, "cache": args.cache,
                           "sparse_us": round(float(np.median(times["sparse"])), 2),
                           "dense_us": round(float(np.median(times["dense"])), 2),
                           "samples": args.samples, "cache_state": "cold (512 MiB scrub before each sample)"}),

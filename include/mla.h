@@ -293,6 +293,21 @@ int mla_absorbed_attention_sparse(const mla_geom* g, int32_t B, int32_t L, const
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_absorbed_attention_sparse_fp8 -- mla_absorbed_attention_sparse over the
+ * fp8 form of the latent cache (codes and scales of mla_quantize_latent_fp8
+ * instead of c_kv and k_pe): the attention over the selected positions of the
+ * dequantised cache, and bit-identical to mla_absorbed_attention_sparse given
+ * that dequantised cache in bf16.  Workspace: mla_absorbed_sparse_workspace_size.
+ * Errors as mla_absorbed_attention_sparse (MLA_E_NULL also for codes or scales).
+ */
+int mla_absorbed_attention_sparse_fp8(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                                      const void* codes, const float* scales, const int32_t* kv_offsets_host,
+                                      const int32_t* kv_offsets_dev, const int32_t* sel,
+                                      const int32_t* sel_offsets_host, const int32_t* sel_offsets_dev,
+                                      const void* w_uv, float scale, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
  * Pooled top-k indexer ("One guard, 110x off the verify step", sections "The
  * sparse model is different" and "The same bug, one layer over").  The indexer
  * pools the cached keys of each sequence into windows of four positions

@@ -431,6 +431,40 @@ def indexer_select(scores, kv_offsets, budget: int, sel_offsets: Offsets | None 
     return out, sel_offsets
 
 
+def absorbed_attention_sparse_fp8(q_lat, q_pe, codes, scales, w_uv, kv_offsets, sel, sel_offsets, scale=None,
+                                  out=None, workspace=None, stream=None, n=None):
+    """absorbed_attention_sparse over the fp8 cache (codes, scales from quantize_latent_fp8)."""
+    torch = _torch()
+    lib = _lib.load()
+    B, L, H, r = q_lat.shape
+    rope = q_pe.shape[-1] if q_pe is not None else 0
+    v = w_uv.shape[-1]
+    offs = _as_offsets(kv_offsets, q_lat.device)
+    soffs = _as_offsets(sel_offsets, q_lat.device)
+    if offs.B != B or soffs.B != B:
+        raise ValueError("offsets do not match the batch")
+    if sel.dtype != torch.int32 or codes.dtype != torch.uint8 or scales.dtype != torch.float32:
+        raise TypeError("sel must be int32, codes uint8, scales float32")
+    if scale is None:
+        if n is None:
+            raise ValueError("give scale, or n to default it to 1/sqrt(n + rope)")
+        scale = 1.0 / math.sqrt(n + rope)
+    g = Geom(r, int(n) if n is not None else 0, v, rope, H)
+    sz = ctypes.c_size_t()
+    _lib.check("mla_absorbed_sparse_workspace_size", lib.mla_absorbed_sparse_workspace_size(
+        ctypes.byref(g), B, L, offs.host_ptr(), soffs.host_ptr(), ctypes.byref(sz)))
+    if workspace is None:
+        workspace = torch.empty(max(int(sz.value), 256), dtype=torch.uint8, device=q_lat.device)
+    if out is None:
+        out = torch.empty((B, L, H, v), dtype=torch.float32, device=q_lat.device)
+    _lib.check("mla_absorbed_attention_sparse_fp8", lib.mla_absorbed_attention_sparse_fp8(
+        ctypes.byref(g), B, L, _ptr(_dev(q_lat, "q_lat")), _ptr(q_pe) if rope else None, _ptr(_dev(codes, "codes")),
+        _ptr(_dev(scales, "scales")), offs.host_ptr(), offs.dev_ptr(), _ptr(_dev(sel, "sel")), soffs.host_ptr(),
+        soffs.dev_ptr(), _ptr(_dev(w_uv, "w_uv")), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def absorbed(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, kv_offsets, scale=None, stream=None, q_lat=None,
              out=None, workspace=None):
     """Whole absorbed path: fold_query then absorbed_attention."""

@@ -355,11 +355,13 @@ int mla_absorbed_sparse_workspace_size(const mla_geom* g, int32_t B, int32_t L, 
   return MLA_OK;
 }
 
-int mla_absorbed_attention_sparse(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
-                                  const void* c_kv, const void* k_pe, const int32_t* kv_offsets_host,
-                                  const int32_t* kv_offsets_dev, const int32_t* sel, const int32_t* sel_offsets_host,
-                                  const int32_t* sel_offsets_dev, const void* w_uv, float scale, float* out,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// Validation and planning shared by the selected-position calls (bf16 cache:
+// c_kv / k_pe; fp8 cache: codes / scales, passed as c_kv / k_pe = codes).
+int sparse_prepare(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe, const void* c_kv,
+                   const void* k_pe, const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, const int32_t* sel,
+                   const int32_t* sel_offsets_host, const int32_t* sel_offsets_dev, const void* w_uv, float scale,
+                   const float* out, void* workspace, size_t workspace_bytes, AbsorbedLaunch* q) {
   int st = check_geom(g);
   if (st) return st;
   if ((st = check_offsets(B, L, kv_offsets_host))) return st;
@@ -371,17 +373,47 @@ int mla_absorbed_attention_sparse(const mla_geom* g, int32_t B, int32_t L, const
   SplitPlan p{};
   if ((st = make_plan(B, L, g->heads, sel_offsets_host, L * g->heads, 1, g->r, 2, true, &p))) return st;
   if (!workspace || workspace_bytes < p.ws_bytes) return MLA_E_WORKSPACE;
+  q->r = g->r; q->rope = g->rope; q->v_dim = g->v; q->H = g->heads; q->B = B; q->L = L;
+  q->q_lat = q_lat; q->q_pe = q_pe; q->c_kv = c_kv; q->k_pe = k_pe; q->w_uv = w_uv;
+  q->off_dev = sel_offsets_dev; q->scale = scale;   // splits and merge run over the selections
+  q->off0 = sel_offsets_host[0]; q->kv1 = sel_offsets_host[1] - sel_offsets_host[0];
+  q->ws_o = workspace;
+  q->ws_ml = (float*)((char*)workspace + align_up(p.ws_o_bytes));
+  q->plan = p;
+  return MLA_OK;
+}
+}  // namespace
+
+int mla_absorbed_attention_sparse(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                                  const void* c_kv, const void* k_pe, const int32_t* kv_offsets_host,
+                                  const int32_t* kv_offsets_dev, const int32_t* sel, const int32_t* sel_offsets_host,
+                                  const int32_t* sel_offsets_dev, const void* w_uv, float scale, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   AbsorbedLaunch q{};
-  q.r = g->r; q.rope = g->rope; q.v_dim = g->v; q.H = g->heads; q.B = B; q.L = L;
-  q.q_lat = q_lat; q.q_pe = q_pe; q.c_kv = c_kv; q.k_pe = k_pe; q.w_uv = w_uv;
-  q.off_dev = sel_offsets_dev; q.scale = scale;   // splits and merge run over the selections
-  q.off0 = sel_offsets_host[0]; q.kv1 = sel_offsets_host[1] - sel_offsets_host[0];
-  q.ws_o = workspace;
-  q.ws_ml = (float*)((char*)workspace + align_up(p.ws_o_bytes));
-  q.plan = p;
+  int st = sparse_prepare(g, B, L, q_lat, q_pe, c_kv, k_pe, kv_offsets_host, kv_offsets_dev, sel, sel_offsets_host,
+                          sel_offsets_dev, w_uv, scale, out, workspace, workspace_bytes, &q);
+  if (st) return st;
   hipStream_t s = (hipStream_t)stream;
   if ((st = hip_status(absorbed_attn_sparse(q, sel, kv_offsets_dev, kv_offsets_host[0],
                                             kv_offsets_host[1] - kv_offsets_host[0], s))))
+    return st;
+  return hip_status(combine_upproj(q, kBF16, out, s));
+}
+
+int mla_absorbed_attention_sparse_fp8(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,
+                                      const void* codes, const float* scales, const int32_t* kv_offsets_host,
+                                      const int32_t* kv_offsets_dev, const int32_t* sel,
+                                      const int32_t* sel_offsets_host, const int32_t* sel_offsets_dev,
+                                      const void* w_uv, float scale, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (!codes || !scales) return MLA_E_NULL;
+  AbsorbedLaunch q{};
+  int st = sparse_prepare(g, B, L, q_lat, q_pe, codes, codes, kv_offsets_host, kv_offsets_dev, sel, sel_offsets_host,
+                          sel_offsets_dev, w_uv, scale, out, workspace, workspace_bytes, &q);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = hip_status(absorbed_attn_sparse_fp8(q, codes, scales, sel, kv_offsets_dev, kv_offsets_host[0],
+                                                kv_offsets_host[1] - kv_offsets_host[0], s))))
     return st;
   return hip_status(combine_upproj(q, kBF16, out, s));
 }

@@ -252,12 +252,13 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   constexpr int F8C = F8 ? (DA + DR) / 16 : 4;           // 16-code chunks per position
   constexpr int F8X = (F8C + 3) / 4;                      // chunks per thread
   static_assert(!F8 || (VK && (DA + DR) % 64 == 0 && BN * 4 == 256), "fp8 rows: four threads per position");
-  static_assert(!SEL || (VK && !F8), "selection only on the absorbed bf16 route");
+  static_assert(!SEL || VK, "selection only on the absorbed route");
   u32x4 f8r[F8 ? F8X : 1];
   float f8s = 0.f;
   auto issue_f8 = [&](int t0, int x) {
     const int key = tid >> 2, j = (tid & 3) + 4 * x;
-    const long long kr = p0 + min(t0 + key, k1 - 1);
+    // SEL: the cache position of key `key` sits in lane `key` of sidx
+    const long long kr = p0 + (SEL ? (long long)__shfl(sidx, key, kWave) : (long long)min(t0 + key, k1 - 1));
     f8r[x] = ld16(p.c8 + kr * (DA + DR) + 16 * j);
     if (x == 0) f8s = p.c8s[kr];
   };
@@ -1130,6 +1131,26 @@ hipError_t absorbed_attn_sparse(const AbsorbedLaunch& q, const int32_t* sel, con
   switch (q.rope) {
     case 0:  hipLaunchKernelGGL((attn_bf16_kernel<512, 0, 512, true, false, true>), grid, dim3(256), 0, st, a); break;
     case 64: hipLaunchKernelGGL((attn_bf16_kernel<512, 64, 512, true, false, true>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t absorbed_attn_sparse_fp8(const AbsorbedLaunch& q, const void* codes, const float* scales,
+                                    const int32_t* sel, const int32_t* koff_dev, int koff0, int kvt1, hipStream_t st) {
+  AttnArgs a{};
+  a.qa = (const uint16_t*)q.q_lat; a.qb = (const uint16_t*)q.q_pe;
+  a.c8 = (const uint8_t*)codes; a.c8s = scales;
+  a.sel = sel; a.koff = koff_dev; a.koff0 = koff0; a.kvt1 = kvt1;
+  a.off = q.off_dev; a.off0 = q.off0; a.kv1 = q.kv1; a.ws_o = q.ws_o; a.ws_ml = q.ws_ml;
+  a.B = q.B; a.L = q.L; a.H = q.H; a.hpr = q.H; a.rows_slot = q.L * q.H; a.head_slots = 1;
+  a.row_tiles = q.plan.row_tiles; a.chunk = q.plan.chunk; a.n_items = q.plan.n_items;
+  a.rows_total = q.L * q.H; a.sl2 = q.scale * 1.4426950408889634f;
+  if (q.r != 512) return hipErrorInvalidValue;
+  const dim3 grid(grid_xcd(a.n_items));
+  switch (q.rope) {
+    case 0:  hipLaunchKernelGGL((attn_bf16_kernel<512, 0, 512, true, true, true>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((attn_bf16_kernel<512, 64, 512, true, true, true>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

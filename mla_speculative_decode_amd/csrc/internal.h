@@ -47,6 +47,8 @@ hipError_t absorbed_attn_bf16(const AbsorbedLaunch& q, hipStream_t st);
 hipError_t absorbed_attn_fp8(const AbsorbedLaunch& q, const void* codes, const float* scales, hipStream_t st);
 hipError_t absorbed_attn_sparse(const AbsorbedLaunch& q, const int32_t* sel, const int32_t* koff_dev, int koff0,
                                 int kvt1, hipStream_t st);
+hipError_t absorbed_attn_sparse_fp8(const AbsorbedLaunch& q, const void* codes, const float* scales,
+                                    const int32_t* sel, const int32_t* koff_dev, int koff0, int kvt1, hipStream_t st);
 hipError_t materialized_attn_bf16(const MaterializedLaunch& q, hipStream_t st);
 bool materialized_bf16_supported(int n, int rope, int v);
 hipError_t attn_f32(const AbsorbedLaunch* qa, const MaterializedLaunch* qm, hipStream_t st);

@@ -114,3 +114,36 @@ def test_absorbed_fp8_full_size_sampled():
     sel = sample_rows(w.batch, x.L, w.heads, 256, seed=11)
     ref = oracle.absorbed(x.q_nope, x.q_pe, ch, kh, x.w_uk, x.w_uv, x.offsets, x.L, x.scale, sel=sel)
     check_close(host64(out).reshape(-1, w.v)[sel], ref, "bf16", "absorbed fp8 full size")
+
+
+@pytest.mark.parametrize("case,budgets", [
+    (("dsv3_sel8", 512, 128, 128, 64, 8, 8, [3000, 700], "bf16"), (512, 300)),
+    (("norope_sel8", 512, 128, 128, 0, 8, 4, [1000, 90, 400], "bf16"), (100, 90, 257)),
+])
+def test_sparse_fp8_matches_oracle_and_sparse_bf16_path(case, budgets):
+    """Selected positions over the fp8 cache: bit-identical to the bf16 selected-position
+    path over the dequantised cache, and within the bf16 bar of the oracle's attention over
+    the selected positions of the dequantised cache."""
+    from oracle import sparse
+    name, r, n, v, rope, H, L, lens, dt = case
+    x, codes, scales, ch, kh = _fp8_inputs(case)
+    rng = np.random.default_rng(len(name) + 7)
+    sels = [np.sort(np.concatenate([rng.choice(k - 4, size=m - 4, replace=False), np.arange(k - 4, k)]))
+            for k, m in zip(lens, budgets)]
+    sel = np.concatenate(sels).astype(np.int32)
+    soff = np.concatenate([[0], np.cumsum([s.size for s in sels])]).astype(np.int32)
+    sel_d = torch.from_numpy(sel).cuda()
+    q_lat = synth.draw_like((len(lens), L, H, r), math.sqrt(n / r), dt, seed=78)
+    offs = x.offsets.astype(np.int32)
+    c_dev, s_dev = mla.quantize_latent_fp8(dev(x.c_kv, "bf16"), dev(x.k_pe, "bf16") if rope else None)
+    ql, qp, wuv = dev(q_lat, "bf16"), dev(x.q_pe, "bf16") if rope else None, dev(x.w_uv, "bf16")
+    out8 = mla.absorbed_attention_sparse_fp8(ql, qp, c_dev, s_dev, wuv, offs, sel_d, soff, scale=x.scale)
+    out16 = mla.absorbed_attention_sparse(ql, qp, dev(ch.astype(np.float32), "bf16"),
+                                          dev(kh.astype(np.float32), "bf16") if rope else None, wuv, offs, sel_d,
+                                          soff, scale=x.scale)
+    again = mla.absorbed_attention_sparse_fp8(ql, qp, c_dev, s_dev, wuv, offs, sel_d, soff, scale=x.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out8, out16), "fp8 selected-position path differs from the bf16 one on the dequantised cache"
+    assert torch.equal(out8, again)
+    ref = sparse.sparse_latent_attention(q_lat, x.q_pe, ch, kh, x.w_uv, x.offsets, sel, soff, L, x.scale)
+    check_close(host64(out8).reshape(-1, v), ref, "bf16", f"sparse fp8 {name}")
