@@ -147,6 +147,17 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.mla_materialized_attention(*margs(FAKE, 1 << 40, v=None)) == -1
     assert lib.mla_materialized_attention(*margs(FAKE, 1 << 40, L=600)) == -2
     assert lib.mla_materialized_attention(*margs(FAKE, 0)) == -4
+    # selected positions over the bf16 and the fp8 cache: the same checks before any launch
+    sel_ok, sel_empty, sel_long = _offs([0, 50]), _offs([0, 0]), _offs([0, 513])
+    sargs = lambda soffh, ws, wsb, **kw: [ctypes.byref(g), 1, 4, FAKE, FAKE, kw.get("c", FAKE), FAKE, off, FAKE,
+                                          kw.get("sel", FAKE), soffh, FAKE, FAKE, f, FAKE, ws, wsb, None]
+    for fn in (lib.mla_absorbed_attention_sparse, lib.mla_absorbed_attention_sparse_fp8):
+        assert fn(*sargs(sel_empty, FAKE, 1 << 40)) == -2      # a sequence with nothing selected
+        assert fn(*sargs(sel_long, FAKE, 1 << 40)) == -2       # more selected than cached
+        assert fn(*sargs(sel_ok, FAKE, 1 << 40, sel=None)) == -1
+        assert fn(*sargs(sel_ok, FAKE, 1 << 40, c=None)) == -1
+        assert fn(*sargs(sel_ok, None, 1 << 40)) == -4
+        assert fn(*sargs(sel_ok, FAKE, 16)) == -4
 
 
 def test_binding_refuses_cpu_tensors():
