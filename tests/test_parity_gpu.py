@@ -41,6 +41,10 @@ CASES = [
     ("bf16_many_splits", 512, 128, 128, 64, 2, 3, [5000], "bf16"),
     # L = 20: two merge row tiles of 16, the second ragged
     ("bf16_L20", 512, 128, 128, 64, 4, 20, [100, 333], "bf16"),
+    # 130 ragged sequences: the split decode and the merge walk the offsets in three
+    # chunks of 64 sequences (caches of 256..454 positions, so every row averages many
+    # keys as in the benchmark workload; short caches have their own cases above)
+    ("bf16_batch130", 512, 128, 128, 64, 2, 2, [256 + (37 * i) % 199 for i in range(130)], "bf16"),
 ]
 
 
@@ -102,14 +106,28 @@ def test_absorbed_attention_given_q_lat(case):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_absorbed_chain(case):
+    # The absorbed route stores the folded query q_lat in the input dtype (bf16): its
+    # rounding moves the logits, and rows led by a few keys carry that into outputs
+    # several times the batch rms.  As for the materialised chain, the bf16 chain is
+    # held to 2e-2 * rms against the oracle that stores its own q_lat in bf16, and to
+    # 4e-2 * rms against the exact one.
     x = _inputs(case)
     dt = case[-1]
+    name, r, n, v, rope, H, L, lens, _ = case
     d = _dev_all(x, dt)
     out = mla.absorbed(d["q_nope"], d["q_pe"], d["c_kv"], d["k_pe"], d["w_uk"], d["w_uv"],
                        x.offsets.astype(np.int32), scale=x.scale)
     torch.cuda.synchronize()
     ref = oracle.absorbed(x.q_nope, x.q_pe, x.c_kv, x.k_pe, x.w_uk, x.w_uv, x.offsets, x.L, x.scale)
-    check_close(host64(out).reshape(ref.shape), ref, dt, f"absorbed {case[0]}")
+    got = host64(out).reshape(ref.shape)
+    if dt == "f32":
+        check_close(got, ref, dt, f"absorbed {name}")
+        return
+    check_close(got, ref, dt, f"absorbed {name} vs exact", rel=4e-2)
+    q_lat = oracle.fold(x.q_nope.reshape(-1, H, n), x.w_uk).reshape(len(lens), L, H, r)
+    q_lat_q = synth.round_bf16(q_lat.astype(np.float32)).astype(np.float64)
+    ref_q = oracle.latent_attention(q_lat_q, x.q_pe, x.c_kv, x.k_pe, x.w_uv, x.offsets, L, x.scale)
+    check_close(got, ref_q, dt, f"absorbed {name} vs bf16-stored q_lat")
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
