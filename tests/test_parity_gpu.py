@@ -41,10 +41,9 @@ CASES = [
     ("bf16_many_splits", 512, 128, 128, 64, 2, 3, [5000], "bf16"),
     # L = 20: two merge row tiles of 16, the second ragged
     ("bf16_L20", 512, 128, 128, 64, 4, 20, [100, 333], "bf16"),
-    # 130 ragged sequences: the split decode and the merge walk the offsets in three
-    # chunks of 64 sequences (caches of 256..454 positions, so every row averages many
-    # keys as in the benchmark workload; short caches have their own cases above)
-    ("bf16_batch130", 512, 128, 128, 64, 2, 2, [256 + (37 * i) % 199 for i in range(130)], "bf16"),
+    # 130 ragged sequences of 2..200 positions: the split decode and the merge walk the
+    # offsets in three chunks of 64 sequences
+    ("bf16_batch130", 512, 128, 128, 64, 2, 2, [2 + (37 * i) % 199 for i in range(130)], "bf16"),
 ]
 
 
