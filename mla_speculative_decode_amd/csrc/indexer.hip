@@ -133,6 +133,7 @@ constexpr int kBuckets = 2048;
 constexpr int kHistCopies = 4;      // radix histograms (waves share them round robin)
 constexpr int kStage = 32768;       // window scores staged in LDS (128 KB)
 constexpr int kCand = 1024;         // boundary-bucket windows kept in an LDS list
+constexpr int kOutStage = kBuckets + 2 * kCand;   // selected positions gathered in LDS, then stored in order
 
 // Exclusive scan over the block of a 64-bit value per thread (two 32-bit
 // counters in the halves, neither of which can overflow); returns the block
@@ -165,14 +166,14 @@ __device__ __forceinline__ uint64_t block_exscan_u64(uint64_t v, uint64_t* sh, u
 // the windows of exactly that key.  for_each(f) calls f(key, weight) for every
 // candidate this thread owns.  Uses hist[kHistCopies][256] and pick[2].
 template <typename ForEach>
-__device__ uint32_t radix_select(ForEach for_each, uint32_t* need, uint32_t (*hist)[256], uint32_t* pick) {
+__device__ __forceinline__ uint32_t radix_select(ForEach for_each, uint32_t* need, uint32_t (*hist)[256], uint32_t* pick) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint32_t prefix = 0u, mask = 0u;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     for (int k = tid; k < kHistCopies * 256; k += kSelThreads) (&hist[0][0])[k] = 0u;
     __syncthreads();
-    for_each([&](uint32_t u, uint32_t wgt) {
+    for_each([&](uint32_t u, uint32_t wgt) __attribute__((always_inline)) {
       if ((u & mask) == prefix) atomicAdd(&hist[wv % kHistCopies][(u >> shift) & 255u], wgt);
     });
     __syncthreads();
@@ -212,15 +213,66 @@ __device__ uint32_t radix_select(ForEach for_each, uint32_t* need, uint32_t (*hi
   return prefix;
 }
 
+// The same select run by one wave over a short list in LDS (cand[c] = (order key,
+// weight), c < nc): no block barriers; the wave's LDS accesses complete in order.
+__device__ __forceinline__ uint32_t wave_radix_list(const uint32_t (*cand)[2], uint32_t nc, uint32_t* need,
+                                                    uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0u, mask = 0u;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (int k = lane; k < 256; k += kWave) hist[k] = 0u;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (uint32_t c = lane; c < nc; c += kWave) {
+      const uint32_t u = cand[c][0];
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], cand[c][1]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint32_t t[4], sum = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t[e] = hist[4 * lane + e];
+      sum += t[e];
+    }
+    uint32_t incl = sum;   // inclusive suffix sum over lanes >= l
+#pragma unroll
+    for (int dd = 1; dd < kWave; dd <<= 1) {
+      const uint32_t x = __shfl_down(incl, dd, kWave);
+      if (lane + dd < kWave) incl += x;
+    }
+    uint32_t above = incl - sum, dsel = 0u, asel = 0u;
+    bool hit = false;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      if (above < *need && *need <= above + t[e]) {
+        hit = true;
+        dsel = (uint32_t)(4 * lane + e);
+        asel = above;
+      }
+      above += t[e];
+    }
+    const int src = max(__ffsll((long long)__ballot(hit)) - 1, 0);   // exactly one lane hits
+    const uint32_t D = __builtin_amdgcn_readlane(dsel, src);
+    *need -= __builtin_amdgcn_readlane(asel, src);
+    prefix |= D << shift;
+    mask |= 255u << shift;
+  }
+  return prefix;
+}
+
 // grid B, 1024 threads: one block per sequence.
 __global__ __launch_bounds__(kSelThreads) void select_positions_kernel(const float* __restrict__ scores, int cap,
                                                                        const int32_t* __restrict__ off, int budget,
                                                                        const int32_t* __restrict__ sel_off,
                                                                        int32_t* __restrict__ sel) {
   __shared__ uint32_t hist[kHistCopies][256];
-  __shared__ uint32_t bhist[kBuckets];
-  __shared__ float sk[kStage + kStage / 32];   // the first kStage window scores (a pad word every 32)
-  __shared__ uint32_t cand[kCand][2];   // (order key, weight) of the windows in the boundary bucket
+  // bucket histogram, then the candidate list (order key, weight) of the windows in
+  // the boundary bucket; at the end the first kOutStage selected positions
+  __shared__ uint32_t aux[kBuckets + 2 * kCand];
+  uint32_t* const bhist = aux;
+  uint32_t (*const cand)[2] = reinterpret_cast<uint32_t (*)[2]>(aux + kBuckets);
+  __shared__ float sk[kStage + kStage / 32];   // window scores, one pad word after each thread's chunk
   __shared__ uint64_t scan_sh[kSelWaves];
   __shared__ float mm[2][kSelWaves];
   __shared__ uint32_t pick[2], ncand;
@@ -240,10 +292,14 @@ __global__ __launch_bounds__(kSelThreads) void select_positions_kernel(const flo
   const float* sc = scores + (long long)b * cap;
   auto weight = [&](int w) -> uint32_t { return (uint32_t)min(kWin, Kv - kWin * w); };
   // thread t owns windows [t C, t C + C): consecutive in index order, so one
-  // block scan orders them; the pad word makes the chunk reads conflict-free
+  // block scan orders them.  Staged, window t C + e sits at t (C + 1) + e: one pad
+  // word per chunk keeps the chunk reads of a wave on distinct banks for even C,
+  // and the reads of a chunk are one base address plus constant offsets.
+  // w / C = (w ceil(2^31 / C)) >> 31 exactly for w < 2^15 and 1 <= C <= 32.
   const int C = (W + kSelThreads - 1) / kSelThreads;
   const int wbeg = min(W, tid * C), wend = min(W, wbeg + C);
-  auto slot = [](int w) { return w + (w >> 5); };
+  const uint32_t cmul = (0x80000000u + (unsigned)C - 1u) / (unsigned)C;   // fits: C >= 1
+  auto slot = [cmul](int w) { return w + (int)(((uint64_t)(unsigned)w * cmul) >> 31); };
 
   // ---- scores -> LDS (every load in flight at once) and their min / max ----
   float lo = INFINITY, hi = -INFINITY;
@@ -271,7 +327,31 @@ __global__ __launch_bounds__(kSelThreads) void select_positions_kernel(const flo
       hi = fmaxf(hi, x);
     }
   }
-  auto val = [&](int w) -> float { return w < kStage ? sk[slot(w)] : sc[w]; };
+  // (the staged scores are read only after the barrier that publishes the min / max)
+  // for_chunk(f) calls f(w, score of w) for this thread's windows in window order;
+  // when every window is staged (the score array fits LDS), the LDS reads go in
+  // batches of 8 independent loads; otherwise the scores come from memory.  (One
+  // load whose address space depends on w would go through a generic pointer.)
+  constexpr int PER = kStage / kSelThreads;
+  constexpr int BATCH = 8;
+  const bool staged = C <= PER;
+  const int cbase = tid * (C + 1);   // LDS index of this thread's first window
+  auto for_chunk = [&](auto f) __attribute__((always_inline)) {
+    if (staged) {
+#pragma unroll 1
+      for (int e0 = 0; e0 < PER; e0 += BATCH) {   // rolled: the kernel's code stays small
+        if (wbeg + e0 >= wend) break;
+        float t[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) t[j] = sk[cbase + e0 + j];   // in bounds: tid (C + 1) + 31 < kStage + kStage / 32
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j)
+          if (wbeg + e0 + j < wend) f(wbeg + e0 + j, t[j]);
+      }
+    } else {   // more windows than LDS holds: read the scores from memory
+      for (int w = wbeg; w < wend; ++w) f(w, sc[w]);
+    }
+  };
 #pragma unroll
   for (int dd = 32; dd >= 1; dd >>= 1) {
     lo = fminf(lo, __shfl_xor(lo, dd, kWave));
@@ -297,7 +377,7 @@ __global__ __launch_bounds__(kSelThreads) void select_positions_kernel(const flo
   float scale = (span > 0.f && span < INFINITY) ? (float)kBuckets / span : 0.f;
   if (!(scale <= 3e38f)) scale = 0.f;   // a span too small to divide: one bucket
   auto bucket = [&](float x) -> int { return scale > 0.f ? min((int)((x - lo) * scale), kBuckets - 1) : 0; };
-  for (int w = wbeg; w < wend; ++w) atomicAdd(&bhist[bucket(val(w))], weight(w));
+  for_chunk([&](int w, float x) __attribute__((always_inline)) { atomicAdd(&bhist[bucket(x)], weight(w)); });
   __syncthreads();
   uint32_t need = (uint32_t)budget;
   {
@@ -322,57 +402,94 @@ __global__ __launch_bounds__(kSelThreads) void select_positions_kernel(const flo
 
   // ---- the windows of that bucket: a short list in LDS, unless there are too
   // many (then the select runs over every window, filtered by bucket)
-  for (int w = wbeg; w < wend; ++w) {
-    const float x = val(w);
-    if (bucket(x) == DB) {
+  // tm: bit e marks window wbeg + e of a staged chunk when its bucket is DB or
+  // above.  Bucket is monotone in the score, so every window the selection takes
+  // is marked, and the count and the placement visit only the marked ones.
+  uint32_t tm = 0u;
+  for_chunk([&](int w, float x) __attribute__((always_inline)) {
+    const int bk = bucket(x);
+    if (bk == DB) {
       const uint32_t c = atomicAdd(&ncand, 1u);
       if (c < kCand) {
         cand[c][0] = order_key(x);
         cand[c][1] = weight(w);
       }
     }
-  }
+    tm |= (bk >= DB ? 1u : 0u) << ((w - wbeg) & 31);   // used only when staged (C <= 32)
+  });
   __syncthreads();
   const uint32_t nc = ncand;
   uint32_t ukey;
   if (nc <= kCand) {
-    ukey = radix_select([&](auto f) {
-      for (uint32_t c = tid; c < nc; c += kSelThreads) f(cand[c][0], cand[c][1]);
-    }, &need, hist, pick);
-  } else {
-    ukey = radix_select([&](auto f) {
-      for (int w = wbeg; w < wend; ++w) {
-        const float x = val(w);
-        if (bucket(x) == DB) f(order_key(x), weight(w));
+    if (wv == 0) {
+      const uint32_t k = wave_radix_list(cand, nc, &need, &hist[0][0]);
+      if (lane == 0) {
+        pick[0] = k;
+        pick[1] = need;
       }
+    }
+    __syncthreads();
+    ukey = pick[0];
+    need = pick[1];
+  } else {
+    ukey = radix_select([&](auto f) __attribute__((always_inline)) {
+      for_chunk([&](int w, float x) __attribute__((always_inline)) {
+        if (bucket(x) == DB) f(order_key(x), weight(w));
+      });
     }, &need, hist, pick);
   }
   // ukey = key of the last window taken; `need` positions come from the
   // windows of exactly that key, in window order.
 
   // ---- placement: this thread's windows, after every earlier thread's ----------
+  // for_taken(f): f(w, score) for the windows that can be taken, in window order
+  // (the rest add nothing to either count)
+  auto for_taken = [&](auto f) __attribute__((always_inline)) {
+    if (staged) {
+      for (uint32_t m = tm; m != 0u; m &= m - 1u) {
+        const int e = __builtin_ctz(m);
+        f(wbeg + e, sk[cbase + e]);
+      }
+    } else {
+      for_chunk(f);
+    }
+  };
   uint32_t sg = 0u, se = 0u;
-  for (int w = wbeg; w < wend; ++w) {
-    const uint32_t u = order_key(val(w));
-    if (u > ukey) sg += weight(w);
-    else if (u == ukey) se += weight(w);
-  }
+  for_taken([&](int w, float x) __attribute__((always_inline)) {
+    const uint32_t u = order_key(x), c = weight(w);
+    sg += u > ukey ? c : 0u;   // branch-free: the two counters stay in registers
+    se += u == ukey ? c : 0u;
+  });
   uint64_t tot;
   const uint64_t ex = block_exscan_u64(((uint64_t)se << 32) | sg, scan_sh, &tot);
   uint32_t gb = (uint32_t)ex, eb = (uint32_t)(ex >> 32);
   if (sg + se > 0u) {
-    for (int w = wbeg; w < wend; ++w) {
-      const uint32_t u = order_key(val(w));
+    for_taken([&](int w, float x) __attribute__((always_inline)) {
+      const uint32_t u = order_key(x);
       const uint32_t c = weight(w);
       // positions taken before window w: all of the higher windows, and the
       // tied windows in order until `need` is met
       const uint32_t pos = gb + min(eb, need);
       const uint32_t n = u > ukey ? c : (u == ukey ? min(c, need - min(eb, need)) : 0u);
-      for (uint32_t j = 0; j < n && pos + j < (uint32_t)budget; ++j) out[pos + j] = kWin * w + (int)j;
-      if (u > ukey) gb += c;
-      else if (u == ukey) eb += c;
-    }
+      if (n > 0u) {   // skipped by the whole wave when none of its lanes takes this window
+#pragma unroll
+        for (uint32_t j = 0; j < (uint32_t)kWin; ++j) {
+          const uint32_t p = pos + j;
+          if (j < n && p < (uint32_t)budget) {
+            if (p < (uint32_t)kOutStage)
+              aux[p] = (uint32_t)(kWin * w) + j;   // written out in order below
+            else
+              out[p] = kWin * w + (int)j;
+          }
+        }
+      }
+      gb += u > ukey ? c : 0u;
+      eb += u == ukey ? c : 0u;
+    });
   }
+  __syncthreads();
+  const int nstage = min(budget, kOutStage);
+  for (int p = tid; p < nstage; p += kSelThreads) out[p] = (int32_t)aux[p];
 }
 
 // ---- launchers ------------------------------------------------------------------

@@ -150,7 +150,7 @@ def _given_scores(W, seed, decimals=1):
 
 def test_select_given_scores_is_exact():
     lens = [1, 5, 6, 10, 2048, 2049, 2051, 700, 9000, 20000]
-    budgets = (1, 6, 7, 2048)
+    budgets = (1, 6, 7, 2048, 5000)   # 5000: positions past the 4096 gathered in LDS are stored directly
     cap = ix.n_windows(max(lens))
     sc = np.zeros((len(lens), cap), dtype=np.float32)
     for b, T in enumerate(lens):
@@ -174,14 +174,13 @@ def test_select_given_scores_is_exact():
 @pytest.mark.parametrize("T", [131072, 140001])
 def test_select_large_given_scores_is_exact(T):
     # 131072: every window staged in LDS; 140001: 35001 windows, those past 32768 read from memory
-    budget = 2048
     W = ix.n_windows(T)
-    for seed, dec in ((40, 2), (41, 6)):
+    for seed, dec, budget in ((40, 2, 2048), (41, 6, 2048), (42, 3, 9000)):
         s = _given_scores(W, seed, dec)[None, :]
         if T > 131072:
             s[0, -200:] = np.float32(50.0)            # the best windows lie past the staged ones
         sel, _ = mla.indexer_select(torch.from_numpy(s).cuda(), [0, T], budget)
-        assert np.array_equal(sel.cpu().numpy(), ix.select_positions(s[0], T, budget))
+        assert np.array_equal(sel.cpu().numpy(), ix.select_positions(s[0], T, budget)), (seed, budget)
 
 
 @pytest.mark.parametrize("lens,d", [([37, 1000, 4], 64), ([513], 512)])
