@@ -395,8 +395,10 @@ def indexer_sweep(args):
     and the absorbed attention over the selected positions that follows
     (GLM-5.3-Flash-like geometry, 64 heads, the step's 8 rows).  Cold: a 512 MiB
     scrub write before every sample; the host queues a sample's launches behind
-    a 2 ms device spin, so they run back to back; events around each piece,
-    median of `samples`, arms interleaved."""
+    a 2 ms device spin, so they run back to back.  Each sample runs twice: with
+    events around each piece (an event between kernels adds a dispatch gap of
+    about 6 us), and with events only around the step, which gives the step
+    figures.  Median of `samples`, arms interleaved."""
     import torch
     import mla_speculative_decode_amd as mla
     from mla_speculative_decode_amd import synth
@@ -459,8 +461,10 @@ def indexer_sweep(args):
             for f in parts:
                 f()
         times = {a: [[] for _ in range(4)] for a in arms}
+        whole = {a: [[], []] for a in arms}
         for i in range(args.samples):
             for a in (("incremental", "full") if i % 2 == 0 else ("full", "incremental")):
+                # pieces: an event after every piece (each event adds a dispatch gap)
                 scrub.fill_(i & 255)
                 torch.cuda._sleep(spin)
                 ev[0].record()
@@ -470,19 +474,30 @@ def indexer_sweep(args):
                 torch.cuda.synchronize()
                 for j in range(4):
                     times[a][j].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+                # whole: events only before the step, after the selection and after the attention
+                scrub.fill_((i + 128) & 255)
+                torch.cuda._sleep(spin)
+                ev[5].record()
+                for f in arms[a][:3]:
+                    f()
+                ev[6].record()
+                arms[a][3]()
+                ev[7].record()
+                torch.cuda.synchronize()
+                whole[a][0].append(ev[5].elapsed_time(ev[6]) * 1e3)
+                whole[a][1].append(ev[5].elapsed_time(ev[7]) * 1e3)
         med = {a: [float(np.median(t)) for t in times[a]] for a in arms}
+        wmed = {a: [float(np.median(t)) for t in whole[a]] for a in arms}
         inc, full = med["incremental"], med["full"]
         W = cap
         print(json.dumps({
             "indexer": wl["name"] if T == wl["kv"] else f"indexer_kv{T}_s{S}_d{d}_top{budget}", "kv": T, "S": S,
             "d": d, "budget": budget, "windows": W,
-            "indexer_step_us": {"incremental": round(sum(inc[:3]), 2), "full": round(sum(full[:3]), 2)},
-            "pool_us": {"tail": round(inc[0], 2), "full": round(full[0], 2)},
-            "scores_us": round(inc[1], 2), "select_us": round(inc[2], 2),
-            "sparse_attention_us": round(inc[3], 2),
-            "layer_step_us": {"incremental": round(sum(inc), 2), "full": round(sum(full), 2)},
-            "scores_GBps": round(W * d * 4 / (inc[1] * 1e-6) / 1e9, 1),
-            "pool_full_GBps": round((T * d * 2 + W * d * 4) / (full[0] * 1e-6) / 1e9, 1),
+            "indexer_step_us": {"incremental": round(wmed["incremental"][0], 2), "full": round(wmed["full"][0], 2)},
+            "layer_step_us": {"incremental": round(wmed["incremental"][1], 2), "full": round(wmed["full"][1], 2)},
+            "pieces_us (each with one dispatch gap)": {
+                "pool_tail": round(inc[0], 2), "pool_full": round(full[0], 2), "scores": round(inc[1], 2),
+                "select": round(inc[2], 2), "sparse_attention": round(inc[3], 2)},
             "attention_geometry": "r 512, n 256, v 256, rope 64, 64 heads, L 8 (GLM-5.3-Flash-like)",
             "samples": args.samples, "cache_state": "cold (512 MiB scrub before each sample)"}), flush=True)
         del pool, keys, k_pe, scores, sel, q_lat, out

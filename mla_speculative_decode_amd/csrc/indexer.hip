@@ -79,7 +79,12 @@ __global__ __launch_bounds__(256) void pool_windows_kernel(const uint16_t* __res
 // ---- scores -----------------------------------------------------------------
 // grid (ceil(wmax / 16), B), 256 threads: wave v takes windows 16 x + 4 v ..
 // + 3, lane l the float4 chunks l, l + 64, ... (d <= 1024: at most 4).
-constexpr int kScoreWin = 4;   // windows per wave
+constexpr int kScoreWin = 4;      // windows per wave and group (the reduction below assumes four)
+constexpr int kScoreBlocks = 512;  // workgroups per launch (4 waves each), shared by the sequences
+// One wave scores groups of kScoreWin consecutive windows, striding over the
+// sequence's groups; the next group's loads are in flight while the current
+// group is reduced.  J = 16-byte loads per lane and window (d <= 256 J).
+template <int J>
 __global__ __launch_bounds__(256) void window_scores_kernel(const float* __restrict__ pooled, int cap, int d,
                                                             const float* __restrict__ q,
                                                             const int32_t* __restrict__ off,
@@ -87,36 +92,60 @@ __global__ __launch_bounds__(256) void window_scores_kernel(const float* __restr
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.y;
   const int W = windows_of(off[b + 1] - off[b]);
-  const int w0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kScoreWin;
-  if (w0 >= W) return;
+  const int ngroups = (W + kScoreWin - 1) / kScoreWin;
+  const int stride = gridDim.x * 4;
+  int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= ngroups) return;
   const int nc = d / 4;
-  f32x4 qv[4];
+  f32x4 qv[J];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = lane + kWave * j;
-    qv[j] = c < nc ? *reinterpret_cast<const f32x4*>(q + (long long)b * d + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  f32x4 pv[kScoreWin][4];
+  for (int j = 0; j < J; ++j) qv[j] = *reinterpret_cast<const f32x4*>(q + (long long)b * d + 4 * min(lane + kWave * j, nc - 1));
+  const float* base = pooled + (long long)b * cap * d;
+  // every load is issued unconditionally (clamped addresses, values masked at use),
+  // so the wait for the current group leaves the next group's loads in flight
+  auto load = [&](int grp, f32x4 (&pv)[kScoreWin][J]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int k = 0; k < kScoreWin; ++k) {
-    const int w = min(w0 + k, W - 1);
-    const float* row = pooled + ((long long)b * cap + w) * d;
+    for (int k = 0; k < kScoreWin; ++k) {
+      const float* row = base + (long long)min(grp * kScoreWin + k, W - 1) * d;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = lane + kWave * j;
-      pv[k][j] = c < nc ? *reinterpret_cast<const f32x4*>(row + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < J; ++j) pv[k][j] = *reinterpret_cast<const f32x4*>(row + 4 * min(lane + kWave * j, nc - 1));
     }
-  }
+  };
+  f32x4 pv[kScoreWin][J];
+  load(g, pv);
+  for (;;) {
+    const int gn = g + stride;
+    f32x4 pn[kScoreWin][J];
+    load(gn < ngroups ? gn : g, pn);   // the last round reads its own group again (from L2)
+    float p[kScoreWin];
 #pragma unroll
-  for (int k = 0; k < kScoreWin; ++k) {
-    float s = 0.f;
+    for (int k = 0; k < kScoreWin; ++k) {
+      p[k] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < J; ++j) {
+        const bool in = lane + kWave * j < nc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s = fmaf(qv[j][e], pv[k][j][e], s);
+        for (int e = 0; e < 4; ++e) p[k] = fmaf(qv[j][e], in ? pv[k][j][e] : 0.f, p[k]);
+      }
+    }
+    // reduce the four windows together: after the xor-32 and xor-16 exchanges lane
+    // l carries window l >> 4 over four lanes, then four more halvings
+    const bool h = (lane & 32) != 0, gbit = (lane & 16) != 0;
+    float c0 = h ? p[2] : p[0], c1 = h ? p[3] : p[1];
+    c0 += __shfl_xor(h ? p[0] : p[2], 32, kWave);
+    c1 += __shfl_xor(h ? p[1] : p[3], 32, kWave);
+    float t = gbit ? c1 : c0;
+    t += __shfl_xor(gbit ? c0 : c1, 16, kWave);
 #pragma unroll
-    for (int dd = 32; dd >= 1; dd >>= 1) s += __shfl_xor(s, dd, kWave);
-    if (lane == 0 && w0 + k < W) scores[(long long)b * cap + w0 + k] = s;
+    for (int dd = 8; dd >= 1; dd >>= 1) t += __shfl_xor(t, dd, kWave);
+    const int w = g * kScoreWin + (lane >> 4);
+    if ((lane & 15) == 0 && w < W) scores[(long long)b * cap + w] = t;
+    if (gn >= ngroups) break;
+#pragma unroll
+    for (int k = 0; k < kScoreWin; ++k)
+#pragma unroll
+      for (int j = 0; j < J; ++j) pv[k][j] = pn[k][j];
+    g = gn;
   }
 }
 
@@ -259,6 +288,25 @@ __device__ __forceinline__ uint32_t wave_radix_list(const uint32_t (*cand)[2], u
     mask |= 255u << shift;
   }
   return prefix;
+}
+
+// The same select for a list of at most one candidate per lane: lane i counts the
+// weight above and equal to its own key directly.
+__device__ __forceinline__ uint32_t wave_rank_list(const uint32_t (*cand)[2], uint32_t nc, uint32_t* need) {
+  const uint32_t lane = threadIdx.x & 63;
+  const bool has = lane < nc;
+  const uint32_t ui = has ? cand[lane][0] : 0u;
+  uint32_t above = 0u, equal = 0u;
+#pragma unroll 4
+  for (uint32_t j = 0; j < nc; ++j) {   // the same entry for every lane: one broadcast read
+    const uint32_t uj = cand[j][0], cj = cand[j][1];
+    above += uj > ui ? cj : 0u;
+    equal += uj == ui ? cj : 0u;
+  }
+  const bool hit = has && above < *need && *need <= above + equal;   // the lanes of one key
+  const int src = max(__ffsll((long long)__ballot(hit)) - 1, 0);
+  *need -= __builtin_amdgcn_readlane(above, src);
+  return __builtin_amdgcn_readlane(ui, src);
 }
 
 // grid B, 1024 threads: one block per sequence.
@@ -422,7 +470,8 @@ __global__ __launch_bounds__(kSelThreads) void select_positions_kernel(const flo
   uint32_t ukey;
   if (nc <= kCand) {
     if (wv == 0) {
-      const uint32_t k = wave_radix_list(cand, nc, &need, &hist[0][0]);
+      const uint32_t k = nc <= (uint32_t)kWave ? wave_rank_list(cand, nc, &need)
+                                               : wave_radix_list(cand, nc, &need, &hist[0][0]);
       if (lane == 0) {
         pick[0] = k;
         pick[1] = need;
@@ -504,8 +553,11 @@ hipError_t indexer_pool(const void* keys, long long ld, const int32_t* off_dev, 
 hipError_t indexer_scores(const float* pooled, int cap, int d, const float* q, const int32_t* off_dev, int B,
                           int wmax, float* scores, hipStream_t st) {
   const int per_block = 4 * kScoreWin;
-  hipLaunchKernelGGL(window_scores_kernel, dim3((wmax + per_block - 1) / per_block, B), dim3(256), 0, st, pooled,
-                     cap, d, q, off_dev, scores);
+  const int gx = std::min((wmax + per_block - 1) / per_block, std::max(1, kScoreBlocks / B));
+  if (d <= 2 * 4 * kWave)
+    hipLaunchKernelGGL(window_scores_kernel<2>, dim3(gx, B), dim3(256), 0, st, pooled, cap, d, q, off_dev, scores);
+  else
+    hipLaunchKernelGGL(window_scores_kernel<4>, dim3(gx, B), dim3(256), 0, st, pooled, cap, d, q, off_dev, scores);
   return hipGetLastError();
 }
 

@@ -183,7 +183,7 @@ def test_select_large_given_scores_is_exact(T):
         assert np.array_equal(sel.cpu().numpy(), ix.select_positions(s[0], T, budget)), (seed, budget)
 
 
-@pytest.mark.parametrize("lens,d", [([37, 1000, 4], 64), ([513], 512)])
+@pytest.mark.parametrize("lens,d", [([37, 1000, 4], 64), ([513], 512), ([77, 300], 520), ([9000], 1024)])
 def test_scores_match_oracle(lens, d):
     x = synth.indexer_inputs(lens, d, seed=50 + d)
     per = [x.keys[x.offsets[b]:x.offsets[b + 1]] for b in range(len(lens))]
