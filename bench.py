@@ -316,13 +316,29 @@ def verify_curve(args):
                       "derived_caps": caps}), flush=True)
 
 
+class ReadScrub:
+    """Evicts the caches between samples by reading 512 MiB (a sum into one float).
+    A read leaves clean lines behind; a scrub by writing would leave dirty lines
+    whose write-back the next sample's reads pay for (measured: a cold 67 MB read
+    at 2.8 TB/s after a write scrub against 5.3 TB/s after this one)."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+        self.sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        import torch
+        torch.sum(self.buf, dim=0, out=self.sink)
+
+
 def sparse_sweep(args):
     """Absorbed attention (after the fold) over a selection of `budget` cached
     positions against dense attention over the whole cache: GLM-5.3-Flash-like
     geometry (r 512, n 256, v 256, rope 64), 64 heads, L = 16, one sequence, caches
     of 2048, 8192 and 32768 positions.  The selection is seeded random positions
     plus the newest L (an indexer's top-k stands in; its scoring is not part of
-    this path).  Cold: a 512 MiB scrub write before every sample; events around
+    this path).  Cold: a 512 MiB read scrub (ReadScrub) before every sample; events around
     the call, median of `samples`."""
     import torch
     import mla_speculative_decode_amd as mla
@@ -330,7 +346,7 @@ def sparse_sweep(args):
 
     budget = args.sparse
     dev = torch.device("cuda:0")
-    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scrub = ReadScrub(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(1000)
     e0.record()
@@ -371,7 +387,7 @@ def sparse_sweep(args):
         times = {a: [] for a in arms}
         for i in range(args.samples):
             for a in (("sparse", "dense") if i % 2 == 0 else ("dense", "sparse")):
-                scrub.fill_(i & 255)
+                scrub()
                 torch.cuda._sleep(spin)
                 e0.record()
                 arms[a]()
@@ -381,7 +397,7 @@ def sparse_sweep(args):
         print(json.dumps({"sparse_attention": w.name, "kv": kv, "budget": k, "cache": args.cache,
                           "sparse_us": round(float(np.median(times["sparse"])), 2),
                           "dense_us": round(float(np.median(times["dense"])), 2),
-                          "samples": args.samples, "cache_state": "cold (512 MiB scrub before each sample)"}),
+                          "samples": args.samples, "cache_state": "cold (512 MiB read scrub before each sample)"}),
               flush=True)
         del d, q_lat, out, sel_d
         torch.cuda.empty_cache()
@@ -394,7 +410,7 @@ def indexer_sweep(args):
     tail (guards hold) against pooling the whole cache, each kernel on its own,
     and the absorbed attention over the selected positions that follows
     (GLM-5.3-Flash-like geometry, 64 heads, the step's 8 rows).  Cold: a 512 MiB
-    scrub write before every sample; the host queues a sample's launches behind
+    read scrub (ReadScrub) before every sample; the host queues a sample's launches behind
     a 2 ms device spin, so they run back to back.  Each sample runs twice: with
     events around each piece (an event between kernels adds a dispatch gap of
     about 6 us), and with events only around the step, which gives the step
@@ -406,7 +422,7 @@ def indexer_sweep(args):
     wl = synth.INDEXER_WORKLOAD
     S, d, budget = wl["S"], wl["d"], wl["budget"]
     dev = torch.device("cuda:0")
-    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scrub = ReadScrub(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
     torch.cuda._sleep(1000)
     ev[0].record()
@@ -465,7 +481,7 @@ def indexer_sweep(args):
         for i in range(args.samples):
             for a in (("incremental", "full") if i % 2 == 0 else ("full", "incremental")):
                 # pieces: an event after every piece (each event adds a dispatch gap)
-                scrub.fill_(i & 255)
+                scrub()
                 torch.cuda._sleep(spin)
                 ev[0].record()
                 for j, f in enumerate(arms[a]):
@@ -475,7 +491,7 @@ def indexer_sweep(args):
                 for j in range(4):
                     times[a][j].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
                 # whole: events only before the step, after the selection and after the attention
-                scrub.fill_((i + 128) & 255)
+                scrub()
                 torch.cuda._sleep(spin)
                 ev[5].record()
                 for f in arms[a][:3]:
@@ -499,7 +515,7 @@ def indexer_sweep(args):
                 "pool_tail": round(inc[0], 2), "pool_full": round(full[0], 2), "scores": round(inc[1], 2),
                 "select": round(inc[2], 2), "sparse_attention": round(inc[3], 2)},
             "attention_geometry": "r 512, n 256, v 256, rope 64, 64 heads, L 8 (GLM-5.3-Flash-like)",
-            "samples": args.samples, "cache_state": "cold (512 MiB scrub before each sample)"}), flush=True)
+            "samples": args.samples, "cache_state": "cold (512 MiB read scrub before each sample)"}), flush=True)
         del pool, keys, k_pe, scores, sel, q_lat, out
         torch.cuda.empty_cache()
 
