@@ -17,11 +17,11 @@
 // min(budget, Kv) positions in the order (score descending, position
 // ascending) are written in increasing position order.  A histogram over
 // 2048 equal slices of the score range finds the slice holding the
-// budget-th position, a weighted radix select (8-bit digits of the score's
-// order key, weight = positions in the window) inside that slice finds the
-// score of the last window taken, and a scan over windows in index order then
-// places each taken window's positions.  Integer work only after the scores: the selection
-// of given scores is exact.
+// budget-th position; inside that slice a direct count (up to 64 windows) or a
+// weighted radix select (8-bit digits of the score's order key, weight =
+// positions in the window) finds the score of the last window taken, and a
+// scan over windows in index order then places each taken window's positions.
+// Integer work only after the scores: the selection of given scores is exact.
 
 #include "mla_device.h"
 #include "internal.h"

@@ -183,7 +183,11 @@ def test_select_large_given_scores_is_exact(T):
         assert np.array_equal(sel.cpu().numpy(), ix.select_positions(s[0], T, budget)), (seed, budget)
 
 
-@pytest.mark.parametrize("lens,d", [([37, 1000, 4], 64), ([513], 512), ([77, 300], 520), ([9000], 1024)])
+@pytest.mark.parametrize("lens,d", [([37, 1000, 4], 64), ([513], 512), ([77, 300], 520), ([9000], 1024),
+                                    # more sequences than the launch has workgroups: one workgroup
+                                    # per sequence striding over its groups of windows
+                                    ([1 + (37 * i) % 41 for i in range(700)], 64), ([2000] * 600, 8)],
+                         ids=["b3", "d512", "d520", "d1024", "b700", "b600_d8"])
 def test_scores_match_oracle(lens, d):
     x = synth.indexer_inputs(lens, d, seed=50 + d)
     per = [x.keys[x.offsets[b]:x.offsets[b + 1]] for b in range(len(lens))]
