@@ -77,8 +77,8 @@ __global__ __launch_bounds__(256) void pool_windows_kernel(const uint16_t* __res
 }
 
 // ---- scores -----------------------------------------------------------------
-// grid (ceil(wmax / 16), B), 256 threads: wave v takes windows 16 x + 4 v ..
-// + 3, lane l the float4 chunks l, l + 64, ... (d <= 1024: at most 4).
+// grid (min(ceil(wmax / 16), max(1, 512 / B)), B), 256 threads: group x of a
+// sequence is windows 4x .. 4x + 3; lane l takes the float4 chunks l, l + 64, ...
 constexpr int kScoreWin = 4;      // windows per wave and group (the reduction below assumes four)
 constexpr int kScoreBlocks = 512;  // workgroups per launch (4 waves each), shared by the sequences
 // One wave scores groups of kScoreWin consecutive windows, striding over the
