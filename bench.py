@@ -407,7 +407,8 @@ def indexer_sweep(args):
     """The pooled top-k indexer of a sparse layer, one sequence, a verify step
     of S = 8 new positions, keys = the bf16 latent rows (width 512), budget 2048:
     the whole indexer step (pooling, scores, selection) with the incremental
-    tail (guards hold) against pooling the whole cache, each kernel on its own,
+    tail (guards hold; separately, or pooled by the scoring launch itself)
+    against pooling the whole cache, each kernel on its own,
     and the absorbed attention over the selected positions that follows
     (GLM-5.3-Flash-like geometry, 64 heads, the step's 8 rows).  Cold: a 512 MiB
     read scrub (ReadScrub) before every sample; the host queues a sample's launches behind
@@ -472,14 +473,22 @@ def indexer_sweep(args):
             mla.fold_query(q_nope, w_uk, out=q_lat)
             mla.absorbed_attention_sparse(q_lat, q_pe, keys, k_pe, w_uv, offs, sel, soffs, scale=aw.scale, out=out)
 
-        arms = {"incremental": (pool_tail, score, select, attend), "full": (pool_full, score, select, attend)}
+        def fused():   # the tail pooled by the scoring launch itself
+            pool.trim([T - S])
+            assert pool.step_scores(keys, offs, S=S, q=q, out=scores)[1]
+
+        def nothing():
+            pass
+
+        arms = {"incremental": (pool_tail, score, select, attend), "full": (pool_full, score, select, attend),
+                "fused": (fused, nothing, select, attend)}
         for parts in arms.values():
             for f in parts:
                 f()
         times = {a: [[] for _ in range(4)] for a in arms}
         whole = {a: [[], []] for a in arms}
         for i in range(args.samples):
-            for a in (("incremental", "full") if i % 2 == 0 else ("full", "incremental")):
+            for a in (("incremental", "full", "fused") if i % 2 == 0 else ("fused", "full", "incremental")):
                 # pieces: an event after every piece (each event adds a dispatch gap)
                 scrub()
                 torch.cuda._sleep(spin)
@@ -509,10 +518,13 @@ def indexer_sweep(args):
         print(json.dumps({
             "indexer": wl["name"] if T == wl["kv"] else f"indexer_kv{T}_s{S}_d{d}_top{budget}", "kv": T, "S": S,
             "d": d, "budget": budget, "windows": W,
-            "indexer_step_us": {"incremental": round(wmed["incremental"][0], 2), "full": round(wmed["full"][0], 2)},
-            "layer_step_us": {"incremental": round(wmed["incremental"][1], 2), "full": round(wmed["full"][1], 2)},
+            "indexer_step_us": {"incremental": round(wmed["incremental"][0], 2), "full": round(wmed["full"][0], 2),
+                                "incremental_fused": round(wmed["fused"][0], 2)},
+            "layer_step_us": {"incremental": round(wmed["incremental"][1], 2), "full": round(wmed["full"][1], 2),
+                              "incremental_fused": round(wmed["fused"][1], 2)},
             "pieces_us (each with one dispatch gap)": {
                 "pool_tail": round(inc[0], 2), "pool_full": round(full[0], 2), "scores": round(inc[1], 2),
+                "pool_tail_and_scores_fused": round(med["fused"][0], 2),
                 "select": round(inc[2], 2), "sparse_attention": round(inc[3], 2)},
             "attention_geometry": "r 512, n 256, v 256, rope 64, 64 heads, L 8 (GLM-5.3-Flash-like)",
             "samples": args.samples, "cache_state": "cold (512 MiB read scrub before each sample)"}), flush=True)

@@ -394,6 +394,20 @@ int mla_indexer_pool_trim(mla_pool* pool, int32_t B, const int32_t* new_lengths)
 int mla_indexer_scores(const mla_pool* pool, int32_t B, const float* q, const int32_t* kv_offsets_host,
                        const int32_t* kv_offsets_dev, float* scores, void* stream);
 
+/*
+ * mla_indexer_pool_step_scores -- mla_indexer_pool_step followed by
+ * mla_indexer_scores, with the same arguments, effects and results (the same
+ * bits in pool->pooled and in scores), in fewer launches: when the guards hold,
+ * the scoring launch pools the tail windows itself (one launch instead of
+ * two); otherwise every window is pooled, then scored.  Errors: those of
+ * mla_indexer_pool_step, and MLA_E_NULL for q or scores NULL; on MLA_E_HIP
+ * the pool is marked invalid.
+ */
+int mla_indexer_pool_step_scores(mla_pool* pool, int32_t B, int32_t d, const void* keys, int64_t key_stride,
+                                 const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, int32_t S,
+                                 int32_t padded, const float* q, float* scores, int32_t* incremental_out,
+                                 void* stream);
+
 /* Offsets of the packed selection (host only): sel_offsets_out[0] = 0,
  * sel_offsets_out[b+1] = sel_offsets_out[b] + min(budget, Kv_b).  Errors:
  * MLA_E_NULL, MLA_E_SHAPE (B < 1, budget < 1, bad offsets). */

@@ -384,6 +384,24 @@ class IndexerPool:
             keys.stride(0), offs.host_ptr(), offs.dev_ptr(), S, int(padded), ctypes.byref(inc), _stream(stream)))
         return bool(inc.value)
 
+    def step_scores(self, keys, kv_offsets, S: int, q, out=None, padded: bool = False, stream=None):
+        """step() then scores() in one call (tail pooling fused into the scoring
+        launch when the guards hold); returns (scores, incremental)."""
+        torch = _torch()
+        if keys.dtype != torch.bfloat16 or keys.dim() != 2 or keys.stride(1) != 1 or keys.shape[1] < self.d:
+            raise ValueError("keys must be a bf16 [T, >= d] device tensor with unit column stride")
+        offs = kv_offsets if isinstance(kv_offsets, Offsets) else Offsets(kv_offsets, keys.device)
+        if q.dtype != torch.float32 or tuple(q.shape) != (offs.B, self.d):
+            raise ValueError("q must be float32 [B, d]")
+        if out is None:
+            out = torch.zeros((offs.B, self.capacity), dtype=torch.float32, device=q.device)
+        inc = ctypes.c_int32()
+        _lib.check("mla_indexer_pool_step_scores", _lib.load().mla_indexer_pool_step_scores(
+            ctypes.byref(self.state), offs.B, self.d, ctypes.c_void_p(_dev(keys, "keys").data_ptr()),
+            keys.stride(0), offs.host_ptr(), offs.dev_ptr(), S, int(padded), _ptr(_dev(q, "q")), _ptr(out),
+            ctypes.byref(inc), _stream(stream)))
+        return out, bool(inc.value)
+
     def trim(self, new_lengths) -> None:
         torch = _torch()
         nl = torch.as_tensor(new_lengths, dtype=torch.int32).contiguous()

@@ -23,8 +23,8 @@ EXPORTS = ("mla_status_string", "mla_version", "mla_select_path", "mla_draft_cap
            "mla_materialized_workspace_size", "mla_materialized_attention", "mla_quantize_latent_fp8",
            "mla_absorbed_attention_fp8", "mla_absorbed_splits_fp8", "mla_absorbed_sparse_workspace_size",
            "mla_absorbed_attention_sparse", "mla_absorbed_attention_sparse_fp8", "mla_indexer_pool_init", "mla_indexer_pool_plan",
-           "mla_indexer_pool_step", "mla_indexer_pool_trim", "mla_indexer_scores", "mla_indexer_selection_offsets",
-           "mla_indexer_select")
+           "mla_indexer_pool_step", "mla_indexer_pool_trim", "mla_indexer_scores", "mla_indexer_pool_step_scores",
+           "mla_indexer_selection_offsets", "mla_indexer_select")
 
 
 class Geom(ctypes.Structure):
@@ -118,6 +118,7 @@ def load() -> ctypes.CDLL:
                        ("mla_indexer_pool_step", [PP, I32, I32, VP, I64, VP, VP, I32, I32, I32P, VP]),
                        ("mla_indexer_pool_trim", [PP, I32, VP]),
                        ("mla_indexer_scores", [PP, I32, VP, VP, VP, VP, VP]),
+                       ("mla_indexer_pool_step_scores", [PP, I32, I32, VP, I64, VP, VP, I32, I32, VP, VP, I32P, VP]),
                        ("mla_indexer_selection_offsets", [I32, VP, I32, VP]),
                        ("mla_indexer_select", [I32, VP, I32, VP, VP, I32, VP, VP, VP])):
         fn = getattr(lib, name)

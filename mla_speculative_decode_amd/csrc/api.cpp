@@ -579,7 +579,46 @@ int mla_indexer_scores(const mla_pool* pool, int32_t B, const float* q, const in
     wmax = std::max(wmax, pool_windows(kv));
   }
   return hip_status(indexer_scores(pool->pooled, pool->capacity, pool->d, q, kv_offsets_dev, B, (int)wmax, scores,
-                                   (hipStream_t)stream));
+                                   nullptr, 0, 0, (hipStream_t)stream));
+}
+
+int mla_indexer_pool_step_scores(mla_pool* pool, int32_t B, int32_t d, const void* keys, int64_t key_stride,
+                                 const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, int32_t S,
+                                 int32_t padded, const float* q, float* scores, int32_t* incremental_out,
+                                 void* stream) {
+  if (!pool || !pool->pooled || !pool->lengths || !keys || !kv_offsets_dev || !q || !scores) return MLA_E_NULL;
+  if (S < 1 || key_stride < d) return MLA_E_SHAPE;
+  int st = check_plain_offsets(B, kv_offsets_host, S);
+  if (st) return st;
+  if (B > pool->batch_max) return MLA_E_SHAPE;
+  if (d < 8 || d > 1024 || d % 8 != 0) return MLA_E_UNSUPPORTED;
+  const bool inc = pool_guards_hold(pool, B, d, kv_offsets_host, S, padded);
+  int64_t wmax = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t kv = (int64_t)kv_offsets_host[b + 1] - kv_offsets_host[b];
+    if (pool_windows(kv) > pool->capacity) return MLA_E_SHAPE;
+    wmax = std::max(wmax, pool_windows(kv));
+  }
+  if ((int64_t)kv_offsets_host[B] * key_stride > INT64_MAX / 2) return MLA_E_SHAPE;
+  pool->valid = 0;   // until the launches are known to be enqueued
+  hipStream_t hs = (hipStream_t)stream;
+  if (inc) {   // one launch: the scoring pools the tail windows itself
+    st = hip_status(indexer_scores(pool->pooled, pool->capacity, d, q, kv_offsets_dev, B, (int)wmax, scores,
+                                   (const uint16_t*)keys, key_stride, S, hs));
+  } else {
+    st = hip_status(indexer_pool(keys, key_stride, kv_offsets_dev, B, d, S, true, (int)wmax, pool->pooled,
+                                 pool->capacity, hs));
+    if (!st)
+      st = hip_status(indexer_scores(pool->pooled, pool->capacity, d, q, kv_offsets_dev, B, (int)wmax, scores,
+                                     nullptr, 0, 0, hs));
+  }
+  if (st) return st;
+  for (int32_t b = 0; b < B; ++b) pool->lengths[b] = kv_offsets_host[b + 1] - kv_offsets_host[b];
+  pool->batch = B;
+  pool->d = d;
+  pool->valid = 1;
+  if (incremental_out) *incremental_out = inc ? 1 : 0;
+  return MLA_OK;
 }
 
 int mla_indexer_selection_offsets(int32_t B, const int32_t* kv_offsets_host, int32_t budget,

@@ -84,18 +84,33 @@ constexpr int kScoreBlocks = 512;  // workgroups per launch (4 waves each), shar
 // One wave scores groups of kScoreWin consecutive windows, striding over the
 // sequence's groups; the next group's loads are in flight while the current
 // group is reduced.  J = 16-byte loads per lane and window (d <= 256 J).
-template <int J>
-__global__ __launch_bounds__(256) void window_scores_kernel(const float* __restrict__ pooled, int cap, int d,
+// TAIL: the launch also pools the tail windows (from floor((Kv - S) / 4) on):
+// the wave that scores such a window pools it from the key rows with the
+// pooling kernel's arithmetic (rows summed in position order in float32, then
+// divided by the row count), stores it and scores the value it holds.
+struct TailArgs {
+  const uint16_t* keys;   // bf16 key rows, position p of sequence b at keys + (off[b] + p) * ld
+  long long ld;
+  int S;
+};
+
+template <int J, bool TAIL>
+__global__ __launch_bounds__(256) void window_scores_kernel(float* __restrict__ pooled, int cap, int d,
                                                             const float* __restrict__ q,
                                                             const int32_t* __restrict__ off,
-                                                            float* __restrict__ scores) {
+                                                            float* __restrict__ scores, TailArgs ta) {
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.y;
-  const int W = windows_of(off[b + 1] - off[b]);
+  const int Kv = off[b + 1] - off[b];
+  const int W = windows_of(Kv);
+  const int first = TAIL ? (Kv - ta.S) / kWin : W;   // windows from here on are pooled here
   const int ngroups = (W + kScoreWin - 1) / kScoreWin;
+  // groups are taken from the end of the sequence backwards, so the groups that
+  // hold tail windows (pooled here first) are each wave's first
   const int stride = gridDim.x * 4;
-  int g = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= ngroups) return;
+  int gi = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gi >= ngroups) return;
+  int g = ngroups - 1 - gi;
   const int nc = d / 4;
   f32x4 qv[J];
 #pragma unroll
@@ -114,9 +129,42 @@ __global__ __launch_bounds__(256) void window_scores_kernel(const float* __restr
   f32x4 pv[kScoreWin][J];
   load(g, pv);
   for (;;) {
-    const int gn = g + stride;
+    if (TAIL && (g + 1) * kScoreWin > first) {   // uniform: this group holds tail windows
+#pragma unroll
+      for (int k = 0; k < kScoreWin; ++k) {
+        const int w = g * kScoreWin + k;
+        if (w < first || w >= W) continue;
+        const int n = min(kWin, Kv - kWin * w);
+        const float fn = (float)n;
+        const uint16_t* src = ta.keys + ((long long)off[b] + kWin * w) * ta.ld;
+        float* dst = pooled + ((long long)b * cap + w) * d;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int c = min(lane + kWave * j, nc - 1);   // columns 4c .. 4c + 3
+          u32x2 x[kWin];   // every row's load in flight at once (rows past n repeat the last)
+#pragma unroll
+          for (int r = 0; r < kWin; ++r) x[r] = *reinterpret_cast<const u32x2*>(src + (long long)min(r, n - 1) * ta.ld + 4 * c);
+          float acc[4] = {bf16_lo(x[0][0]), bf16_hi(x[0][0]), bf16_lo(x[0][1]), bf16_hi(x[0][1])};
+#pragma unroll
+          for (int r = 1; r < kWin; ++r) {
+            if (r < n) {   // rows summed in position order, as in the pooling kernel
+              acc[0] += bf16_lo(x[r][0]);
+              acc[1] += bf16_hi(x[r][0]);
+              acc[2] += bf16_lo(x[r][1]);
+              acc[3] += bf16_hi(x[r][1]);
+            }
+          }
+          f32x4 m;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m[e] = acc[e] / fn;   // correctly rounded, as in the pooling kernel
+          if (lane + kWave * j < nc) *reinterpret_cast<f32x4*>(dst + 4 * c) = m;
+          pv[k][j] = m;
+        }
+      }
+    }
+    const int gni = gi + stride, gn = ngroups - 1 - gni;
     f32x4 pn[kScoreWin][J];
-    load(gn < ngroups ? gn : g, pn);   // the last round reads its own group again (from L2)
+    load(gni < ngroups ? gn : g, pn);   // the last round reads its own group again (from L2)
     float p[kScoreWin];
 #pragma unroll
     for (int k = 0; k < kScoreWin; ++k) {
@@ -140,11 +188,12 @@ __global__ __launch_bounds__(256) void window_scores_kernel(const float* __restr
     for (int dd = 8; dd >= 1; dd >>= 1) t += __shfl_xor(t, dd, kWave);
     const int w = g * kScoreWin + (lane >> 4);
     if ((lane & 15) == 0 && w < W) scores[(long long)b * cap + w] = t;
-    if (gn >= ngroups) break;
+    if (gni >= ngroups) break;
 #pragma unroll
     for (int k = 0; k < kScoreWin; ++k)
 #pragma unroll
       for (int j = 0; j < J; ++j) pv[k][j] = pn[k][j];
+    gi = gni;
     g = gn;
   }
 }
@@ -550,14 +599,23 @@ hipError_t indexer_pool(const void* keys, long long ld, const int32_t* off_dev, 
   return hipGetLastError();
 }
 
-hipError_t indexer_scores(const float* pooled, int cap, int d, const float* q, const int32_t* off_dev, int B,
-                          int wmax, float* scores, hipStream_t st) {
+hipError_t indexer_scores(float* pooled, int cap, int d, const float* q, const int32_t* off_dev, int B, int wmax,
+                          float* scores, const uint16_t* tail_keys, long long tail_ld, int tail_S, hipStream_t st) {
   const int per_block = 4 * kScoreWin;
   const int gx = std::min((wmax + per_block - 1) / per_block, std::max(1, kScoreBlocks / B));
-  if (d <= 2 * 4 * kWave)
-    hipLaunchKernelGGL(window_scores_kernel<2>, dim3(gx, B), dim3(256), 0, st, pooled, cap, d, q, off_dev, scores);
-  else
-    hipLaunchKernelGGL(window_scores_kernel<4>, dim3(gx, B), dim3(256), 0, st, pooled, cap, d, q, off_dev, scores);
+  const TailArgs ta{tail_keys, tail_ld, tail_S};
+  const dim3 grid(gx, B);
+  if (tail_keys) {
+    if (d <= 2 * 4 * kWave)
+      hipLaunchKernelGGL((window_scores_kernel<2, true>), grid, dim3(256), 0, st, pooled, cap, d, q, off_dev, scores, ta);
+    else
+      hipLaunchKernelGGL((window_scores_kernel<4, true>), grid, dim3(256), 0, st, pooled, cap, d, q, off_dev, scores, ta);
+  } else {
+    if (d <= 2 * 4 * kWave)
+      hipLaunchKernelGGL((window_scores_kernel<2, false>), grid, dim3(256), 0, st, pooled, cap, d, q, off_dev, scores, ta);
+    else
+      hipLaunchKernelGGL((window_scores_kernel<4, false>), grid, dim3(256), 0, st, pooled, cap, d, q, off_dev, scores, ta);
+  }
   return hipGetLastError();
 }
 

@@ -62,8 +62,10 @@ hipError_t quantize_latent_fp8(long long T, int r, int rope, const void* c_kv, c
 // indexer.hip
 hipError_t indexer_pool(const void* keys, long long ld, const int32_t* off_dev, int B, int d, int S, bool full,
                         int wmax, float* pooled, int cap, hipStream_t st);
-hipError_t indexer_scores(const float* pooled, int cap, int d, const float* q, const int32_t* off_dev, int B,
-                          int wmax, float* scores, hipStream_t st);
+// tail_keys != null: the launch also pools the windows from floor((Kv - tail_S) / 4)
+// on from those key rows (row stride tail_ld elements) before scoring them
+hipError_t indexer_scores(float* pooled, int cap, int d, const float* q, const int32_t* off_dev, int B, int wmax,
+                          float* scores, const uint16_t* tail_keys, long long tail_ld, int tail_S, hipStream_t st);
 hipError_t indexer_select(const float* scores, int cap, const int32_t* off_dev, int B, int budget,
                           const int32_t* sel_off_dev, int32_t* sel, hipStream_t st);
 

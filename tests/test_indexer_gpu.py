@@ -285,3 +285,35 @@ def test_indexer_feeds_sparse_attention():
     ref = sparse.sparse_latent_attention(q_lat, q_pe, c_kv, k_pe, w_uv, off, np.concatenate(ref_sel), ref_soff,
                                          L, scale)
     check_close(out.double().cpu().numpy().reshape(-1, v), ref, "bf16", "indexer -> sparse attention")
+
+
+@pytest.mark.parametrize("d", [64, 520])
+def test_step_scores_equals_step_then_scores(d):
+    # the fused call pools the tail inside the scoring launch; pooled keys and
+    # scores must carry the same bits as the two separate calls, on the full
+    # path (first step, padded step) and on the incremental one
+    lens0 = [37, 1000, 4]
+    steps = [(1, False), (3, False), (8, False), (2, True), (5, False), (4, False)]
+    total = [n + sum(s for s, _ in steps) for n in lens0]
+    x = synth.indexer_inputs(total, d, seed=90 + d)
+    per = [x.keys[x.offsets[b]:x.offsets[b + 1]] for b in range(len(total))]
+    cap = ix.n_windows(max(total))
+    a = mla.IndexerPool(capacity=cap, batch_max=3, d=d)
+    f = mla.IndexerPool(capacity=cap, batch_max=3, d=d)
+    qs = synth.draw_like((len(steps) + 1, 3, d), 1.0, "f32", seed=91)
+    lens = list(lens0)
+    for i, (S, padded) in enumerate([(1, False)] + steps):
+        if i > 0:
+            lens = [n + S for n in lens]
+        keys, off = _packed([p[:n] for p, n in zip(per, lens)])
+        q = torch.from_numpy(np.ascontiguousarray(qs[i])).cuda()
+        inc_a = a.step(keys, off, S=S, padded=padded)
+        sa = a.scores(q, off)
+        sf, inc_f = f.step_scores(keys, off, S=S, q=q, padded=padded)
+        torch.cuda.synchronize()
+        assert inc_a == inc_f, (i, inc_a, inc_f)
+        for b, T in enumerate(lens):
+            W = ix.n_windows(T)
+            assert torch.equal(a.pooled[b, :W], f.pooled[b, :W]), (i, b)
+            assert torch.equal(sa[b, :W], sf[b, :W]), (i, b)
+    assert inc_f   # the last steps ran the fused tail

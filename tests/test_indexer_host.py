@@ -126,6 +126,18 @@ def test_errors_before_any_launch(lib):
     assert step(2, 16, dummy, 16, _off([40, 12]), 1) == MLA_E_SHAPE    # 10 windows > capacity 8
     assert step(2, 16, None, 16, off, 1) == MLA_E_NULL
     assert p.st.valid == 0
+    # the fused step + scores validates the same way, and needs q and scores
+    fused = lambda B, d, stride, o, S, q=dummy, sc=dummy, pool=p: lib.mla_indexer_pool_step_scores(   # noqa: E731
+        ctypes.byref(pool.st), B, d, dummy, stride, vp(o), dummy, S, 0, q, sc, None, None)
+    assert fused(2, 12, 12, off, 1) == MLA_E_UNSUPPORTED
+    assert fused(2, 16, 8, off, 1) == MLA_E_SHAPE
+    assert fused(2, 16, 16, off, 0) == MLA_E_SHAPE
+    assert fused(2, 16, 16, off, 13) == MLA_E_SHAPE
+    assert fused(3, 16, 16, _off([4, 4, 4]), 1) == MLA_E_SHAPE
+    assert fused(2, 16, 16, _off([40, 12]), 1) == MLA_E_SHAPE
+    assert fused(2, 16, 16, off, 1, q=None) == MLA_E_NULL
+    assert fused(2, 16, 16, off, 1, sc=None) == MLA_E_NULL
+    assert p.st.valid == 0
     # scores need a valid pool that covers the caches as they are
     assert lib.mla_indexer_scores(ctypes.byref(p.st), 2, dummy, vp(off), dummy, dummy, None) == MLA_E_SHAPE
     p.pretend_step([20, 11], 16)
