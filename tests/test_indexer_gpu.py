@@ -292,15 +292,15 @@ def test_step_scores_equals_step_then_scores(d):
     # the fused call pools the tail inside the scoring launch; pooled keys and
     # scores must carry the same bits as the two separate calls, on the full
     # path (first step, padded step) and on the incremental one
-    lens0 = [37, 1000, 4]
+    lens0 = [37, 1000, 4, 1]   # the last: every window of the first steps is a tail window
     steps = [(1, False), (3, False), (8, False), (2, True), (5, False), (4, False)]
     total = [n + sum(s for s, _ in steps) for n in lens0]
     x = synth.indexer_inputs(total, d, seed=90 + d)
     per = [x.keys[x.offsets[b]:x.offsets[b + 1]] for b in range(len(total))]
     cap = ix.n_windows(max(total))
-    a = mla.IndexerPool(capacity=cap, batch_max=3, d=d)
-    f = mla.IndexerPool(capacity=cap, batch_max=3, d=d)
-    qs = synth.draw_like((len(steps) + 1, 3, d), 1.0, "f32", seed=91)
+    a = mla.IndexerPool(capacity=cap, batch_max=4, d=d)
+    f = mla.IndexerPool(capacity=cap, batch_max=4, d=d)
+    qs = synth.draw_like((len(steps) + 1, 4, d), 1.0, "f32", seed=91)
     lens = list(lens0)
     for i, (S, padded) in enumerate([(1, False)] + steps):
         if i > 0:
