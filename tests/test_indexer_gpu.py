@@ -250,6 +250,14 @@ def test_indexer_workload_full_size():
     assert np.all(np.abs(got_s - ref_s) <= sbar)
     sel, _ = mla.indexer_select(inc.scores(q, [0, T]), [0, T], budget)
     _check_selection(sel.cpu().numpy(), ref_s, T, budget, sbar)
+    # the fused step (tail pooled by the scoring launch) at the same size: same bits
+    fused = mla.IndexerPool(capacity=cap, batch_max=1, d=d)
+    assert not fused.step(keys[:T - S], [0, T - S], S=T - S)
+    sf, was_inc = fused.step_scores(keys, [0, T], S=S, q=q)
+    torch.cuda.synchronize()
+    assert was_inc
+    assert torch.equal(fused.pooled[0], inc.pooled[0])
+    assert torch.equal(sf, inc.scores(q, [0, T]))
 
 
 def test_indexer_feeds_sparse_attention():
