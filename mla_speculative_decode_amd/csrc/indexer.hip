@@ -77,17 +77,20 @@ __global__ __launch_bounds__(256) void pool_windows_kernel(const uint16_t* __res
 }
 
 // ---- scores -----------------------------------------------------------------
-// grid (min(ceil(wmax / 16), max(1, 512 / B)), B), 256 threads: group x of a
-// sequence is windows 4x .. 4x + 3; lane l takes the float4 chunks l, l + 64, ...
+// grid (min(ceil(wmax / 16), max(1, 512 / B)) [+ 1 with TAIL], B), 256 threads:
+// group x of a sequence is windows 4x .. 4x + 3; lane l takes the float4 chunks
+// l, l + 64, ...
 constexpr int kScoreWin = 4;      // windows per wave and group (the reduction below assumes four)
 constexpr int kScoreBlocks = 512;  // workgroups per launch (4 waves each), shared by the sequences
 // One wave scores groups of kScoreWin consecutive windows, striding over the
 // sequence's groups; the next group's loads are in flight while the current
 // group is reduced.  J = 16-byte loads per lane and window (d <= 256 J).
-// TAIL: the launch also pools the tail windows (from floor((Kv - S) / 4) on):
-// the wave that scores such a window pools it from the key rows with the
-// pooling kernel's arithmetic (rows summed in position order in float32, then
-// divided by the row count), stores it and scores the value it holds.
+// TAIL: the launch also pools the tail windows (from floor((Kv - S) / 4) on).
+// The first workgroup of the grid (dispatched first) takes the groups that hold them: each wave
+// pools its tail windows from the key rows with the pooling kernel's arithmetic
+// (rows summed in position order in float32, then divided by the row count),
+// stores them and scores the values it holds; the other workgroups stream the
+// groups before them.
 struct TailArgs {
   const uint16_t* keys;   // bf16 key rows, position p of sequence b at keys + (off[b] + p) * ld
   long long ld;
@@ -99,19 +102,17 @@ __global__ __launch_bounds__(256) void window_scores_kernel(float* __restrict__ 
                                                             const float* __restrict__ q,
                                                             const int32_t* __restrict__ off,
                                                             float* __restrict__ scores, TailArgs ta) {
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
   const int Kv = off[b + 1] - off[b];
   const int W = windows_of(Kv);
-  const int first = TAIL ? (Kv - ta.S) / kWin : W;   // windows from here on are pooled here
   const int ngroups = (W + kScoreWin - 1) / kScoreWin;
-  // groups are taken from the end of the sequence backwards, so the groups that
-  // hold tail windows (pooled here first) are each wave's first
-  const int stride = gridDim.x * 4;
-  int gi = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (gi >= ngroups) return;
-  int g = ngroups - 1 - gi;
+  const int first = TAIL ? (Kv - ta.S) / kWin : W;   // windows from here on are pooled here
+  const int gtail = TAIL ? min(first / kScoreWin, ngroups) : ngroups;   // first group with a tail window
+  const bool tail_block = TAIL && blockIdx.x == 0;
+  const int sb = (int)blockIdx.x - (TAIL ? 1 : 0);   // index among the streaming workgroups
   const int nc = d / 4;
+  if (tail_block ? gtail + wave >= ngroups : sb * 4 + wave >= gtail) return;
   f32x4 qv[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) qv[j] = *reinterpret_cast<const f32x4*>(q + (long long)b * d + 4 * min(lane + kWave * j, nc - 1));
@@ -126,10 +127,37 @@ __global__ __launch_bounds__(256) void window_scores_kernel(float* __restrict__ 
       for (int j = 0; j < J; ++j) pv[k][j] = *reinterpret_cast<const f32x4*>(row + 4 * min(lane + kWave * j, nc - 1));
     }
   };
-  f32x4 pv[kScoreWin][J];
-  load(g, pv);
-  for (;;) {
-    if (TAIL && (g + 1) * kScoreWin > first) {   // uniform: this group holds tail windows
+  // scores of the group's four windows from pv: fixed-order fma chains, then the four
+  // reduced together (after the xor-32 and xor-16 exchanges lane l carries window
+  // l >> 4 over four lanes, then four more halvings)
+  auto score = [&](int grp, const f32x4 (&pv)[kScoreWin][J]) __attribute__((always_inline)) {
+    float p[kScoreWin];
+#pragma unroll
+    for (int k = 0; k < kScoreWin; ++k) {
+      p[k] = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const bool in = lane + kWave * j < nc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[k] = fmaf(qv[j][e], in ? pv[k][j][e] : 0.f, p[k]);
+      }
+    }
+    const bool h = (lane & 32) != 0, gbit = (lane & 16) != 0;
+    float c0 = h ? p[2] : p[0], c1 = h ? p[3] : p[1];
+    c0 += __shfl_xor(h ? p[0] : p[2], 32, kWave);
+    c1 += __shfl_xor(h ? p[1] : p[3], 32, kWave);
+    float t = gbit ? c1 : c0;
+    t += __shfl_xor(gbit ? c0 : c1, 16, kWave);
+#pragma unroll
+    for (int dd = 8; dd >= 1; dd >>= 1) t += __shfl_xor(t, dd, kWave);
+    const int w = grp * kScoreWin + (lane >> 4);
+    if ((lane & 15) == 0 && w < W) scores[(long long)b * cap + w] = t;
+  };
+
+  if (TAIL && tail_block) {
+    for (int g = gtail + wave; g < ngroups; g += 4) {
+      f32x4 pv[kScoreWin][J];
+      load(g, pv);   // windows before `first` keep their pooled keys
 #pragma unroll
       for (int k = 0; k < kScoreWin; ++k) {
         const int w = g * kScoreWin + k;
@@ -161,34 +189,23 @@ __global__ __launch_bounds__(256) void window_scores_kernel(float* __restrict__ 
           pv[k][j] = m;
         }
       }
+      score(g, pv);
     }
-    const int gni = gi + stride, gn = ngroups - 1 - gni;
+    return;
+  }
+
+  // streaming workgroups: groups [0, gtail), from the end backwards
+  const int stride = (int)(TAIL ? gridDim.x - 1 : gridDim.x) * 4;
+  int gi = sb * 4 + wave;
+  int g = gtail - 1 - gi;
+  f32x4 pv[kScoreWin][J];
+  load(g, pv);
+  for (;;) {
+    const int gni = gi + stride, gn = gtail - 1 - gni;
     f32x4 pn[kScoreWin][J];
-    load(gni < ngroups ? gn : g, pn);   // the last round reads its own group again (from L2)
-    float p[kScoreWin];
-#pragma unroll
-    for (int k = 0; k < kScoreWin; ++k) {
-      p[k] = 0.f;
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const bool in = lane + kWave * j < nc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[k] = fmaf(qv[j][e], in ? pv[k][j][e] : 0.f, p[k]);
-      }
-    }
-    // reduce the four windows together: after the xor-32 and xor-16 exchanges lane
-    // l carries window l >> 4 over four lanes, then four more halvings
-    const bool h = (lane & 32) != 0, gbit = (lane & 16) != 0;
-    float c0 = h ? p[2] : p[0], c1 = h ? p[3] : p[1];
-    c0 += __shfl_xor(h ? p[0] : p[2], 32, kWave);
-    c1 += __shfl_xor(h ? p[1] : p[3], 32, kWave);
-    float t = gbit ? c1 : c0;
-    t += __shfl_xor(gbit ? c0 : c1, 16, kWave);
-#pragma unroll
-    for (int dd = 8; dd >= 1; dd >>= 1) t += __shfl_xor(t, dd, kWave);
-    const int w = g * kScoreWin + (lane >> 4);
-    if ((lane & 15) == 0 && w < W) scores[(long long)b * cap + w] = t;
-    if (gni >= ngroups) break;
+    load(gni < gtail ? gn : g, pn);   // the last round reads its own group again (from L2)
+    score(g, pv);
+    if (gni >= gtail) break;
 #pragma unroll
     for (int k = 0; k < kScoreWin; ++k)
 #pragma unroll
@@ -604,7 +621,7 @@ hipError_t indexer_scores(float* pooled, int cap, int d, const float* q, const i
   const int per_block = 4 * kScoreWin;
   const int gx = std::min((wmax + per_block - 1) / per_block, std::max(1, kScoreBlocks / B));
   const TailArgs ta{tail_keys, tail_ld, tail_S};
-  const dim3 grid(gx, B);
+  const dim3 grid(gx + (tail_keys ? 1 : 0), B);   // + the workgroup that pools and scores the tail
   if (tail_keys) {
     if (d <= 2 * 4 * kWave)
       hipLaunchKernelGGL((window_scores_kernel<2, true>), grid, dim3(256), 0, st, pooled, cap, d, q, off_dev, scores, ta);
