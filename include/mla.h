@@ -343,7 +343,9 @@ typedef struct mla_pool {
   int32_t batch_max;    /* sequences the buffer (and lengths) hold                        */
   int32_t batch;        /* sequences the pool was last built for                          */
   int32_t d;            /* key width the pool was last built for                          */
-  int32_t valid;        /* 1 once a step has pooled keys; 0 after init or a failed step   */
+  int32_t valid;        /* 1 once a step has pooled keys; 0 after init or a failed step;  */
+                        /* 2 after a trim that cut inside a window (a step must run       */
+                        /* before the pool is scored; it still seeds an incremental step)  */
   int32_t* lengths;     /* host [batch_max]: cache length per sequence the pool covers    */
 } mla_pool;
 
@@ -380,16 +382,20 @@ int mla_indexer_pool_step(mla_pool* pool, int32_t B, int32_t d, const void* keys
 /* A speculative rejection cut sequence b's cache back to new_lengths[b]
  * positions (host array [B]): the pool forgets what it covered past the cut
  * (host only; the next step recomputes from the window holding the cut).
- * Entries not below the remembered length change nothing.  Errors: MLA_E_NULL,
- * MLA_E_SHAPE (pool not valid, B != pool->batch, a negative length). */
+ * Entries not below the remembered length change nothing.  A cut inside a
+ * window (new length not a multiple of 4) leaves that window's pooled key
+ * holding rows past the cut, so the pool is marked valid = 2 and
+ * mla_indexer_scores refuses it until the next step has run.  Errors:
+ * MLA_E_NULL, MLA_E_SHAPE (pool not valid, B != pool->batch, a negative length). */
 int mla_indexer_pool_trim(mla_pool* pool, int32_t B, const int32_t* new_lengths);
 
 /*
  * mla_indexer_scores -- scores[b * capacity + w] = q[b] . pooled key of window
  * w, for w < ceil(Kv_b / 4) (the rest untouched).  q: device float32 [B][d].
- * The pool must cover the caches as they are (pool->lengths[b] == Kv_b).
- * Errors: MLA_E_NULL, MLA_E_SHAPE (pool not valid, B != pool->batch, a length
- * not covered), MLA_E_HIP.
+ * The pool must cover the caches as they are (pool->lengths[b] == Kv_b) and
+ * hold no window cut by a trim (valid == 1).  Errors: MLA_E_NULL, MLA_E_SHAPE
+ * (pool not valid or trimmed inside a window, B != pool->batch, a length not
+ * covered), MLA_E_HIP.
  */
 int mla_indexer_scores(const mla_pool* pool, int32_t B, const float* q, const int32_t* kv_offsets_host,
                        const int32_t* kv_offsets_dev, float* scores, void* stream);
@@ -397,9 +403,10 @@ int mla_indexer_scores(const mla_pool* pool, int32_t B, const float* q, const in
 /*
  * mla_indexer_pool_step_scores -- mla_indexer_pool_step followed by
  * mla_indexer_scores, with the same arguments, effects and results (the same
- * bits in pool->pooled and in scores), in fewer launches: when the guards hold,
- * the scoring launch pools the tail windows itself (one launch instead of
- * two); otherwise every window is pooled, then scored.  Errors: those of
+ * bits in pool->pooled and in scores), in fewer launches: when the guards hold
+ * and every sequence's tail is at most 16 windows, the scoring launch pools the
+ * tail windows itself (one launch instead of two); a longer tail is pooled by
+ * the pooling kernel first; otherwise every window is pooled, then scored.  Errors: those of
  * mla_indexer_pool_step, and MLA_E_NULL for q or scores NULL; on MLA_E_HIP
  * the pool is marked invalid.
  */

@@ -4,7 +4,7 @@
 
 #include "../../include/mla.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cmath>
@@ -481,6 +481,11 @@ int mla_materialized_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32
 // ---- pooled top-k indexer ------------------------------------------------------
 namespace {
 constexpr int kPoolWindow = 4;
+constexpr int32_t kPoolReady = 1;   // mla_pool.valid: every covered window is pooled
+constexpr int32_t kPoolStale = 2;   // mla_pool.valid: a trim cut a window (a step must run before scores)
+// The fused step pools the tail windows on one workgroup per sequence: used
+// only while the tail is short, else the pooling kernel spreads it out.
+constexpr int64_t kFusedTailWindows = 16;
 int64_t pool_windows(int64_t T) { return (T + kPoolWindow - 1) / kPoolWindow; }
 
 // offsets: off[0] >= 0, non-decreasing, every Kv_b >= min_len
@@ -552,7 +557,7 @@ int mla_indexer_pool_step(mla_pool* pool, int32_t B, int32_t d, const void* keys
   for (int32_t b = 0; b < B; ++b) pool->lengths[b] = kv_offsets_host[b + 1] - kv_offsets_host[b];
   pool->batch = B;
   pool->d = d;
-  pool->valid = 1;
+  pool->valid = kPoolReady;
   if (incremental_out) *incremental_out = inc ? 1 : 0;
   return MLA_OK;
 }
@@ -562,7 +567,17 @@ int mla_indexer_pool_trim(mla_pool* pool, int32_t B, const int32_t* new_lengths)
   if (!pool->valid || B != pool->batch) return MLA_E_SHAPE;
   for (int32_t b = 0; b < B; ++b)
     if (new_lengths[b] < 0) return MLA_E_SHAPE;
-  for (int32_t b = 0; b < B; ++b) pool->lengths[b] = std::min(pool->lengths[b], new_lengths[b]);
+  // A cut inside a window leaves that window's pooled key holding rows past the
+  // cut: the pool may seed the next step (which recomputes from that window on)
+  // but must not be scored until a step has run.
+  bool stale = false;
+  for (int32_t b = 0; b < B; ++b) {
+    if (new_lengths[b] < pool->lengths[b]) {
+      if (new_lengths[b] % kPoolWindow != 0) stale = true;
+      pool->lengths[b] = new_lengths[b];
+    }
+  }
+  if (stale) pool->valid = kPoolStale;
   return MLA_OK;
 }
 
@@ -571,7 +586,7 @@ int mla_indexer_scores(const mla_pool* pool, int32_t B, const float* q, const in
   if (!pool || !pool->pooled || !pool->lengths || !q || !kv_offsets_dev || !scores) return MLA_E_NULL;
   int st = check_plain_offsets(B, kv_offsets_host, 1);
   if (st) return st;
-  if (!pool->valid || B != pool->batch) return MLA_E_SHAPE;
+  if (pool->valid != kPoolReady || B != pool->batch) return MLA_E_SHAPE;   // a trim cut a window: step first
   int64_t wmax = 0;
   for (int32_t b = 0; b < B; ++b) {
     const int64_t kv = (int64_t)kv_offsets_host[b + 1] - kv_offsets_host[b];
@@ -593,21 +608,22 @@ int mla_indexer_pool_step_scores(mla_pool* pool, int32_t B, int32_t d, const voi
   if (B > pool->batch_max) return MLA_E_SHAPE;
   if (d < 8 || d > 1024 || d % 8 != 0) return MLA_E_UNSUPPORTED;
   const bool inc = pool_guards_hold(pool, B, d, kv_offsets_host, S, padded);
-  int64_t wmax = 0;
+  int64_t wmax = 0, tail_max = 0;
   for (int32_t b = 0; b < B; ++b) {
     const int64_t kv = (int64_t)kv_offsets_host[b + 1] - kv_offsets_host[b];
     if (pool_windows(kv) > pool->capacity) return MLA_E_SHAPE;
     wmax = std::max(wmax, pool_windows(kv));
+    tail_max = std::max(tail_max, pool_windows(kv) - (kv - S) / kPoolWindow);
   }
   if ((int64_t)kv_offsets_host[B] * key_stride > INT64_MAX / 2) return MLA_E_SHAPE;
   pool->valid = 0;   // until the launches are known to be enqueued
   hipStream_t hs = (hipStream_t)stream;
-  if (inc) {   // one launch: the scoring pools the tail windows itself
+  if (inc && tail_max <= kFusedTailWindows) {   // one launch: the scoring pools the tail windows itself
     st = hip_status(indexer_scores(pool->pooled, pool->capacity, d, q, kv_offsets_dev, B, (int)wmax, scores,
                                    (const uint16_t*)keys, key_stride, S, hs));
-  } else {
-    st = hip_status(indexer_pool(keys, key_stride, kv_offsets_dev, B, d, S, true, (int)wmax, pool->pooled,
-                                 pool->capacity, hs));
+  } else {   // every window, or a long tail spread over the pooling kernel's workgroups; then score
+    st = hip_status(indexer_pool(keys, key_stride, kv_offsets_dev, B, d, S, !inc, (int)(inc ? tail_max : wmax),
+                                 pool->pooled, pool->capacity, hs));
     if (!st)
       st = hip_status(indexer_scores(pool->pooled, pool->capacity, d, q, kv_offsets_dev, B, (int)wmax, scores,
                                      nullptr, 0, 0, hs));
@@ -616,7 +632,7 @@ int mla_indexer_pool_step_scores(mla_pool* pool, int32_t B, int32_t d, const voi
   for (int32_t b = 0; b < B; ++b) pool->lengths[b] = kv_offsets_host[b + 1] - kv_offsets_host[b];
   pool->batch = B;
   pool->d = d;
-  pool->valid = 1;
+  pool->valid = kPoolReady;
   if (incremental_out) *incremental_out = inc ? 1 : 0;
   return MLA_OK;
 }

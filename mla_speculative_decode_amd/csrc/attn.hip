@@ -206,7 +206,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       // one latent row per instruction: uniform row address + constant lane offset
       const int key = wu + 4 * x;
       const int kr = SEL ? __builtin_amdgcn_readlane(sidx, key) : __builtin_amdgcn_readfirstlane(min(t0 + key, k1 - 1));
-      __builtin_amdgcn_global_load_lds(lbase + kr * DA + 8 * lane,
+      // 64-bit row offset: kr * DA passes 2^31 at 2^22 positions
+      __builtin_amdgcn_global_load_lds(lbase + (long long)kr * DA + 8 * lane,
                                        (__attribute__((address_space(3))) void*)(kdst + key * KRB), 16, 0, 0);
     } else if (x < NLW_K) {
       const int j = wu + 4 * x;
@@ -240,8 +241,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       const int C = tid + 256 * x;
       if (C < BN * RCH) {
         const int key = C / RCH, ch = C % RCH;
-        const unsigned kr = SEL ? (unsigned)__shfl(sidx, key, kWave) : (unsigned)min(t0 + key, k1 - 1);
-        rst[x] = ld16(rseq + kr * (unsigned)DR + 8 * ch);
+        const int kr = SEL ? __shfl(sidx, key, kWave) : min(t0 + key, k1 - 1);
+        rst[x] = ld16(rseq + (long long)kr * DR + 8 * ch);
       }
     }
   };

@@ -2,7 +2,7 @@
 // and the kernel files (attn.hip, gemm.hip, quant.hip, indexer.hip).  Not part of the public ABI.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 

@@ -299,9 +299,11 @@ def test_indexer_feeds_sparse_attention():
 def test_step_scores_equals_step_then_scores(d):
     # the fused call pools the tail inside the scoring launch; pooled keys and
     # scores must carry the same bits as the two separate calls, on the full
-    # path (first step, padded step) and on the incremental one
+    # path (first step, padded step) and on the incremental one; a step of 60
+    # (at most 16 tail windows: the fused launch, each tail wave taking its
+    # groups) and one of 70 (a longer tail: pooled by the pooling kernel first)
     lens0 = [37, 1000, 4, 1]   # the last: every window of the first steps is a tail window
-    steps = [(1, False), (3, False), (8, False), (2, True), (5, False), (4, False)]
+    steps = [(1, False), (3, False), (8, False), (2, True), (5, False), (60, False), (70, False), (4, False)]
     total = [n + sum(s for s, _ in steps) for n in lens0]
     x = synth.indexer_inputs(total, d, seed=90 + d)
     per = [x.keys[x.offsets[b]:x.offsets[b + 1]] for b in range(len(total))]

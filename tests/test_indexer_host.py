@@ -149,3 +149,28 @@ def test_errors_before_any_launch(lib):
     assert sel(2, 4, off, 16) == MLA_E_SHAPE          # 5 windows > capacity 4
     assert sel(0, 8, off, 16) == MLA_E_SHAPE
     assert lib.mla_indexer_select(2, None, 8, vp(off), dummy, 16, dummy, dummy, None) == MLA_E_NULL
+
+
+def test_scores_rejected_after_a_trim_inside_a_window(lib):
+    """A cut at 9 positions leaves window 2 (positions 8..11) holding the mean of
+    rejected rows: scoring before the next step must be refused before any
+    launch; a cut on a window boundary leaves every covered window exact."""
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)   # noqa: E731
+    dummy = ctypes.c_void_p(16)   # never dereferenced: the calls below fail validation first
+    p = HostPool(lib)
+    p.pretend_step([12], 16)
+    assert lib.mla_indexer_pool_trim(ctypes.byref(p.st), 1, vp(np.array([9], dtype=np.int32))) == MLA_OK
+    assert p.st.valid == 2 and list(p.lengths[:1]) == [9]
+    assert lib.mla_indexer_scores(ctypes.byref(p.st), 1, dummy, vp(_off([9])), dummy, dummy, None) == MLA_E_SHAPE
+    # the stale pool still seeds an incremental step (it recomputes from window 2 on)
+    assert _plan(lib, p, [12], 3, 16) == (MLA_OK, 1)
+    # a cut on a window boundary: the pool stays scoreable
+    q = HostPool(lib)
+    q.pretend_step([12], 16)
+    assert lib.mla_indexer_pool_trim(ctypes.byref(q.st), 1, vp(np.array([8], dtype=np.int32))) == MLA_OK
+    assert q.st.valid == 1
+    # (the call then gets past validation and would launch: only its validation is checked here)
+    r = HostPool(lib)
+    r.pretend_step([12], 16)
+    assert lib.mla_indexer_pool_trim(ctypes.byref(r.st), 1, vp(np.array([12], dtype=np.int32))) == MLA_OK
+    assert r.st.valid == 1     # nothing was cut

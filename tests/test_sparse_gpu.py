@@ -88,3 +88,59 @@ def test_rows_that_see_nothing_output_zero():
     assert np.all(got[:3] == 0)       # row i sees positions < 193 + i: rows 0..2 see none of 195, 197, 199
     assert np.all(np.any(got[3:] != 0, axis=-1))
     check_close(got.reshape(-1, v), ref, "bf16", "sparse late selection")
+
+
+def test_long_block_counts_visible_entries_by_search():
+    # L = 80 rows: a row's invisible entries are among the selection's last
+    # L - 1 = 79 > 64, so the kernel counts each row's visible entries by a
+    # binary search of the selection instead of from one register of its tail
+    case = ("long_block", 512, 128, 128, 64, 2, 80, [600, 300], "bf16")
+    name, r, n, v, rope, H, L, lens, dt = case
+    rng = np.random.default_rng(66)
+    sels = []
+    for k in lens:
+        old = rng.choice(k - L, size=90, replace=False)             # positions every row sees
+        new = rng.choice(np.arange(k - L, k), size=50, replace=False)   # among the block's own rows
+        sels.append(np.sort(np.concatenate([old, new, [k - 1]])))
+    x, q_lat, out, ref = _run(case, [np.unique(s) for s in sels])
+    check_close(host64(out).reshape(-1, v), ref, "bf16", "sparse long block")
+
+
+def test_positions_past_2_22_are_addressed():
+    # A cache of 2^22 + 192 positions (4.3 GB of latent rows): the latent and
+    # rope rows of selected positions past 2^22 lie beyond what a 32-bit
+    # element offset (position x 512) reaches.  The dense and selected-position
+    # kernels share the row-address code, so this covers both.  Only the
+    # selected rows hold data; the oracle runs on those rows packed densely, with
+    # the block's own rows kept last, which leaves every row's view unchanged
+    # (a row i sees position p iff p < Kv - L + i + 1).
+    r, rope, H, L, v = 512, 64, 2, 4, 128
+    Kv = (1 << 22) + 192
+    rng = np.random.default_rng(22)
+    old = np.sort(np.concatenate([rng.choice(1000, 20, replace=False),
+                                  (1 << 22) - 64 + rng.choice(64, 8, replace=False),
+                                  (1 << 22) + rng.choice(Kv - L - (1 << 22), 30, replace=False)]))
+    sel = np.concatenate([np.unique(old), np.arange(Kv - L, Kv)]).astype(np.int32)
+    k = sel.size
+    rows = synth.draw_like((k, r), 1.0, "bf16", seed=221)
+    ropes = synth.draw_like((k, rope), 1.0, "bf16", seed=222)
+    q_lat = synth.draw_like((1, L, H, r), math.sqrt(128 / r), "bf16", seed=223)
+    q_pe = synth.draw_like((1, L, H, rope), 1.0, "bf16", seed=224)
+    w_uv = synth.draw_like((H, r, v), 1.0 / math.sqrt(r), "bf16", seed=225)
+    scale = 1.0 / math.sqrt(128 + rope)
+    c_kv = torch.zeros((Kv, r), dtype=torch.bfloat16, device="cuda")
+    k_pe = torch.zeros((Kv, rope), dtype=torch.bfloat16, device="cuda")
+    idx = torch.from_numpy(sel.astype(np.int64)).cuda()
+    c_kv[idx] = dev(rows, "bf16")
+    k_pe[idx] = dev(ropes, "bf16")
+    soff = np.array([0, k], dtype=np.int32)
+    out = mla.absorbed_attention_sparse(dev(q_lat, "bf16"), dev(q_pe, "bf16"), c_kv, k_pe, dev(w_uv, "bf16"),
+                                        np.array([0, Kv], dtype=np.int32), torch.from_numpy(sel).cuda(), soff,
+                                        scale=scale)
+    torch.cuda.synchronize()
+    del c_kv, k_pe
+    m = k - L   # packed: the old selected rows first, then the block's own L rows
+    ref = sparse.sparse_latent_attention(q_lat, q_pe, rows, ropes, w_uv, np.array([0, k]), np.arange(k), soff,
+                                         L, scale)
+    assert m == int(np.sum(sel < Kv - L))
+    check_close(host64(out).reshape(-1, v), ref, "bf16", "sparse past 2^22")
