@@ -189,6 +189,32 @@ int mla_absorbed_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L
                            float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_absorbed_attention_noalloc -- mla_absorbed_attention for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels and the same result bits.  The split-KV partial
+ * results go to a static device array of MLA_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * that the library holds on every GPU it runs on until the process ends; its
+ * address is looked up on the first call on a device.  Nothing is allocated,
+ * freed or copied, and no library routine that allocates is called.
+ * Calls that would need more partial-result space than the array holds (the
+ * size mla_absorbed_workspace_size reports) return MLA_E_WORKSPACE before
+ * anything is enqueued: one-sequence verify steps fit (the 128-head, 8-row
+ * step over 8192 positions needs about 16 MiB); large batches may not.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other host threads) race and must be serialised by the
+ * caller.  Nothing in the array needs to start at zero; it keeps the last
+ * call's contents.  Other errors as for mla_absorbed_attention, plus MLA_E_HIP
+ * if the array's address cannot be looked up.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int mla_absorbed_attention_noalloc(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L,
+                                   const void* q_lat, const void* q_pe, const void* c_kv,
+                                   const void* k_pe, const int32_t* kv_offsets_host,
+                                   const int32_t* kv_offsets_dev, const void* w_uv, float scale,
+                                   float* out, void* stream);
+
+/*
  * mla_absorbed_splits / mla_absorbed_merge -- the two launches that make up
  * mla_absorbed_attention, exposed separately so that each kernel can be
  * timed or overlapped on its own.  mla_absorbed_splits runs the split-KV

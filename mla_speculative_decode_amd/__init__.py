@@ -22,7 +22,8 @@ from . import _lib
 from ._lib import Geom, MlaError, MLA_ABSORBED, MLA_MATERIALIZED, MLA_BF16, MLA_F32  # noqa: F401
 
 __all__ = ["Geom", "MlaError", "MLA_ABSORBED", "MLA_MATERIALIZED", "Offsets", "select_path",
-           "fold_query", "absorbed_workspace_size", "absorbed_attention", "absorbed_splits",
+           "fold_query", "absorbed_workspace_size", "absorbed_attention", "absorbed_attention_noalloc",
+           "absorbed_splits",
            "absorbed_merge", "materialize_kv",
            "materialized_workspace_size", "materialized_attention", "absorbed", "materialized",
            "library_path", "IndexerPool", "selection_offsets", "indexer_select"]
@@ -172,6 +173,25 @@ def absorbed_attention(q_lat, q_pe, c_kv, k_pe, w_uv, kv_offsets, scale=None, ou
         _ptr(_dev(c_kv, "c_kv")), _ptr(k_pe) if rope else None, offs.host_ptr(), offs.dev_ptr(),
         _ptr(_dev(w_uv, "w_uv")), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def absorbed_attention_noalloc(q_lat, q_pe, c_kv, k_pe, w_uv, kv_offsets: Offsets, out, scale: float, n: int = 0,
+                               stream=None):
+    """absorbed_attention without a workspace (mla_absorbed_attention_noalloc): the
+    split partials go to the library's static device array.  Every tensor,
+    ``out`` and the offsets included, is the caller's; nothing is allocated here."""
+    lib = _lib.load()
+    B, L, H, r = q_lat.shape
+    rope = q_pe.shape[-1] if q_pe is not None else 0
+    v = w_uv.shape[-1]
+    if not isinstance(kv_offsets, Offsets) or kv_offsets.B != B:
+        raise ValueError("kv_offsets must be an Offsets of the batch")
+    g = Geom(r, int(n), v, rope, H)
+    _lib.check("mla_absorbed_attention_noalloc", lib.mla_absorbed_attention_noalloc(
+        ctypes.byref(g), _dtype_code(q_lat), B, L, _ptr(_dev(q_lat, "q_lat")), _ptr(q_pe) if rope else None,
+        _ptr(_dev(c_kv, "c_kv")), _ptr(k_pe) if rope else None, kv_offsets.host_ptr(), kv_offsets.dev_ptr(),
+        _ptr(_dev(w_uv, "w_uv")), ctypes.c_float(scale), _ptr(_dev(out, "out")), _stream(stream)))
     return out
 
 

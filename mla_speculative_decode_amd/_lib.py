@@ -18,7 +18,8 @@ STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_UNSUPPORT
 
 # Every symbol include/mla.h declares.
 EXPORTS = ("mla_status_string", "mla_version", "mla_select_path", "mla_draft_cap", "mla_fold_query",
-           "mla_absorbed_workspace_size", "mla_absorbed_attention", "mla_absorbed_splits",
+           "mla_absorbed_workspace_size", "mla_absorbed_attention", "mla_absorbed_attention_noalloc",
+           "mla_absorbed_splits",
            "mla_absorbed_merge", "mla_materialize_kv",
            "mla_materialized_workspace_size", "mla_materialized_attention", "mla_quantize_latent_fp8",
            "mla_absorbed_attention_fp8", "mla_absorbed_splits_fp8", "mla_absorbed_sparse_workspace_size",
@@ -84,6 +85,9 @@ def load() -> ctypes.CDLL:
     lib.mla_absorbed_attention.restype = ctypes.c_int
     lib.mla_absorbed_attention.argtypes = [GP, ctypes.c_int, I32, I32, VP, VP, VP, VP, VP, VP, VP,
                                            ctypes.c_float, VP, VP, ctypes.c_size_t, VP]
+    lib.mla_absorbed_attention_noalloc.restype = ctypes.c_int
+    lib.mla_absorbed_attention_noalloc.argtypes = [GP, ctypes.c_int, I32, I32, VP, VP, VP, VP, VP, VP, VP,
+                                                   ctypes.c_float, VP, VP]
     lib.mla_absorbed_splits.restype = ctypes.c_int
     lib.mla_absorbed_splits.argtypes = [GP, ctypes.c_int, I32, I32, VP, VP, VP, VP, VP, VP, ctypes.c_float,
                                         VP, ctypes.c_size_t, VP]

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
 BENCH_LIB = os.path.join(HERE, "libmla_bench.so")   # timing loop used by bench.py only
-SOURCES = ["attn.hip", "gemm.hip", "quant.hip", "indexer.hip", "api.cpp"]
+SOURCES = ["attn.hip", "gemm.hip", "quant.hip", "indexer.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 # Per-file extra flags (none at present).
 EXTRA: dict = {}

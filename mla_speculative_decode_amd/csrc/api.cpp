@@ -259,6 +259,24 @@ int mla_absorbed_attention(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L
   return hip_status(combine_upproj(q, dt == MLA_BF16 ? kBF16 : kF32, out, s));
 }
 
+int mla_absorbed_attention_noalloc(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, const void* q_lat,
+                                   const void* q_pe, const void* c_kv, const void* k_pe,
+                                   const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, const void* w_uv,
+                                   float scale, float* out, void* stream) {
+  // size check first: the planned partials must fit the static scratch array
+  AbsorbedLaunch q{};
+  void* scratch = nullptr;
+  int st = absorbed_prepare(g, dt, B, L, q_lat, q_pe, c_kv, k_pe, kv_offsets_host, kv_offsets_dev, w_uv, out,
+                            reinterpret_cast<void*>(kAlign), kScratchBytes, scale, true, true, &q);
+  if (st) return st;
+  if ((st = hip_status(scratch_address(&scratch)))) return st;
+  q.ws_o = scratch;
+  q.ws_ml = (float*)((char*)scratch + align_up(q.plan.ws_o_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = absorbed_split_launch(q, dt, s))) return st;
+  return hip_status(combine_upproj(q, dt == MLA_BF16 ? kBF16 : kF32, out, s));
+}
+
 int mla_absorbed_splits(const mla_geom* g, mla_dtype dt, int32_t B, int32_t L, const void* q_lat,
                         const void* q_pe, const void* c_kv, const void* k_pe, const int32_t* kv_offsets_host,
                         const int32_t* kv_offsets_dev, float scale, void* workspace, size_t workspace_bytes,

@@ -69,6 +69,11 @@ hipError_t indexer_scores(float* pooled, int cap, int d, const float* q, const i
 hipError_t indexer_select(const float* scores, int cap, const int32_t* off_dev, int B, int budget,
                           const int32_t* sel_off_dev, int32_t* sel, hipStream_t st);
 
+// noalloc.hip: the device address of the static scratch array on the current
+// device (looked up once per device; thread-safe).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_address(void** out);
+
 // gemm.hip
 struct GemmArgs {
   const uint16_t* A; long long a_row, a_head;   // element strides of A rows / heads

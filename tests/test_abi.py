@@ -167,3 +167,22 @@ def test_binding_refuses_cpu_tensors():
     w = torch.zeros(2, 128, 512)
     with pytest.raises(ValueError):
         mla.fold_query(x, w, out=torch.zeros(1, 2, 512))
+
+
+def test_noalloc_rejects_partials_beyond_its_array(lib):
+    # the 32-sequence, 128-head batch plans about 83 MiB of partial results: more
+    # than the static array holds, refused before any device call
+    import numpy as np
+    from mla_speculative_decode_amd import synth
+    w = synth.WORKLOADS["dsv3_h128_b32_varlen_l8_bf16"]
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    lens = rng.integers(w.kv_range[0], w.kv_range[1], size=w.batch, endpoint=True)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    g = _lib.Geom(512, 128, 128, 64, 128)
+    dummy = ctypes.c_void_p(256)
+    vp = off.ctypes.data_as(ctypes.c_void_p)
+    st = lib.mla_absorbed_attention_noalloc(ctypes.byref(g), _lib.MLA_BF16, w.batch, 8, dummy, dummy, dummy, dummy,
+                                            vp, dummy, dummy, ctypes.c_float(0.1), dummy, None)
+    assert st == -4   # MLA_E_WORKSPACE
+    assert lib.mla_absorbed_attention_noalloc(None, _lib.MLA_BF16, 1, 8, dummy, dummy, dummy, dummy, vp, dummy,
+                                              dummy, ctypes.c_float(0.1), dummy, None) == -1
