@@ -11,8 +11,10 @@ float64 CPU oracle timed beside it.
 
 A step is one whole absorbed verify call over one batch of synthetic inputs
 already resident in device memory: mla_fold_query (q_lat = q_nope . W_UK),
-mla_absorbed_splits (split-KV latent attention) and mla_absorbed_merge
-(log-sum-exp merge and W_UV up-projection).  Default workload: DeepSeek-V3
+then mla_absorbed_attention: the split-KV latent attention pass and the merge
+(log-sum-exp combine and W_UV up-projection).  The split pass and the merge
+are also timed alone (mla_absorbed_splits / mla_absorbed_merge, launches back
+to back).  Default workload: DeepSeek-V3
 MLA geometry (r 512, n 128, v 128, rope 64), 128 heads, one sequence with a
 cache of 8192 positions, L = 8 query rows, bf16 storage, fp32 accumulation.
 
@@ -152,7 +154,7 @@ def main():
     cache_bytes = float(lens.sum() * ((w.r + w.rope) + 4)) if fp8 else float(lens.sum() * (w.r + w.rope) * 2)
     q_bytes = float(B * L * H * (w.r + w.rope) * 2)                       # q_lat + q_pe read by the split kernel
     weight_bytes = float(2 * H * w.n * w.r * 2)                            # W_UK + W_UV, bf16
-    us_step, us_fold, us_split, us_merge, us_evented, us_split_b2b, us_merge_b2b, us_fold_b2b = cold
+    us_step, us_fold, us_attn, _, us_evented, us_split_b2b, us_merge_b2b, us_fold_b2b = cold
     # roofline of the split kernel: its launches back to back (per-launch duration
     # without the dispatch gap that an event pair around one launch also measures)
     intensity = attn_flop / cache_bytes
@@ -190,11 +192,11 @@ def main():
         "latent_cache_GBps_split_merge": round(cache_bytes / ((us_split_b2b + us_merge_b2b) * 1e-6) / 1e9, 1),
         "step_GBps": round((cache_bytes + weight_bytes) / (us_step * 1e-6) / 1e9, 1),
         "flop_per_cache_byte": round(intensity, 1),
-        "per_launch_us": {"fold": round(us_fold, 3), "splits": round(us_split, 3), "merge": round(us_merge, 3),
+        "per_launch_us": {"fold": round(us_fold, 3), "attention": round(us_attn, 3),
                           "splits_back_to_back": round(us_split_b2b, 3),
                           "merge_back_to_back": round(us_merge_b2b, 3), "fold_back_to_back": round(us_fold_b2b, 3)},
         "warm_us_per_call": round(warm[0], 3),
-        "warm_per_launch_us": {"fold": round(warm[1], 3), "splits": round(warm[2], 3), "merge": round(warm[3], 3),
+        "warm_per_launch_us": {"fold": round(warm[1], 3), "attention": round(warm[2], 3),
                                "splits_back_to_back": round(warm[5], 3)},
         "roofline": roof,
         "peaks_measured": {k: round(v, 1) for k, v in peaks.items()},

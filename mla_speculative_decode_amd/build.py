@@ -19,10 +19,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
 BENCH_LIB = os.path.join(HERE, "libmla_bench.so")   # timing loop used by bench.py only
-SOURCES = ["attn.hip", "gemm.hip", "quant.hip", "indexer.hip", "noalloc.hip", "api.cpp"]
+SOURCES = ["attn.hip", "split_absorbed.hip", "gemm.hip", "quant.hip", "indexer.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
-# Per-file extra flags (none at present).
-EXTRA: dict = {}
+# Per-file extra flags.  The absorbed split kernel takes maxima of scores that
+# are never NaN, without the canonicalising moves IEEE NaN handling adds.
+EXTRA: dict = {"split_absorbed.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:

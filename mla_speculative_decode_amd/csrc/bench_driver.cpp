@@ -1,8 +1,9 @@
 // bench_driver.cpp -- native timing loop for bench.py (built as a separate
 // libmla_bench.so; not part of libmla's ABI).  Issues the absorbed verify
-// step -- mla_fold_query, mla_absorbed_splits, mla_absorbed_merge -- from C so
-// that host launch cost stays below the GPU time per step, and times it with
-// HIP events on the caller's stream.  Input sets are rotated so that a set is
+// step -- mla_fold_query, then mla_absorbed_attention (split pass and merge) --
+// from C so that host launch cost stays below the GPU time per step, and times
+// it with HIP events on the caller's stream.  The split pass and the merge are
+// also timed alone, through their separate entry points.  Input sets are rotated so that a set is
 // evicted from the caches before it is used again when enough sets are given.
 
 #include "../../include/mla.h"
@@ -28,16 +29,23 @@ int splits(const mla_geom* g, int B, int L, const Sets& s, int k, const int32_t*
                              ws, ws_bytes, st);
 }
 
+int attention(const mla_geom* g, int B, int L, const Sets& s, int k, const int32_t* off_h, const int32_t* off_d,
+              float scale, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (s.codes)
+    return mla_absorbed_attention_fp8(g, B, L, s.q_lat[k], s.q_pe[k], s.codes[k], s.scales[k], off_h, off_d,
+                                      s.w_uv[k], scale, s.out[k], ws, ws_bytes, st);
+  return mla_absorbed_attention(g, MLA_BF16, B, L, s.q_lat[k], s.q_pe[k], s.c_kv[k], s.k_pe[k], off_h, off_d,
+                                s.w_uv[k], scale, s.out[k], ws, ws_bytes, st);
+}
+
 int step(const mla_geom* g, int B, int L, const Sets& s, int k, const int32_t* off_h, const int32_t* off_d,
          float scale, void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev) {
   int rc;
   if (ev) hipEventRecord(ev[0], st);
   if ((rc = mla_fold_query(g, MLA_BF16, (int64_t)B * L, s.q_nope[k], s.w_uk[k], s.q_lat[k], st))) return rc;
   if (ev) hipEventRecord(ev[1], st);
-  if ((rc = splits(g, B, L, s, k, off_h, off_d, scale, ws, ws_bytes, st))) return rc;
+  if ((rc = attention(g, B, L, s, k, off_h, off_d, scale, ws, ws_bytes, st))) return rc;
   if (ev) hipEventRecord(ev[2], st);
-  if ((rc = mla_absorbed_merge(g, MLA_BF16, B, L, off_h, off_d, s.w_uv[k], s.out[k], ws, ws_bytes, st))) return rc;
-  if (ev) hipEventRecord(ev[3], st);
   return 0;
 }
 
@@ -46,8 +54,9 @@ int step(const mla_geom* g, int B, int L, const Sets& s, int k, const int32_t* o
 extern "C" {
 
 // res[0] us/step, plain back-to-back steps (events only around the run)
-// res[1] us fold, res[2] us splits, res[3] us merge (per-launch means, evented run;
-//        each includes the dispatch gap before its kernel)
+// res[1] us fold, res[2] us attention call (split pass + merge) (per-call means,
+//        evented run; each includes the dispatch gap before its first kernel)
+// res[3] unused (0)
 // res[4] us/step of the evented run
 // res[5] us per mla_absorbed_splits launch, launches back to back over the same
 //        rotation of input sets (events only around the run)
@@ -78,23 +87,24 @@ int mlab_absorbed_run(const mla_geom* g, int B, int L, int nsets, void* const* q
   hipEventElapsedTime(&ms, a, b);
   res[0] = 1e3 * ms / steps;
 
-  std::vector<hipEvent_t> ev((size_t)steps * 4);
+  std::vector<hipEvent_t> ev((size_t)steps * 3);
   for (auto& e : ev) hipEventCreate(&e);
   hipStreamSynchronize(st);
   for (int i = 0; i < steps; ++i)
-    if ((rc = step(g, B, L, s, i % nsets, off_h, off_d, scale, ws, ws_bytes, st, &ev[(size_t)i * 4]))) return rc;
+    if ((rc = step(g, B, L, s, i % nsets, off_h, off_d, scale, ws, ws_bytes, st, &ev[(size_t)i * 3]))) return rc;
   hipStreamSynchronize(st);
-  double t[3] = {0, 0, 0};
+  double t[2] = {0, 0};
   for (int i = 0; i < steps; ++i) {
-    for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < 2; ++j) {
       float x = 0.f;
-      hipEventElapsedTime(&x, ev[(size_t)i * 4 + j], ev[(size_t)i * 4 + j + 1]);
+      hipEventElapsedTime(&x, ev[(size_t)i * 3 + j], ev[(size_t)i * 3 + j + 1]);
       t[j] += x;
     }
   }
   float whole = 0.f;
-  hipEventElapsedTime(&whole, ev[0], ev[(size_t)(steps - 1) * 4 + 3]);
-  for (int j = 0; j < 3; ++j) res[1 + j] = 1e3 * t[j] / steps;
+  hipEventElapsedTime(&whole, ev[0], ev[(size_t)(steps - 1) * 3 + 2]);
+  for (int j = 0; j < 2; ++j) res[1 + j] = 1e3 * t[j] / steps;
+  res[3] = 0.0;
   res[4] = 1e3 * whole / steps;
 
   // split launches alone (q_lat of every set was written by the steps above)

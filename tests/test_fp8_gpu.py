@@ -1,8 +1,8 @@
 """GPU parity of the fp8 latent cache: mla_quantize_latent_fp8 bit-exact against
 the oracle's encoding (codes and power-of-two scales), and the absorbed
 attention over the fp8 cache against the oracle's attention over the
-dequantised cache -- and bit-identical to the bf16 path fed the dequantised
-cache, which it must equal since the tiles it expands hold exactly those values."""
+dequantised cache (as is the bf16 path fed that dequantised cache: the same
+values, summed by another kernel in another order)."""
 
 import math
 
@@ -94,10 +94,12 @@ def test_absorbed_fp8_matches_oracle_and_bf16_path(case):
                                    wuv, offs, scale=x.scale)
     again = mla.absorbed_attention_fp8(ql, qp, c_dev, s_dev, wuv, offs, scale=x.scale)
     torch.cuda.synchronize()
-    assert torch.equal(out8, out16), "fp8 path differs from the bf16 path on the dequantised cache"
     assert torch.equal(out8, again), "fp8 path is not deterministic"
     ref = oracle.latent_attention(q_lat, x.q_pe, ch, kh, x.w_uv, x.offsets, L, x.scale)
     check_close(host64(out8).reshape(-1, v), ref, "bf16", f"absorbed fp8 {name}")
+    # the bf16 path on the dequantised cache: the same values through kernels that
+    # sum in another order, so the same bar rather than the same bits
+    check_close(host64(out16).reshape(-1, v), ref, "bf16", f"absorbed bf16 on the dequantised cache {name}")
 
 
 def test_absorbed_fp8_full_size_sampled():
@@ -121,9 +123,9 @@ def test_absorbed_fp8_full_size_sampled():
     (("norope_sel8", 512, 128, 128, 0, 8, 4, [1000, 90, 400], "bf16"), (100, 90, 257)),
 ])
 def test_sparse_fp8_matches_oracle_and_sparse_bf16_path(case, budgets):
-    """Selected positions over the fp8 cache: bit-identical to the bf16 selected-position
-    path over the dequantised cache, and within the bf16 bar of the oracle's attention over
-    the selected positions of the dequantised cache."""
+    """Selected positions over the fp8 cache (and the bf16 selected-position path over the
+    dequantised cache): within the bf16 bar of the oracle's attention over the selected
+    positions of the dequantised cache."""
     from oracle import sparse
     name, r, n, v, rope, H, L, lens, dt = case
     x, codes, scales, ch, kh = _fp8_inputs(case)
@@ -143,7 +145,7 @@ def test_sparse_fp8_matches_oracle_and_sparse_bf16_path(case, budgets):
                                           soff, scale=x.scale)
     again = mla.absorbed_attention_sparse_fp8(ql, qp, c_dev, s_dev, wuv, offs, sel_d, soff, scale=x.scale)
     torch.cuda.synchronize()
-    assert torch.equal(out8, out16), "fp8 selected-position path differs from the bf16 one on the dequantised cache"
     assert torch.equal(out8, again)
     ref = sparse.sparse_latent_attention(q_lat, x.q_pe, ch, kh, x.w_uv, x.offsets, sel, soff, L, x.scale)
     check_close(host64(out8).reshape(-1, v), ref, "bf16", f"sparse fp8 {name}")
+    check_close(host64(out16).reshape(-1, v), ref, "bf16", f"sparse bf16 on the dequantised cache {name}")
