@@ -1070,6 +1070,124 @@ __global__ __launch_bounds__(256, 1) void merge_upproj_kernel(MergeUpArgs p) {
   }
 }
 
+// Absorbed route, bf16, few (sequence, row, head) triples: merge and
+// up-projection with one work item per (sequence b, query row i, head h, 64
+// output columns).  The four waves share the splits of the row (wave w takes
+// splits w, w + 4, ...; lane l latent columns 8l .. 8l + 7), the four partial
+// latents meet in LDS in a fixed order, and the merged latent (float32) is
+// multiplied by the W_UV tile [r x 64] on the VALU (thread t: the 8 columns
+// 8 (t % 8) .., latent indices 16 (t / 8) .. + 15, all 16 weight loads of 16
+// bytes issued before the first product; the 32 slices summed in LDS).  Items of
+// the same (b, h, column tile) are adjacent, so they share their W_UV tile in
+// one XCD's L2.  Used when the head-tile merge would leave most CUs idle.
+template <int R>
+__global__ __launch_bounds__(256) void merge_rows_kernel(MergeUpArgs p) {
+  static_assert(R / 8 == kWave, "one lane per 8 latent columns");
+  __shared__ __attribute__((aligned(16))) float part[4][R];
+  __shared__ __attribute__((aligned(16))) float ocol[32][64 + 4];
+  __shared__ float wstat[2];
+  static_assert(R == 32 * 16, "32 slices of 16 latent indices");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int item = xcd_item(blockIdx.x, p.n_items);
+  if (item >= p.n_items) return;
+  // item = ((b * H + h) * CT + ct) * L + i
+  const int i = item % p.L;
+  int tmp = item / p.L;
+  const int ct = tmp % p.CT;
+  tmp /= p.CT;
+  const int h = tmp % p.H, b = tmp / p.H;
+  const int rows_total = p.L * p.H;
+  const int prow = i * p.H + h;
+  int g0 = 0, S = p.S1;
+  if (p.B > 1) {
+    seq_splits(b, p.off, p.chunk, &g0, &S);
+    g0 = __builtin_amdgcn_readfirstlane(g0);
+    S = __builtin_amdgcn_readfirstlane(S);
+  }
+  const float* ml = p.ws_ml + ((long long)g0 * rows_total + prow) * 2;
+  // merge statistics: M = max_s m_s, den = sum_s 2^(m_s - M) l_s (wave 0, lane-strided)
+  if (w == 0) {
+    float mx = -INFINITY;
+    for (int s = lane; s < S; s += kWave) mx = fmaxf(mx, ml[(long long)s * rows_total * 2]);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+    float den = 0.f;
+    for (int s = lane; s < S; s += kWave) {
+      const float m = ml[(long long)s * rows_total * 2];
+      if (m != -INFINITY) den += __builtin_amdgcn_exp2f(m - mx) * ml[(long long)s * rows_total * 2 + 1];
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d, kWave);
+    if (lane == 0) { wstat[0] = mx; wstat[1] = den; }
+  }
+  __syncthreads();
+  const float M = wstat[0], inv = 1.f / wstat[1];
+  // this thread's W_UV slice, loaded while the partial sums stream in
+  const int cg = tid & 7, ks = tid >> 3;
+  const uint16_t* wsrc = p.w_uv + (long long)h * R * p.V + (long long)(16 * ks) * p.V + ct * 64 + 8 * cg;
+  u32x4 wv[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) wv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + (long long)k * p.V));
+  // this wave's splits: 8 latent columns per lane, float32
+  float o[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o[c] = 0.f;
+  const uint16_t* obase = p.ws_o + ((long long)g0 * rows_total + prow) * R + 8 * lane;
+  int s = w;
+  for (; s + 12 < S; s += 16) {   // four splits of this wave in flight
+    u32x4 v[4];
+    float wt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(obase + (long long)(s + 4 * j) * rows_total * R));
+      const float m = ml[(long long)(s + 4 * j) * rows_total * 2];
+      wt[j] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M) * inv;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        o[2 * c] = fmaf(wt[j], bf16_lo(v[j][c]), o[2 * c]);
+        o[2 * c + 1] = fmaf(wt[j], bf16_hi(v[j][c]), o[2 * c + 1]);
+      }
+  }
+  for (; s < S; s += 4) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(obase + (long long)s * rows_total * R));
+    const float m = ml[(long long)s * rows_total * 2];
+    const float wt = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M) * inv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      o[2 * c] = fmaf(wt, bf16_lo(v[c]), o[2 * c]);
+      o[2 * c + 1] = fmaf(wt, bf16_hi(v[c]), o[2 * c + 1]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) part[w][8 * lane + c] = o[c];
+  __syncthreads();
+  // merged latent row (waves' sums in a fixed order) times W_UV[h][:, 64 ct ..]
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int kk = 16 * ks + k;
+    const float x = (part[0][kk] + part[1][kk]) + (part[2][kk] + part[3][kk]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc[2 * c] = fmaf(x, bf16_lo(wv[k][c]), acc[2 * c]);
+      acc[2 * c + 1] = fmaf(x, bf16_hi(wv[k][c]), acc[2 * c + 1]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) ocol[ks][8 * cg + c] = acc[c];
+  __syncthreads();
+  if (tid < 64) {
+    float t = 0.f;
+    for (int k = 0; k < 32; ++k) t += ocol[k][tid];
+    p.out[(((long long)b * p.L + i) * p.H + h) * p.V + ct * 64 + tid] = t;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -1202,6 +1320,13 @@ hipError_t combine_upproj(const AbsorbedLaunch& q, mla_dtype_t dt, float* out, h
   const long long items = (long long)q.B * q.H * a.MTS * a.CT;
   if (items > INT32_MAX) return hipErrorInvalidValue;
   a.n_items = (int)items;
+  // few (sequence, head) pairs: one item per query row instead, the splits shared by the waves
+  const long long row_items = (long long)q.B * q.H * q.L * a.CT;
+  if (items < kNumCUs && row_items <= INT32_MAX) {
+    a.n_items = (int)row_items;
+    hipLaunchKernelGGL((merge_rows_kernel<512>), dim3(grid_xcd(a.n_items)), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   const int rpw = (std::min(16, q.L) + 3) / 4;   // query rows per wave
   const dim3 grid(grid_xcd(a.n_items));
   if (rpw == 1) hipLaunchKernelGGL((merge_upproj_kernel<512, 1>), grid, dim3(256), 0, st, a);

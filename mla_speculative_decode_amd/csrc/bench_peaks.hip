@@ -12,21 +12,25 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Each thread reads 8 independent 16-byte words per round (grid-stride), so
-// every wave keeps 8 KB of loads in flight.
+// Each workgroup streams one contiguous chunk of the buffer: per round its 256
+// threads read 8 x 4 KB with 16-byte non-temporal loads (8 KB in flight per
+// wave).  On MI355X this pattern reads about 7 TB/s; a grid-stride pattern
+// (each load a whole grid apart) or ordinary cached loads stay near 5.5-6.3.
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, long long n16,
                                                           uint32_t* __restrict__ sink) {
   u32x4 acc = {0u, 0u, 0u, 0u};
-  const long long stride = (long long)gridDim.x * 256;
-  long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
+  const long long per = (n16 + gridDim.x - 1) / gridDim.x;
+  const long long b0 = (long long)blockIdx.x * per;
+  const long long b1 = b0 + per < n16 ? b0 + per : n16;
+  long long i = b0 + threadIdx.x;
+  for (; i + 7 * 256 < b1; i += 8 * 256) {
     u32x4 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = p[i + j * stride];
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(p + i + j * 256);
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc ^= v[j];
   }
-  for (; i < n16; i += stride) acc ^= p[i];
+  for (; i < b1; i += 256) acc ^= p[i];
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) sink[0] = acc.x;   // keeps the loads live
 }
 
@@ -60,7 +64,7 @@ extern "C" {
 int mlab_stream_read(const void* buf, size_t bytes, void* sink, void* stream, int reps, double* gbps) {
   hipStream_t st = (hipStream_t)stream;
   const long long n16 = (long long)(bytes / 16);
-  const unsigned grid = 256 * 8;
+  const unsigned grid = 256 * 16;
   hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, st, (const u32x4*)buf, n16, (uint32_t*)sink);
   hipEvent_t a, b;
   hipEventCreate(&a);

@@ -10,6 +10,8 @@ namespace mla {
 
 enum mla_dtype_t { kF32 = 0, kBF16 = 1 };
 
+constexpr int kNumCUs = 256;   // MI355X compute units (launch planning)
+
 // Split-KV launch plan.  Sequence b is cut into ceil(Kv_b / chunk) splits;
 // work item = (split, head slot, row tile).
 struct SplitPlan {

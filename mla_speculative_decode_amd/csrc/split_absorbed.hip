@@ -33,6 +33,7 @@
 // (SEL) runs over a per-sequence list of cache positions instead of all of
 // them.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "mla_device.h"
@@ -57,6 +58,7 @@ struct SplitArgs {
   int B, L, H;
   int rows;                // L * H query rows per sequence
   int row_tiles;           // ceil(rows / 64)
+  int pf_ahead;            // tiles of L2 prefetch ahead of the tile being scored
   int chunk;               // positions per split (multiple of 64)
   int n_items;
   float sl2;               // scale * log2(e)
@@ -263,19 +265,24 @@ __global__ __launch_bounds__(256, 1) void absorbed_split_kernel(SplitArgs p) {
   const int pa_off = l32 * PRB + 16 * half;                              // + rb*32*PRB + 32 kc
   const int pw_off = l16 * PRB + (16 * w + 4 * lg) * 2;                  // + 16 rb * PRB
 
-  // This workgroup's share of the split's cache lines -> L2 (positions k0 + rt +
-  // row_tiles * j, one 4-byte load per 128-byte line into a dummy LDS slot): the
-  // row tiles of a split run on one XCD, so the later tile copies hit L2.  Issued
-  // once the first tile is in LDS; it completes before the second tile's barrier.
-  auto prefetch_split = [&]() {
+  // Cache lines of the split's positions [ta, tb) -> L2 ahead of their tile
+  // copies: this workgroup takes the positions p with (p - k0) % row_tiles == rt,
+  // one 4-byte load per 128-byte line into a dummy LDS slot (the row tiles of a
+  // split run on one XCD and share its L2).  Each tile fetches the lines of the
+  // tile pf_ahead tiles on; the first one fetches the tiles up to there.
+  const int kPfAhead = p.pf_ahead;
+  auto prefetch_range = [&](int ta, int tb) {
     if (SEL) return;
     constexpr int LPP = DA / 64 + (DR > 0 ? 1 : 0);   // 128-byte lines per position
-    const int cnt = max(0, (k1 - k0 - rt + p.row_tiles - 1) / p.row_tiles);
+    tb = min(tb, k1);
+    const int rel = ta - k0;
+    const int first = ta + ((rt - rel % p.row_tiles) + p.row_tiles) % p.row_tiles;
+    const int cnt = first < tb ? (tb - 1 - first) / p.row_tiles + 1 : 0;
     const int nl = cnt * LPP;
     for (int e0 = 0; e0 < nl; e0 += 256) {
       const int e = min(e0 + tid, nl - 1);
       const int j = e / LPP, ln = e - j * LPP;
-      const long long pos = p0 + k0 + rt + (long long)p.row_tiles * j;
+      const long long pos = p0 + first + (long long)p.row_tiles * j;
       const uint16_t* src = ln < DA / 64 ? p.c_kv + pos * DA + 64 * ln : p.k_pe + pos * DR;
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)pfd, 4, 0, 0);
     }
@@ -327,7 +334,10 @@ __global__ __launch_bounds__(256, 1) void absorbed_split_kernel(SplitArgs p) {
     // the split's first tile on the first pass: the query fragments come from
     // buf1 during its scores, so the next tile's copy waits for PV
     const bool first = t0 == k0 && !rerun;
-    if (first) prefetch_split();
+    if (!rerun) {
+      if (first) prefetch_range(t0 + BN, t0 + (kPfAhead + 1) * BN);
+      else prefetch_range(t0 + kPfAhead * BN, t0 + (kPfAhead + 1) * BN);
+    }
 
     // ---- scores: S^T [16 keys x 64 rows] -----------------------------------
     f32x4 acc[4];
@@ -571,6 +581,10 @@ SplitArgs split_args(const AbsorbedLaunch& q) {
   a.B = q.B; a.L = q.L; a.H = q.H; a.rows = q.L * q.H;
   a.row_tiles = q.plan.row_tiles; a.chunk = q.plan.chunk; a.n_items = q.plan.n_items;
   a.sl2 = q.scale * 1.4426950408889634f;
+  // L2 prefetch window: an XCD's 32 CUs run 32 / row_tiles distinct splits at a
+  // time, each with pf_ahead tiles (72 KB) in flight; about row_tiles tiles keeps
+  // that near 2 MB of its 4 MB L2
+  a.pf_ahead = std::min(16, std::max(2, a.row_tiles));
   return a;
 }
 unsigned grid_of(int n_items) { return (unsigned)(((n_items + kXcds - 1) / kXcds) * kXcds); }
