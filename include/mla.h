@@ -405,6 +405,47 @@ int mla_indexer_pool_step(mla_pool* pool, int32_t B, int32_t d, const void* keys
                           const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, int32_t S, int32_t padded,
                           int32_t* incremental_out, void* stream);
 
+/*
+ * Fixed-capacity update lists ("Over 107 tok/s Qwen3.8-Flash-Next on M3 Ultra",
+ * section "Why doing eight rows can beat doing two", and its algorithm for
+ * constructing a fixed-capacity update list), read for this indexer: a block is
+ * a window of four positions and its destination the window's own slot in the
+ * pooled array.  An incremental step's real updates are the windows from
+ * floor((Kv - S) / 4) on, a count that varies with S and the alignment; padding
+ * them to a fixed capacity P (8 or 16) with complete windows whose rows did not
+ * change (each written back with the bits it already holds, at a destination not
+ * otherwise in the list) gives every step one launch shape.
+ *
+ * mla_indexer_update_list -- the list for one sequence (host only): real updates
+ * are the windows first .. windows - 1, the complete windows 0 .. complete - 1
+ * (0 <= first <= complete <= windows), S the tokens of the step, target P in
+ * {8, 16}.  The capacity is max(1, windows - first), raised to P when S <= 16,
+ * that count is at most P and at least P windows are complete; an empty update
+ * lists window 0 if complete, else window windows - 1 (-1 for an empty cache).
+ * The real updates come first, in order, then fillers (complete windows in
+ * increasing order whose destinations are not yet listed) up to the capacity.
+ * list_out (host) must hold max(1, windows - first, target) entries; the list
+ * length is *capacity_out.  Errors: MLA_E_NULL, MLA_E_SHAPE (bounds or target).
+ */
+int mla_indexer_update_list(int32_t first, int32_t windows, int32_t complete, int32_t S, int32_t target,
+                            int32_t* list_out, int32_t* capacity_out);
+
+/*
+ * mla_indexer_pool_step_fixed -- mla_indexer_pool_step with the same arguments
+ * plus target (8 or 16).  When the four guards hold, S <= 16, and every sequence
+ * has at most target real updates and at least target complete windows, one
+ * launch of fixed shape (target windows per sequence: the list of
+ * mla_indexer_update_list) pools them, and *capacity_out = target; otherwise the
+ * ordinary step runs (*capacity_out = 0).  Either way the pooled keys, lengths
+ * and state after the call are those of mla_indexer_pool_step, bit for bit.
+ * capacity_out and incremental_out may be NULL.  Errors: those of
+ * mla_indexer_pool_step, and MLA_E_SHAPE for a target other than 8 or 16.
+ */
+int mla_indexer_pool_step_fixed(mla_pool* pool, int32_t B, int32_t d, const void* keys, int64_t key_stride,
+                                const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, int32_t S,
+                                int32_t padded, int32_t target, int32_t* incremental_out, int32_t* capacity_out,
+                                void* stream);
+
 /* A speculative rejection cut sequence b's cache back to new_lengths[b]
  * positions (host array [B]): the pool forgets what it covered past the cut
  * (host only; the next step recomputes from the window holding the cut).

@@ -26,7 +26,7 @@ __all__ = ["Geom", "MlaError", "MLA_ABSORBED", "MLA_MATERIALIZED", "Offsets", "s
            "absorbed_splits",
            "absorbed_merge", "materialize_kv",
            "materialized_workspace_size", "materialized_attention", "absorbed", "materialized",
-           "library_path", "IndexerPool", "selection_offsets", "indexer_select"]
+           "library_path", "IndexerPool", "selection_offsets", "indexer_select", "update_list"]
 
 
 def library_path() -> str:
@@ -404,6 +404,21 @@ class IndexerPool:
             keys.stride(0), offs.host_ptr(), offs.dev_ptr(), S, int(padded), ctypes.byref(inc), _stream(stream)))
         return bool(inc.value)
 
+    def step_fixed(self, keys, kv_offsets, S: int, target: int = 8, padded: bool = False, stream=None):
+        """step() with a fixed-capacity update list (mla_indexer_pool_step_fixed):
+        returns (incremental, capacity), capacity = target when the fixed launch
+        shape ran and 0 when the ordinary step did."""
+        torch = _torch()
+        if keys.dtype != torch.bfloat16 or keys.dim() != 2 or keys.stride(1) != 1 or keys.shape[1] < self.d:
+            raise ValueError("keys must be a bf16 [T, >= d] device tensor with unit column stride")
+        offs = kv_offsets if isinstance(kv_offsets, Offsets) else Offsets(kv_offsets, keys.device)
+        inc, cap = ctypes.c_int32(), ctypes.c_int32()
+        _lib.check("mla_indexer_pool_step_fixed", _lib.load().mla_indexer_pool_step_fixed(
+            ctypes.byref(self.state), offs.B, self.d, ctypes.c_void_p(_dev(keys, "keys").data_ptr()),
+            keys.stride(0), offs.host_ptr(), offs.dev_ptr(), S, int(padded), int(target), ctypes.byref(inc),
+            ctypes.byref(cap), _stream(stream)))
+        return bool(inc.value), int(cap.value)
+
     def step_scores(self, keys, kv_offsets, S: int, q, out=None, padded: bool = False, stream=None):
         """step() then scores() in one call (tail pooling fused into the scoring
         launch when the guards hold); returns (scores, incremental)."""
@@ -440,6 +455,16 @@ class IndexerPool:
             ctypes.byref(self.state), offs.B, _ptr(_dev(q, "q")), offs.host_ptr(), offs.dev_ptr(), _ptr(out),
             _stream(stream)))
         return out
+
+
+def update_list(first: int, windows: int, complete: int, S: int, target: int = 8) -> list[int]:
+    """The fixed-capacity update list of one sequence (mla_indexer_update_list)."""
+    lib = _lib.load()
+    buf = (ctypes.c_int32 * max(1, windows - first, target))()
+    cap = ctypes.c_int32()
+    _lib.check("mla_indexer_update_list", lib.mla_indexer_update_list(int(first), int(windows), int(complete), int(S),
+                                                                      int(target), buf, ctypes.byref(cap)))
+    return [int(buf[i]) for i in range(cap.value)]
 
 
 def selection_offsets(kv_offsets, budget: int, device=None) -> Offsets:

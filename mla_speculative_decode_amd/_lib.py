@@ -24,7 +24,7 @@ EXPORTS = ("mla_status_string", "mla_version", "mla_select_path", "mla_draft_cap
            "mla_materialized_workspace_size", "mla_materialized_attention", "mla_quantize_latent_fp8",
            "mla_absorbed_attention_fp8", "mla_absorbed_splits_fp8", "mla_absorbed_sparse_workspace_size",
            "mla_absorbed_attention_sparse", "mla_absorbed_attention_sparse_fp8", "mla_indexer_pool_init", "mla_indexer_pool_plan",
-           "mla_indexer_pool_step", "mla_indexer_pool_trim", "mla_indexer_scores", "mla_indexer_pool_step_scores",
+           "mla_indexer_pool_step", "mla_indexer_update_list", "mla_indexer_pool_step_fixed", "mla_indexer_pool_trim", "mla_indexer_scores", "mla_indexer_pool_step_scores",
            "mla_indexer_selection_offsets", "mla_indexer_select")
 
 
@@ -120,6 +120,8 @@ def load() -> ctypes.CDLL:
     for name, args in (("mla_indexer_pool_init", [PP, VP, I32, I32, VP]),
                        ("mla_indexer_pool_plan", [PP, I32, I32, VP, I32, I32, I32P]),
                        ("mla_indexer_pool_step", [PP, I32, I32, VP, I64, VP, VP, I32, I32, I32P, VP]),
+                       ("mla_indexer_update_list", [I32, I32, I32, I32, I32, VP, I32P]),
+                       ("mla_indexer_pool_step_fixed", [PP, I32, I32, VP, I64, VP, VP, I32, I32, I32, I32P, I32P, VP]),
                        ("mla_indexer_pool_trim", [PP, I32, VP]),
                        ("mla_indexer_scores", [PP, I32, VP, VP, VP, VP, VP]),
                        ("mla_indexer_pool_step_scores", [PP, I32, I32, VP, I64, VP, VP, I32, I32, VP, VP, I32P, VP]),

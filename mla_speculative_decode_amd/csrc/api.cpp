@@ -504,6 +504,7 @@ constexpr int32_t kPoolStale = 2;   // mla_pool.valid: a trim cut a window (a st
 // The fused step pools the tail windows on one workgroup per sequence: used
 // only while the tail is short, else the pooling kernel spreads it out.
 constexpr int64_t kFusedTailWindows = 16;
+constexpr int32_t kFixedMaxTokens = 16;   // fixed-capacity update lists: steps of at most this many tokens
 int64_t pool_windows(int64_t T) { return (T + kPoolWindow - 1) / kPoolWindow; }
 
 // offsets: off[0] >= 0, non-decreasing, every Kv_b >= min_len
@@ -577,6 +578,64 @@ int mla_indexer_pool_step(mla_pool* pool, int32_t B, int32_t d, const void* keys
   pool->d = d;
   pool->valid = kPoolReady;
   if (incremental_out) *incremental_out = inc ? 1 : 0;
+  return MLA_OK;
+}
+
+int mla_indexer_update_list(int32_t first, int32_t windows, int32_t complete, int32_t S, int32_t target,
+                            int32_t* list_out, int32_t* capacity_out) {
+  if (!list_out || !capacity_out) return MLA_E_NULL;
+  if (first < 0 || windows < first || complete < 0 || complete > windows || first > complete || S < 0 ||
+      !(target == 8 || target == 16))
+    return MLA_E_SHAPE;
+  const int32_t nd = windows - first;                  // real updates: windows first .. windows - 1
+  int32_t C = std::max<int32_t>(1, nd);
+  int32_t n = 0;
+  for (int32_t w = first; w < windows; ++w) list_out[n++] = w;
+  if (S <= kFixedMaxTokens && C <= target && complete >= target) C = target;
+  if (n == 0) list_out[n++] = complete > 0 ? 0 : windows - 1;   // an empty update still has one row
+  // fillers: the complete windows in order whose destinations are not in the list
+  for (int32_t w = 0; w < complete && n < C; ++w) {
+    bool used = false;
+    for (int32_t k = 0; k < n; ++k) used = used || list_out[k] == w;
+    if (!used) list_out[n++] = w;
+  }
+  *capacity_out = C;
+  return n == C ? MLA_OK : MLA_E_SHAPE;
+}
+
+int mla_indexer_pool_step_fixed(mla_pool* pool, int32_t B, int32_t d, const void* keys, int64_t key_stride,
+                                const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev, int32_t S,
+                                int32_t padded, int32_t target, int32_t* incremental_out, int32_t* capacity_out,
+                                void* stream) {
+  if (!pool || !pool->pooled || !pool->lengths || !keys || !kv_offsets_dev) return MLA_E_NULL;
+  if (S < 1 || key_stride < d || !(target == 8 || target == 16)) return MLA_E_SHAPE;
+  int st = check_plain_offsets(B, kv_offsets_host, S);
+  if (st) return st;
+  if (B > pool->batch_max) return MLA_E_SHAPE;
+  if (d < 8 || d > 1024 || d % 8 != 0) return MLA_E_UNSUPPORTED;
+  bool fixed = pool_guards_hold(pool, B, d, kv_offsets_host, S, padded) && S <= kFixedMaxTokens;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t kv = (int64_t)kv_offsets_host[b + 1] - kv_offsets_host[b];
+    if (pool_windows(kv) > pool->capacity) return MLA_E_SHAPE;
+    const int64_t nd = pool_windows(kv) - (kv - S) / kPoolWindow;
+    fixed = fixed && nd <= target && kv / kPoolWindow >= target;
+  }
+  if ((int64_t)kv_offsets_host[B] * key_stride > INT64_MAX / 2) return MLA_E_SHAPE;
+  if (!fixed) {   // the ordinary step, with its own shape
+    if (capacity_out) *capacity_out = 0;
+    return mla_indexer_pool_step(pool, B, d, keys, key_stride, kv_offsets_host, kv_offsets_dev, S, padded,
+                                 incremental_out, stream);
+  }
+  pool->valid = 0;   // until the launch is known to be enqueued
+  st = hip_status(indexer_pool_fixed(keys, key_stride, kv_offsets_dev, B, d, S, target, pool->pooled,
+                                     pool->capacity, (hipStream_t)stream));
+  if (st) return st;
+  for (int32_t b = 0; b < B; ++b) pool->lengths[b] = kv_offsets_host[b + 1] - kv_offsets_host[b];
+  pool->batch = B;
+  pool->d = d;
+  pool->valid = kPoolReady;
+  if (incremental_out) *incremental_out = 1;
+  if (capacity_out) *capacity_out = target;
   return MLA_OK;
 }
 

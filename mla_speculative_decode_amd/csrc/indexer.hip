@@ -33,21 +33,12 @@ constexpr int kWin = 4;
 __device__ __forceinline__ int windows_of(int T) { return (T + kWin - 1) / kWin; }
 
 // ---- pooling ----------------------------------------------------------------
-// grid (ceil(wmax / 4), B), 256 threads: one wave per window, lane l takes the
-// 8-column chunks l, l + 64, ...
-__global__ __launch_bounds__(256) void pool_windows_kernel(const uint16_t* __restrict__ keys, long long ld,
-                                                           const int32_t* __restrict__ off, int d, int S, int full,
-                                                           float* __restrict__ pooled, int cap) {
+// One wave pools window w of a sequence (rows src .. src + (n - 1) ld, n <= 4)
+// into dst: lane l takes the 8-column chunks l, l + 64, ...; rows are summed in
+// position order in float32, then divided by n (correctly rounded).
+__device__ __forceinline__ void pool_one_window(const uint16_t* __restrict__ src, long long ld, int n, int d,
+                                                float* __restrict__ dst) {
   const int lane = threadIdx.x & 63;
-  const int b = blockIdx.y;
-  const int o0 = off[b];
-  const int Kv = off[b + 1] - o0;
-  const int first = full ? 0 : (Kv - S) / kWin;
-  const int w = first + blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= windows_of(Kv)) return;
-  const int n = min(kWin, Kv - kWin * w);
-  const uint16_t* src = keys + ((long long)o0 + kWin * w) * ld;
-  float* dst = pooled + ((long long)b * cap + w) * d;
   const float fn = (float)n;
   for (int c = lane; c < d / 8; c += kWave) {
     float acc[8];
@@ -74,6 +65,42 @@ __global__ __launch_bounds__(256) void pool_windows_kernel(const uint16_t* __res
     *reinterpret_cast<f32x4*>(dst + 8 * c) = m0;
     *reinterpret_cast<f32x4*>(dst + 8 * c + 4) = m1;
   }
+}
+
+// grid (ceil(wmax / 4), B), 256 threads: one wave per window
+__global__ __launch_bounds__(256) void pool_windows_kernel(const uint16_t* __restrict__ keys, long long ld,
+                                                           const int32_t* __restrict__ off, int d, int S, int full,
+                                                           float* __restrict__ pooled, int cap) {
+  const int b = blockIdx.y;
+  const int o0 = off[b];
+  const int Kv = off[b + 1] - o0;
+  const int first = full ? 0 : (Kv - S) / kWin;
+  const int w = first + blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= windows_of(Kv)) return;
+  pool_one_window(keys + ((long long)o0 + kWin * w) * ld, ld, min(kWin, Kv - kWin * w), d,
+                  pooled + ((long long)b * cap + w) * d);
+}
+
+// The fixed-capacity update list ("Over 107 tok/s Qwen3.8-Flash-Next on M3
+// Ultra", section "Why doing eight rows can beat doing two"): every sequence
+// recomputes exactly P windows, its real updates (windows first .. W - 1, the
+// old tail window and the new ones) followed by fillers, the complete windows
+// 0, 1, ... (all before first, so their destinations are distinct from the real
+// ones), whose rows have not changed: a filler writes back the bits already
+// stored.  The host launches this only where every sequence has at most P real
+// updates and at least P complete windows.  grid (P / 4, B): one wave per slot.
+__global__ __launch_bounds__(256) void pool_fixed_kernel(const uint16_t* __restrict__ keys, long long ld,
+                                                         const int32_t* __restrict__ off, int d, int S,
+                                                         float* __restrict__ pooled, int cap) {
+  const int b = blockIdx.y;
+  const int o0 = off[b];
+  const int Kv = off[b + 1] - o0;
+  const int first = (Kv - S) / kWin;
+  const int nd = windows_of(Kv) - first;              // real updates
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);  // slot of the list
+  const int w = c < nd ? first + c : c - nd;
+  pool_one_window(keys + ((long long)o0 + kWin * w) * ld, ld, min(kWin, Kv - kWin * w), d,
+                  pooled + ((long long)b * cap + w) * d);
 }
 
 // ---- scores -----------------------------------------------------------------
@@ -613,6 +640,13 @@ hipError_t indexer_pool(const void* keys, long long ld, const int32_t* off_dev, 
   if (wmax <= 0) return hipSuccess;
   hipLaunchKernelGGL(pool_windows_kernel, dim3((wmax + 3) / 4, B), dim3(256), 0, st, (const uint16_t*)keys, ld,
                      off_dev, d, S, full ? 1 : 0, pooled, cap);
+  return hipGetLastError();
+}
+
+hipError_t indexer_pool_fixed(const void* keys, long long ld, const int32_t* off_dev, int B, int d, int S, int P,
+                              float* pooled, int cap, hipStream_t st) {
+  hipLaunchKernelGGL(pool_fixed_kernel, dim3(P / 4, B), dim3(256), 0, st, (const uint16_t*)keys, ld, off_dev, d, S,
+                     pooled, cap);
   return hipGetLastError();
 }
 

@@ -64,6 +64,9 @@ hipError_t quantize_latent_fp8(long long T, int r, int rope, const void* c_kv, c
 // indexer.hip
 hipError_t indexer_pool(const void* keys, long long ld, const int32_t* off_dev, int B, int d, int S, bool full,
                         int wmax, float* pooled, int cap, hipStream_t st);
+// the fixed-capacity step: P (8 or 16) windows per sequence, real updates then fillers
+hipError_t indexer_pool_fixed(const void* keys, long long ld, const int32_t* off_dev, int B, int d, int S, int P,
+                              float* pooled, int cap, hipStream_t st);
 // tail_keys != null: the launch also pools the windows from floor((Kv - tail_S) / 4)
 // on from those key rows (row stride tail_ld elements) before scoring them
 hipError_t indexer_scores(float* pooled, int cap, int d, const float* q, const int32_t* off_dev, int B, int wmax,

@@ -36,6 +36,9 @@ hipError_t quantize_latent_fp8(long long, int, int, const void*, const void*, vo
 hipError_t indexer_pool(const void*, long long, const int32_t*, int, int, int, bool, int, float*, int, hipStream_t) {
   return reached();
 }
+hipError_t indexer_pool_fixed(const void*, long long, const int32_t*, int, int, int, int, float*, int, hipStream_t) {
+  return reached();
+}
 hipError_t indexer_scores(float*, int, int, const float*, const int32_t*, int, int, float*, const uint16_t*, long long,
                           int, hipStream_t) {
   return reached();

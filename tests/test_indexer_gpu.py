@@ -327,3 +327,45 @@ def test_step_scores_equals_step_then_scores(d):
             assert torch.equal(a.pooled[b, :W], f.pooled[b, :W]), (i, b)
             assert torch.equal(sa[b, :W], sf[b, :W]), (i, b)
     assert inc_f   # the last steps ran the fused tail
+
+
+def test_fixed_capacity_step_equals_the_ordinary_step():
+    # the same steps through step() and step_fixed(): the pooled keys carry the
+    # same bits after every step (the fillers write back what they hold); steps
+    # that qualify run the fixed shape (capacity 8 or 16), the others (a first
+    # step, a step of 20 tokens, a sequence with too few complete windows) the
+    # ordinary one
+    d = 64
+    lens0 = [70, 300, 36]
+    steps = [(1, 8), (3, 8), (5, 16), (2, 8), (8, 8), (16, 16), (20, 8), (4, 8), (7, 16)]
+    total = [n + sum(s for s, _ in steps) for n in lens0]
+    x = synth.indexer_inputs(total, d, seed=131)
+    per = [x.keys[x.offsets[b]:x.offsets[b + 1]] for b in range(len(total))]
+    cap = ix.n_windows(max(total))
+    a = mla.IndexerPool(capacity=cap, batch_max=3, d=d)
+    f = mla.IndexerPool(capacity=cap, batch_max=3, d=d)
+    lens = list(lens0)
+    keys, off = _packed([p[:n] for p, n in zip(per, lens)])
+    a.step(keys, off, S=1)            # no pool yet: every window
+    inc, c = f.step_fixed(keys, off, S=1)
+    assert not inc and c == 0
+    seen = set()
+    for S, target in steps:
+        lens = [n + S for n in lens]
+        keys, off = _packed([p[:n] for p, n in zip(per, lens)])
+        inc_a = a.step(keys, off, S=S)
+        inc_f, c = f.step_fixed(keys, off, S=S, target=target)
+        torch.cuda.synchronize()
+        assert inc_a and inc_f
+        qualifies = S <= 16 and all((n // 4) >= target and ix.n_windows(n) - (n - S) // 4 <= target for n in lens)
+        assert c == (target if qualifies else 0), (S, target, lens)
+        seen.add(c)
+        for b, T in enumerate(lens):
+            W = ix.n_windows(T)
+            assert torch.equal(a.pooled[b, :W], f.pooled[b, :W]), (S, b)
+    assert seen == {0, 8, 16}
+    # and against the oracle's pooling of every window
+    for b, T in enumerate(lens):
+        ref = ix.pool_all(per[b][:T], T)
+        got = f.pooled[b, :ix.n_windows(T)].double().cpu().numpy()
+        assert np.max(np.abs(got - ref)) <= 1e-5

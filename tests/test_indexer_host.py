@@ -174,3 +174,43 @@ def test_scores_rejected_after_a_trim_inside_a_window(lib):
     r.pretend_step([12], 16)
     assert lib.mla_indexer_pool_trim(ctypes.byref(r.st), 1, vp(np.array([12], dtype=np.int32))) == MLA_OK
     assert r.st.valid == 1     # nothing was cut
+
+
+def test_update_list_matches_the_oracle(lib):
+    """mla_indexer_update_list against the oracle's fixed-capacity list, over every
+    small (first, windows, complete, S, target) and the page's example."""
+    import mla_speculative_decode_amd as mla
+    assert mla.update_list(6, 8, 8, 5, 8) == [6, 7, 0, 1, 2, 3, 4, 5]      # two real updates, six fillers
+    n = 0
+    for windows in range(0, 21):
+        for complete in range(max(0, windows - 1), windows + 1):          # at most the tail window is partial
+            for first in range(0, complete + 1):
+                for S in (0, 1, 5, 16, 17):
+                    for target in (8, 16):
+                        want, C = ix.update_list(list(range(first, windows)), list(range(complete)), target, S,
+                                                 fallback=windows - 1)
+                        assert mla.update_list(first, windows, complete, S, target) == want, \
+                            (first, windows, complete, S, target)
+                        n += 1
+    assert n > 1000
+    out = np.zeros(16, dtype=np.int32)
+    cap = ctypes.c_int32()
+    vp = out.ctypes.data_as(ctypes.c_void_p)
+    assert lib.mla_indexer_update_list(5, 4, 4, 1, 8, vp, ctypes.byref(cap)) == MLA_E_SHAPE   # first > windows
+    assert lib.mla_indexer_update_list(0, 4, 5, 1, 8, vp, ctypes.byref(cap)) == MLA_E_SHAPE   # complete > windows
+    assert lib.mla_indexer_update_list(0, 4, 4, 1, 12, vp, ctypes.byref(cap)) == MLA_E_SHAPE  # target not 8 / 16
+    assert lib.mla_indexer_update_list(0, 4, 4, 1, 8, None, ctypes.byref(cap)) == MLA_E_NULL
+
+
+def test_fixed_step_validates_before_any_launch(lib):
+    p = HostPool(lib, capacity=8, batch_max=2)
+    off = _off([20, 12])
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)   # noqa: E731
+    dummy = ctypes.c_void_p(16)
+    step = lambda S, target, d=16, o=off: lib.mla_indexer_pool_step_fixed(   # noqa: E731
+        ctypes.byref(p.st), 2, d, dummy, d, vp(o), dummy, S, 0, target, None, None, None)
+    assert step(1, 12) == MLA_E_SHAPE
+    assert step(0, 8) == MLA_E_SHAPE
+    assert step(1, 8, d=12) == MLA_E_UNSUPPORTED
+    assert step(1, 8, o=_off([40, 12])) == MLA_E_SHAPE    # 10 windows > capacity 8
+    assert p.st.valid == 0

@@ -175,3 +175,73 @@ def test_selection_invariants_random():
             tied_out = rest[s[rest // 4] == worst_in]
             if tied_out.size:
                 assert tied_in.max() < tied_out.min()
+
+
+# ---- fixed-capacity update list ------------------------------------------------
+
+def _golden_lists():
+    from tests.conftest import golden_path
+    out = []
+    with open(golden_path("pad8_update_list.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            name, delta, complete, P, m, want, C = [x.strip() for x in line.split("|")]
+            ints = lambda s: [] if s == "-" else [int(v) for v in s.split(",")]   # noqa: E731
+            out.append((name, ints(delta), ints(complete), int(P), int(m), ints(want), int(C)))
+    return out
+
+
+@pytest.mark.parametrize("case", _golden_lists(), ids=lambda c: c[0])
+def test_update_list_matches_the_page(case):
+    name, delta, complete, P, m, want, C = case
+    assert ix.update_list(delta, complete, P, m) == (want, C)
+
+
+def test_update_list_without_anything_uses_the_fallback():
+    assert ix.update_list([], [], 8, 1, fallback="fb") == (["fb"], 1)
+    # padding off: the list keeps its size
+    assert ix.update_list([5, 6], list(range(10)), 8, 2, padding=False) == ([5, 6], 2)
+
+
+def test_update_list_invariants_on_random_steps():
+    rng = np.random.default_rng(17)
+    for _ in range(2000):
+        T = int(rng.integers(1, 200))
+        S = int(rng.integers(1, min(T, 24) + 1))
+        P = int(rng.choice([8, 16]))
+        delta = list(range((T - S) // ix.WINDOW, ix.n_windows(T)))
+        complete = list(range(T // ix.WINDOW))
+        U, C = ix.update_list(delta, complete, P, S)
+        assert len(U) == C and U[:len(delta)] == delta            # every real update is kept, first
+        assert len(set(U)) == len(U)                               # distinct destinations
+        assert all(u in complete for u in U[len(delta):])          # fillers are complete windows
+        padded = S <= 16 and len(delta) <= P and len(complete) >= P
+        assert C == (P if padded else len(delta))
+
+
+def test_fixed_step_pools_like_the_variable_step():
+    # the same step sequence through pool_step and pool_step_fixed: identical
+    # pooled keys (the fillers' writes reproduce the stored values exactly)
+    rng = np.random.default_rng(23)
+    d = 6
+    total = 160
+    keys = rng.standard_normal((total, d))
+    a, f = ix.PoolState(), ix.PoolState()
+    T = 40
+    ix.pool_step(a, [keys[:T]], T)
+    ix.pool_step_fixed(f, [keys[:T]], T)
+    padded_steps = 0
+    for S in [1, 3, 5, 2, 8, 4, 7, 1, 16, 6, 9, 20]:
+        T += S
+        stored = {w: v.copy() for w, v in f.pooled[0].items()}
+        ia = ix.pool_step(a, [keys[:T]], S)
+        inc, lists = ix.pool_step_fixed(f, [keys[:T]], S)
+        assert ia and inc
+        U = lists[0]
+        padded_steps += len(U) == 8
+        for w in U:
+            if w < (T - S) // ix.WINDOW:      # a filler: its value is unchanged, bit for bit
+                assert np.array_equal(f.pooled[0][w], stored[w])
+        assert np.array_equal(ix.pooled_array(a, 0), ix.pooled_array(f, 0))
+    assert padded_steps == 11                  # every step pads but the last: 20 tokens > 16 keep their 6 windows
