@@ -46,28 +46,130 @@ sys.path.insert(0, ROOT)
 
 METRIC = "absorbed MLA verify µs/call + latent-cache HBM GB/s (L=8, Kv=8192, H=128)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)   # FLOP per byte where the two bounds meet
 HEADLINE = "dsv3_h128_kv8192_l8_bf16"
 
-# HBM traffic of the split kernel per launch, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
-# (KiB per dispatch) scaled by what the same counters read for a plain 256 MiB device copy
-# (FETCH x2.00, WRITE x1.00); valid only for the kernel source it was measured on.
-SPLIT_TRAFFIC = {"source_sha256": "6108d7700fddea7e7762fcc7e8937d3c5a43beb1f3e56433f3cfbcce49b01c0b",
-                 "fetch_kib": 9373.6, "write_kib": 16512.0, "fetch_factor": 2.0, "write_factor": 1.0}
-KERNEL_SOURCES = ("mla_speculative_decode_amd/csrc/attn.hip", "mla_speculative_decode_amd/csrc/mla_device.h")
+# HBM traffic of the split kernel per launch comes from a committed counter
+# summary (rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by the same
+# counter on a plain device copy of known size), written by --write-counters
+# and keyed to a hash of the kernel's sources: when the kernel has changed since
+# the counters were taken the field is reported as null.
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "absorbed_split_dsv3_h128_kv8192_l8_counters.md")
+KERNEL_SOURCES = ("mla_speculative_decode_amd/csrc/split_absorbed.hip", "mla_speculative_decode_amd/csrc/mla_device.h",
+                  "mla_speculative_decode_amd/csrc/internal.h")
+SPLIT_KERNEL = "absorbed_split_kernel"
 
 
-def split_traffic_bytes():
+def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    t = SPLIT_TRAFFIC
-    if h.hexdigest() != t["source_sha256"]:
-        return None   # the kernel changed since the counters were taken
-    return round(1024 * (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]))
+    return h.hexdigest()
+
+
+def read_counter_summary(path=COUNTERS_FILE):
+    """The key: value lines of the fenced 'traffic' block of a counter summary, or None."""
+    if not os.path.exists(path):
+        return None
+    out, inside = {}, False
+    with open(path) as f:
+        for line in f:
+            if line.strip() == "```traffic":
+                inside = True
+            elif inside and line.strip() == "```":
+                break
+            elif inside and ":" in line:
+                k, v = line.split(":", 1)
+                out[k.strip()] = v.strip()
+    return out or None
+
+
+def split_traffic_bytes():
+    """HBM bytes per split-kernel launch from the counter summary, if it was taken
+    on the kernel source that is built now; else None."""
+    t = read_counter_summary()
+    if not t or t.get("source_sha256") != kernel_source_hash():
+        return None
+    return round(1024 * (float(t["fetch_kib"]) * float(t["fetch_factor"]) +
+                         float(t["write_kib"]) * float(t["write_factor"])))
+
+
+def write_counter_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_mib, out_path, commands):
+    """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every kernel in the
+    rocprofv3 counter CSVs, the calibration factors from the plain-copy runs
+    (--copy-calibration MIB: MIB read and written per copy), and the fenced
+    block bench.py reads, keyed to the hash of the kernel sources built now."""
+    import csv
+    from collections import defaultdict
+
+    def means(path, counter):
+        acc = defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+    fetch, write = means(fetch_csv, "FETCH_SIZE"), means(write_csv, "WRITE_SIZE")
+    nbytes = cal_mib * 1048576.0
+    cf = max(v[0] for v in means(cal_fetch_csv, "FETCH_SIZE").values())
+    cw = max(v[0] for v in means(cal_write_csv, "WRITE_SIZE").values())
+    f_fac, w_fac = nbytes / (cf * 1024), nbytes / (cw * 1024)
+    split = [k for k in fetch if SPLIT_KERNEL in k]
+    if not split:
+        raise SystemExit(f"no {SPLIT_KERNEL} dispatch in {fetch_csv}")
+    k = split[0]
+    lines = ["# Counters: absorbed verify step, DeepSeek-V3 geometry, 128 heads, Kv 8192, L 8, bf16", "",
+             "Commands (repository root, on the GPU; one counter per run):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", f"Calibration: the largest kernel of a plain {cal_mib} MiB device copy reads FETCH_SIZE x "
+                  f"{f_fac:.3f} and WRITE_SIZE x {w_fac:.3f} of the bytes it moves.", "",
+              "| kernel | dispatches | FETCH_SIZE KiB | fetched (scaled) | WRITE_SIZE KiB | written (scaled) |",
+              "|---|---:|---:|---:|---:|---:|"]
+    for name in sorted(fetch, key=lambda n: -fetch[n][0]):
+        if name not in write:
+            continue
+        fk, n = fetch[name]
+        wk = write[name][0]
+        short = name.split("(")[0][:70]
+        lines.append(f"| {short} | {n} | {fk:,.1f} | {fk * 1024 * f_fac / 1e6:.2f} MB | {wk:,.1f} | "
+                     f"{wk * 1024 * w_fac / 1e6:.2f} MB |")
+    fk, wk = fetch[k][0], write[k][0]
+    lines += ["", "Machine-readable summary of the split kernel (read by bench.py; valid only while the",
+              "kernel sources hash to source_sha256):", "", "```traffic",
+              f"source_sha256: {kernel_source_hash()}", f"kernel: {k.split('(')[0]}",
+              f"fetch_kib: {fk:.1f}", f"write_kib: {wk:.1f}", f"fetch_factor: {f_fac:.4f}",
+              f"write_factor: {w_fac:.4f}", "```", ""]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out_path}: {SPLIT_KERNEL} fetch {fk:.1f} KiB x {f_fac:.3f}, write {wk:.1f} KiB x {w_fac:.3f}")
+
+
+def host_info():
+    """CPU model and software versions of the machine the line was measured on."""
+    import platform
+    import torch
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(path):
+            with open(path) as f:
+                rocm = f.read().strip()
+            break
+    gpu = torch.cuda.get_device_name(0) if torch.cuda.is_available() else None
+    return {"cpu_model": cpu, "host_cpus": os.cpu_count(), "rocm": rocm, "torch": torch.__version__,
+            "hip": getattr(torch.version, "hip", None), "gpu": gpu}
 
 
 def parse():
@@ -94,6 +196,10 @@ def parse():
     ap.add_argument("--indexer", action="store_true",
                     help="time the pooled top-k indexer step (tail vs full pooling, scores, selection) and the "
                          "sparse attention it feeds, caches of 8192 and 131072")
+    ap.add_argument("--write-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="write the split kernel's counter summary from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                         "CSVs of the benchmark and of --copy-calibration runs (no GPU needed)")
+    ap.add_argument("--calibration-mib", type=int, default=256, help="MiB copied by the calibration runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -101,6 +207,20 @@ def parse():
 
 def main():
     args = parse()
+    if args.write_counters:
+        cmds = ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o fetch -- python bench.py --steps 20 "
+                "--warmup 5 --no-cpu-baseline",
+                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out> -o write -- python bench.py --steps 20 "
+                "--warmup 5 --no-cpu-baseline",
+                f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o cfetch -- python bench.py "
+                f"--copy-calibration {args.calibration_mib}",
+                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out> -o cwrite -- python bench.py "
+                f"--copy-calibration {args.calibration_mib}",
+                "python bench.py --write-counters <out>/fetch_counter_collection.csv "
+                "<out>/write_counter_collection.csv <out>/cfetch_counter_collection.csv "
+                "<out>/cwrite_counter_collection.csv"]
+        write_counter_summary(*args.write_counters, args.calibration_mib, COUNTERS_FILE, cmds)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
@@ -154,21 +274,36 @@ def main():
     cache_bytes = float(lens.sum() * ((w.r + w.rope) + 4)) if fp8 else float(lens.sum() * (w.r + w.rope) * 2)
     q_bytes = float(B * L * H * (w.r + w.rope) * 2)                       # q_lat + q_pe read by the split kernel
     weight_bytes = float(2 * H * w.n * w.r * 2)                            # W_UK + W_UV, bf16
+    # split partials written by the split pass and read back by the merge (bf16 sums + (max, sum) floats)
+    geom = mla.Geom(w.r, w.n, w.v, w.rope, H)
+    ws_bytes = mla.absorbed_workspace_size(geom, _lib.MLA_BF16, L, mla.Offsets(x.offsets.astype(np.int32), "cpu"))
+    partial_bytes = float(ws_bytes)
     us_step, us_fold, us_attn, _, us_evented, us_split_b2b, us_merge_b2b, us_fold_b2b = cold
     # roofline of the split kernel: its launches back to back (per-launch duration
     # without the dispatch gap that an event pair around one launch also measures)
     intensity = attn_flop / cache_bytes
-    if intensity >= RIDGE:
+    # fp8 cache: the scores run on fp8 MFMA, PV on bf16, so the contraction's peak
+    # is the rate at which both halves would finish at their own peaks
+    score_flop = 2.0 * (w.r + w.rope) * vis
+    mfma_peak = (attn_flop / (score_flop / PEAK_FP8_TFLOPS + (attn_flop - score_flop) / PEAK_BF16_TFLOPS)
+                 if fp8 else PEAK_BF16_TFLOPS)
+    if intensity >= mfma_peak * 1e12 / (PEAK_HBM_GBPS * 1e9):
         achieved = attn_flop / (us_split_b2b * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(mfma_peak, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / mfma_peak, 4)}
     else:
         achieved = (cache_bytes + q_bytes) / (us_split_b2b * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4)}
-    measured = peaks["mfma_bf16_TFLOPs"] if roof["bound"] == "mfma" else peaks["hbm_read_GBps"]
-    roof = {"kernel": "attn_bf16_kernel (mla_absorbed_splits)", **roof, "duration_us": round(us_split_b2b, 3),
-            "traffic": split_traffic_bytes() if (w.name == HEADLINE and not fp8) else None,
+    measured = (peaks["mfma_bf16_TFLOPs"] * mfma_peak / PEAK_BF16_TFLOPS if roof["bound"] == "mfma"
+                else peaks["hbm_read_GBps"])
+    traffic = split_traffic_bytes() if (w.name == HEADLINE and not fp8) else None
+    alg_bytes = cache_bytes + q_bytes + partial_bytes
+    roof = {"kernel": ("absorbed_split_f8_kernel (mla_absorbed_splits_fp8)" if fp8 else
+                       "absorbed_split_kernel (mla_absorbed_splits)"), **roof, "duration_us": round(us_split_b2b, 3),
+            "traffic": traffic,
+            "traffic_over_algorithmic": round(traffic / alg_bytes, 3) if traffic else None,
+            "algorithmic_bytes": round(alg_bytes),
             "measured_peak": round(measured, 1), "frac_measured": round(roof["achieved"] / measured, 4)}
 
     line = {
@@ -198,7 +333,9 @@ def main():
         "warm_us_per_call": round(warm[0], 3),
         "warm_per_launch_us": {"fold": round(warm[1], 3), "attention": round(warm[2], 3),
                                "splits_back_to_back": round(warm[5], 3)},
+        "partial_sum_bytes_per_step": round(partial_bytes),
         "roofline": roof,
+        "host": host_info(),
         "peaks_measured": {k: round(v, 1) for k, v in peaks.items()},
         "wall_s": round(wall, 3),
     }

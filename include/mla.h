@@ -277,8 +277,17 @@ int mla_quantize_latent_fp8(const mla_geom* g, int64_t T, const void* c_kv, cons
 /*
  * mla_absorbed_attention_fp8 -- mla_absorbed_attention (bf16 queries q_lat, q_pe
  * and W_UV; float32 out) with the latent cache given as (codes, scales) from
- * mla_quantize_latent_fp8 instead of c_kv and k_pe: the split kernel reads the
- * codes (half the bytes of the bf16 cache) and expands each tile to bf16 in LDS.
+ * mla_quantize_latent_fp8 instead of c_kv and k_pe.  The scores run on the fp8
+ * matrix cores: each query row is quantised in the kernel to E4M3 with one
+ * power-of-two scale per 32-wide block of its key dimension (blocks 32j ..
+ * 32j + 31 of q_lat, then of q_pe), the smallest scale 2^e with every
+ * |q| <= 448 x 2^e (e in [-126, 127]; 2^0 for an all-zero block), codes the
+ * nearest E4M3 value of q / 2^e, ties to even; the score of a cached position is
+ * the exact product of those values with its dequantised key, summed in float32.
+ * The values are the dequantised cache, exact in bf16.  So the result is the
+ * absorbed attention of the block-quantised queries over the dequantised cache
+ * (within the bf16 path's rounding), and, against the unquantised inputs, within
+ * the error that E4M3 rounding of queries and cache implies.
  * Workspace: mla_absorbed_workspace_size with MLA_BF16.  mla_absorbed_splits_fp8
  * is its split pass alone; mla_absorbed_merge (MLA_BF16) completes it.
  * Supported: r = 512, rope in {0, 64}; otherwise MLA_E_UNSUPPORTED.  Other
@@ -321,9 +330,10 @@ int mla_absorbed_attention_sparse(const mla_geom* g, int32_t B, int32_t L, const
 /*
  * mla_absorbed_attention_sparse_fp8 -- mla_absorbed_attention_sparse over the
  * fp8 form of the latent cache (codes and scales of mla_quantize_latent_fp8
- * instead of c_kv and k_pe): the attention over the selected positions of the
- * dequantised cache, and bit-identical to mla_absorbed_attention_sparse given
- * that dequantised cache in bf16.  Workspace: mla_absorbed_sparse_workspace_size.
+ * instead of c_kv and k_pe), with the scores on the fp8 matrix cores exactly as
+ * in mla_absorbed_attention_fp8 (block-quantised queries): the attention of
+ * those queries over the selected positions of the dequantised cache.
+ * Workspace: mla_absorbed_sparse_workspace_size.
  * Errors as mla_absorbed_attention_sparse (MLA_E_NULL also for codes or scales).
  */
 int mla_absorbed_attention_sparse_fp8(const mla_geom* g, int32_t B, int32_t L, const void* q_lat, const void* q_pe,

@@ -1199,44 +1199,6 @@ static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t absorbed_attn_fp8(const AbsorbedLaunch& q, const void* codes, const float* scales, hipStream_t st) {
-  AttnArgs a{};
-  a.qa = (const uint16_t*)q.q_lat; a.qb = (const uint16_t*)q.q_pe;
-  a.c8 = (const uint8_t*)codes; a.c8s = scales;
-  a.off = q.off_dev; a.off0 = q.off0; a.kv1 = q.kv1; a.ws_o = q.ws_o; a.ws_ml = q.ws_ml;
-  a.B = q.B; a.L = q.L; a.H = q.H; a.hpr = q.H; a.rows_slot = q.L * q.H; a.head_slots = 1;
-  a.row_tiles = q.plan.row_tiles; a.chunk = q.plan.chunk; a.n_items = q.plan.n_items;
-  a.rows_total = q.L * q.H; a.sl2 = q.scale * 1.4426950408889634f;
-  if (q.r != 512) return hipErrorInvalidValue;
-  const dim3 grid(grid_xcd(a.n_items));
-  switch (q.rope) {
-    case 0:  hipLaunchKernelGGL((attn_bf16_kernel<512, 0, 512, true, true>), grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((attn_bf16_kernel<512, 64, 512, true, true>), grid, dim3(256), 0, st, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t absorbed_attn_sparse_fp8(const AbsorbedLaunch& q, const void* codes, const float* scales,
-                                    const int32_t* sel, const int32_t* koff_dev, int koff0, int kvt1, hipStream_t st) {
-  AttnArgs a{};
-  a.qa = (const uint16_t*)q.q_lat; a.qb = (const uint16_t*)q.q_pe;
-  a.c8 = (const uint8_t*)codes; a.c8s = scales;
-  a.sel = sel; a.koff = koff_dev; a.koff0 = koff0; a.kvt1 = kvt1;
-  a.off = q.off_dev; a.off0 = q.off0; a.kv1 = q.kv1; a.ws_o = q.ws_o; a.ws_ml = q.ws_ml;
-  a.B = q.B; a.L = q.L; a.H = q.H; a.hpr = q.H; a.rows_slot = q.L * q.H; a.head_slots = 1;
-  a.row_tiles = q.plan.row_tiles; a.chunk = q.plan.chunk; a.n_items = q.plan.n_items;
-  a.rows_total = q.L * q.H; a.sl2 = q.scale * 1.4426950408889634f;
-  if (q.r != 512) return hipErrorInvalidValue;
-  const dim3 grid(grid_xcd(a.n_items));
-  switch (q.rope) {
-    case 0:  hipLaunchKernelGGL((attn_bf16_kernel<512, 0, 512, true, true, true>), grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((attn_bf16_kernel<512, 64, 512, true, true, true>), grid, dim3(256), 0, st, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 hipError_t materialized_attn_bf16(const MaterializedLaunch& q, hipStream_t st) {
   AttnArgs a{};
   const int D = q.n + q.rope;

@@ -34,6 +34,33 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 16x16x128 fp8 (E4M3) with block scales, gfx950: A lane l holds row l%16, and
+// its 32 bytes are k = 16*(l/16) + j (bytes j < 16) and k = 64 + 16*(l/16) + j - 16
+// (bytes j >= 16); B lane l holds col l%16, same k; C as mfma16.  The E8M0
+// scale of A lane l (2^(s - 127)) multiplies row l%16 over k block l/16 (k in
+// 32*(l/16) .. +31), and likewise for B and its column.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+// SEL_B picks the byte of scale_b that holds B's scale (so four scales can share
+// a register).
+template <int SEL_B = 0>
+__device__ __forceinline__ f32x4 mfma16_f8(i32x8 a, i32x8 b, f32x4 c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, SEL_B, scale_b);
+}
+
+// ---- E4M3 ------------------------------------------------------------------
+// Smallest k with a <= 448 x 2^k for a float a >= 0 (exact, from the bits):
+// a = f x 2^E with f in [1, 2); 448 = 1.75 x 2^8.
+__device__ __forceinline__ int e4m3_scale_exponent(float a) {
+  if (!(a > 0.f)) return 0;
+  const uint32_t b = __float_as_uint(a);
+  const int e = (int)((b >> 23) & 0xffu);
+  if (e == 0) return -126;                            // float32 subnormal: the floor of the range
+  const int E = e - 127;
+  const int k = E - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return k < -126 ? -126 : (k > 127 ? 127 : k);
+}
+
+
 // ---- bfloat16 ----------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

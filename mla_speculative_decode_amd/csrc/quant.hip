@@ -16,18 +16,6 @@
 
 namespace mla {
 
-// Smallest k with a <= 448 x 2^k for a float a >= 0 (exact, from the bits):
-// a = f x 2^E with f in [1, 2); 448 = 1.75 x 2^8.
-__device__ __forceinline__ int e4m3_scale_exponent(float a) {
-  if (!(a > 0.f)) return 0;
-  const uint32_t b = __float_as_uint(a);
-  const int e = (int)((b >> 23) & 0xffu);
-  if (e == 0) return -126;                            // float32 subnormal: the floor of the range
-  const int E = e - 127;
-  const int k = E - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
-  return k < -126 ? -126 : (k > 127 ? 127 : k);
-}
-
 // Nearest E4M3 code of y (|y| <= 448 after saturation), ties to the even code.
 __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   const float a = fminf(fabsf(y), 448.f);

@@ -48,6 +48,8 @@ struct SplitArgs {
   const uint16_t* q_pe;    // [B, L, H, DR]
   const uint16_t* c_kv;    // [T, 512]
   const uint16_t* k_pe;    // [T, DR]
+  const uint8_t* c8;       // fp8 form: E4M3 codes [T, 512 + DR] (latent | rope)
+  const float* s8;         // fp8 form: one power-of-two scale per position [T]
   const int32_t* sel;      // SEL: selected positions per sequence (packed by off; relative, increasing)
   const int32_t* koff;     // SEL: cache offsets [B+1] (off then indexes the selection)
   int koff0, kvt1;         // SEL, B == 1: koff[0] and koff[1] - koff[0]
@@ -59,6 +61,7 @@ struct SplitArgs {
   int rows;                // L * H query rows per sequence
   int row_tiles;           // ceil(rows / 64)
   int pf_ahead;            // tiles of L2 prefetch ahead of the tile being scored
+  int pf_lines;            // fp8 form: 128-byte lines of a tile each row tile prefetches
   int chunk;               // positions per split (multiple of 64)
   int n_items;
   float sl2;               // scale * log2(e)
@@ -569,6 +572,566 @@ __global__ __launch_bounds__(256, 1) void absorbed_split_kernel(SplitArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// The same split over the fp8 form of the latent cache (E4M3 codes of each
+// position's row [c_kv | k_pe] with one power-of-two scale per position).
+//
+//   scores  on the scaled fp8 MFMA (16x16x128): the query block is quantised
+//           once, in the prologue, to E4M3 with one power-of-two scale per
+//           (row, 32-wide block of the key dimension), the smallest with every
+//           |q| <= 448 x scale; the keys' codes come straight from LDS, with
+//           their position's scale as the A-side block scale.  The rope part
+//           is one more k step whose upper half is zero.
+//   softmax as above; each weight is then multiplied by its key's scale (a
+//           power of two, so bf16(P) x 2^k is exact) before it goes to LDS, and
+//           the row sums add the unscaled weights.
+//   PV      bf16 MFMAs as above; a V^T fragment is one transposed byte read
+//           (ds_read_b64_tr_b8: 8 keys of one column) widened to bf16 (codes are
+//           exact in bf16), the scale having gone into P.
+// LDS: two tile buffers of 64 code rows (row stride DW + 16 bytes: the 16 rows a
+// score fragment reads fall in distinct 16-byte bank groups) followed by the
+// tile's 64 scales, then P; the epilogue stages O in the two buffers.
+// ---------------------------------------------------------------------------
+namespace {
+// x -> E4M3 codes of x / s (nearest, ties to even; |x| <= 448 s), four per word
+__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d, float s) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  s16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, a, b, s, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, s, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+// Direct global -> LDS copy (BYTES = 16 or 4 per lane) written as inline asm:
+// the compiler then does not track it, so it adds no waits of its own before
+// LDS reads of other buffers.  The kernel waits for its copies itself (vmcnt)
+// before the barrier that publishes a tile.  M0 is written here and used by
+// nothing else in the kernel.
+template <int BYTES>
+__device__ __forceinline__ void dma(const void* gsrc, const void* lds_dst) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_dst);
+  if (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(m) : "memory");
+}
+// mfma16_f8 with B's scale in byte `sel` of scale_b (sel known once the caller's
+// loop is unrolled)
+__device__ __forceinline__ f32x4 mfma16_f8_sel(i32x8 a, i32x8 b, f32x4 c, int scale_a, int scale_b, int sel) {
+  switch (sel) {
+    case 0: return mfma16_f8<0>(a, b, c, scale_a, scale_b);
+    case 1: return mfma16_f8<1>(a, b, c, scale_a, scale_b);
+    case 2: return mfma16_f8<2>(a, b, c, scale_a, scale_b);
+    default: return mfma16_f8<3>(a, b, c, scale_a, scale_b);
+  }
+}
+// two E4M3 codes (bytes 2 HI, 2 HI + 1 of w) -> packed bf16 (exact)
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ float absmax8(u32x4 v, float m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
+  return m;
+}
+// 8 bf16 values -> 8 E4M3 codes of x / s
+__device__ __forceinline__ u32x2 e4m3x8(u32x4 v, float s) {
+  return u32x2{cvt4_e4m3(bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1]), s),
+               cvt4_e4m3(bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3]), s)};
+}
+}  // namespace
+
+template <int DR, bool SEL>
+__global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) {
+  constexpr int DA = 512, DV = 512;
+  constexpr int BM = 32, BN = 64;
+  constexpr int NRB = BM / 16;            // 16-row blocks of the score layout
+  constexpr int DW = DA + DR;             // codes per cached position
+  constexpr int ROPE = BN * DA;           // rope region: 64 rows of DR bytes after the latent rows
+  constexpr int SOFF = ROPE + BN * DR;    // the tile's 64 scales follow
+  constexpr int BUF = SOFF + BN * 4;
+  constexpr int NLI = BN / 2;             // latent copy instructions per tile (two rows each)
+  constexpr int NRI = BN * DR / 1024;     // rope copy instructions per tile (16 rows each)
+  constexpr int KS = DA / 128;            // 128-wide score k steps over the latent part
+  constexpr int NQ = KS + (DR > 0 ? 1 : 0);
+  constexpr int PRB = 9 * 16;             // P row: 64 keys (8 chunks) + one chunk holding 4 exchange floats
+  constexpr int CPW = DV / 4;             // value columns per wave
+  constexpr int NCB = CPW / 32;           // 32-column MFMA blocks per wave
+  constexpr int NLW = NLI / 4;            // latent copies per wave per tile
+  constexpr int NC = NLW / 2;             // ... of which these go with the scores, the rest with PV
+  constexpr int SROW = DV * 2 + 8;        // epilogue staging row (bf16; 8 mod 256 bytes)
+  constexpr int QBYTES = NRB * KS * kWave * 32 + (DR > 0 ? NRB * kWave * 16 : 0);   // query codes
+  static_assert(DR == 0 || DR == 64, "rope width 0 or 64");
+  static_assert(BUF % 16 == 0, "layout");
+  static_assert(QBYTES <= BUF && NRB * NQ * kWave * 4 <= BM * PRB, "query codes fit in a tile buffer, their scales in pl");
+  static_assert(BM * SROW <= BUF, "O staging fits in a tile buffer");
+  static_assert(2 * BUF + BM * PRB + 4 * kWave <= 160 * 1024 / 2, "two workgroups per CU");
+  static_assert(NRI <= 4 && NLW % 2 == 0, "copy layout");
+
+  // separate arrays, so that the compiler can tell the tile being read from the
+  // one the direct loads are filling
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t pl[BM * PRB];
+  __shared__ uint32_t pfd[kWave];   // landing slot of the L2 prefetch (never read)
+  auto red = [&](int row) -> float* { return reinterpret_cast<float*>(pl + row * PRB + 128); };
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int item = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, p.n_items));
+  if (item >= p.n_items) return;
+  const int rt = __builtin_amdgcn_readfirstlane(item % p.row_tiles);
+  const int g = __builtin_amdgcn_readfirstlane(item / p.row_tiles);
+  int b = 0, ps = g, off_b = p.off0, Kv = p.kv1;
+  if (p.B > 1) {
+    const SplitPos sp = decode_split(g, p.off, p.B, p.chunk);
+    b = __builtin_amdgcn_readfirstlane(sp.b);
+    ps = __builtin_amdgcn_readfirstlane(sp.s);
+    off_b = __builtin_amdgcn_readfirstlane(p.off[b]);
+    Kv = __builtin_amdgcn_readfirstlane(p.off[b + 1]) - off_b;
+  }
+  long long p0 = off_b;
+  int Kt = Kv;
+  if (SEL) {
+    p0 = p.B > 1 ? (long long)__builtin_amdgcn_readfirstlane(p.koff[b]) : (long long)p.koff0;
+    Kt = p.B > 1 ? __builtin_amdgcn_readfirstlane(p.koff[b + 1]) - (int)p0 : p.kvt1;
+  }
+  const int sel0 = off_b;
+  const int k0 = __builtin_amdgcn_readfirstlane(ps * p.chunk);
+  const int k1 = __builtin_amdgcn_readfirstlane(min(Kv, k0 + p.chunk));
+  const int ntail = min(p.L - 1, Kv);
+  int tailv = -1;
+  if (SEL && ntail <= kWave && lane < ntail) tailv = p.sel[sel0 + Kv - 1 - lane];
+  auto visible = [&](int i) -> int {   // split indices query row i may see
+    const int bound = Kt - p.L + i + 1;
+    if (!SEL) return bound;
+    if (ntail <= kWave) {
+      int above = 0;
+      for (int j = 0; j < ntail; ++j) above += __builtin_amdgcn_readlane(tailv, j) >= bound ? 1 : 0;
+      return Kv - above;
+    }
+    int lo = 0, hi = Kv;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.sel[sel0 + mid] < bound) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  int sidx = 0;
+  auto load_idx = [&](int t0) {
+    if (SEL) sidx = min(max(p.sel[sel0 + min(t0 + lane, k1 - 1)], 0), Kt - 1);
+  };
+  const int idx0 = rt * BM;
+  const int nrows = min(BM, p.rows - idx0);
+  const uint8_t* cbase = p.c8 + p0 * DW;
+  const float* sbase = p.s8 + p0;
+
+  // ---- tile copy: global -> LDS ----------------------------------------------
+  // Latent rows of 512 codes, unpadded, 16-byte chunk c of row r stored at
+  // chunk c ^ (r & 15): the 16 rows of a score fragment, and the 8 rows of a
+  // transposed V read, then fall in distinct bank groups.  One wave
+  // instruction fills two rows (lane l: row 2 j + l / 32, stored chunk l % 32),
+  // every lane active; the rope parts (64 bytes a row, chunk c at c ^ (r & 3))
+  // take one instruction per 16 rows, the scales one per tile.
+  // This wave's latent pairs are j = wu + 4 x: lane l copies row r = 2 j + l / 32
+  // = 8 x + (2 wu + l / 32), whose swizzle r & 15 is 8 (x & 1) + (2 wu + l / 32).
+  const int lrow = 2 * wu + (lane >> 5);                   // row of the pair (x = 0) for this lane
+  const int lsw0 = 16 * ((lane & 31) ^ lrow), lsw1 = 16 * ((lane & 31) ^ (8 + lrow));
+  const int rrow = lane >> 2, rpc = lane & 3;              // rope copy: row in the 16, stored chunk
+  auto pos_of = [&](int t0, int key) -> int {              // cache position of tile row `key` (per lane)
+    return SEL ? __shfl(sidx, key, kWave) : min(t0 + key, k1 - 1);
+  };
+  auto issue_latent = [&](int t0, uint8_t* kdst, int x) {
+    const int pos = pos_of(t0, 8 * x + lrow);
+    dma<16>(cbase + (long long)pos * DW + ((x & 1) ? lsw1 : lsw0), kdst + 1024 * (wu + 4 * x));
+  };
+  auto issue_rope = [&](int t0, uint8_t* kdst, int j) {
+    const int r = 16 * j + rrow;
+    const int pos = pos_of(t0, r);
+    dma<16>(cbase + (long long)pos * DW + DA + 16 * (rpc ^ (r & 3)), kdst + ROPE + 1024 * j);
+  };
+  // the tile's 64 scales (lane j: key j)
+  auto issue_scales = [&](int t0, uint8_t* kdst) {
+    dma<4>(sbase + pos_of(t0, lane), kdst + SOFF);
+  };
+  // copy x of this wave (x < NLW: latent pair wu + 4 x; NLW: its rope block or
+  // the scales)
+  auto issue_part = [&](int t0, uint8_t* kdst, int x) {
+    if (x < NLW) issue_latent(t0, kdst, x);
+    else if (wu < NRI) issue_rope(t0, kdst, wu);
+    else if (wu == 3) issue_scales(t0, kdst);
+  };
+  auto issue_tile = [&](int t0, uint8_t* kdst) {
+#pragma unroll
+    for (int x = 0; x <= NLW; ++x) issue_part(t0, kdst, x);
+    if (NRI == 4 && wu == 0) issue_scales(t0, kdst);
+  };
+  // barrier over LDS traffic that does not wait for the direct loads in flight
+  // (a tile is waited for, with vmcnt, before the barrier that publishes it)
+  auto lgkm_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  int kend[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int idx = idx0 + min(16 * rb + l16, nrows - 1);
+    kend[rb] = min(k1, visible(idx / p.H));
+  }
+  const int kfull = __builtin_amdgcn_readfirstlane(min(k1, visible(idx0 / p.H)));
+
+  // ---- query block -> E4M3 codes and block scales -----------------------------
+  // One thread per (row, 32-wide block of the key dimension): the block's
+  // scale 2^e is the smallest with every |q| <= 448 x 2^e, and its codes go to
+  // buf1 (idle until the next tile's copy) in the B layout of the score MFMA:
+  // lane l = row 16 rb + l % 16 over k = 128 ks + 16 (l / 16) .. (bytes 0..15)
+  // and 128 ks + 64 + 16 (l / 16) .. (bytes 16..31), fragment (rb, ks < KS) of
+  // lane l at 32 (64 (rb KS + ks) + l).  Block j of step ks thus fills bytes
+  // 16 (j / 2) .. of lane groups 2 (j % 2) and 2 (j % 2) + 1, and group j
+  // supplies its scale (an int per lane and step, in pl).  The rope step keeps
+  // only its lower halves (at 32 NRB KS 64 + 16 (64 rb + l)); its upper halves
+  // and blocks 2, 3 are zero.  Rows past the last query row repeat it (their
+  // results are never stored).  A thread's query loads are issued before the
+  // first tile's copy, so waiting for them does not wait for the tile.
+  i32x8 qf[NRB][NQ];
+  int qs[NRB][(NQ + 3) / 4];   // E8M0 scales, step ks in byte ks % 4 of qs[rb][ks / 4]
+  {
+    constexpr int NB = DA / 32 + DR / 32;     // blocks per row
+    constexpr int NU = (BM * NB + 255) / 256; // blocks per thread (the last round partial)
+    constexpr int ROPE_OFF = NRB * KS * kWave * 32;
+    const long long qflat0 = (long long)b * p.rows + idx0;
+    u32x4 qv[NU][4];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = min(tid + 256 * i, BM * NB - 1);
+      const int row = u / NB, blk = u - row * NB;
+      const long long qrow = qflat0 + min(row, nrows - 1);
+      const uint16_t* src = blk >= DA / 32 ? p.q_pe + qrow * DR + 32 * (blk - DA / 32) : p.q_lat + qrow * DA + 32 * blk;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qv[i][c] = ld16(src + 8 * c);
+    }
+    load_idx(k0);
+    issue_tile(k0, buf0);   // first tile in flight while the queries are quantised
+    load_idx(k0 + BN);
+    int* const qsl = reinterpret_cast<int*>(pl);
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = tid + 256 * i;
+      if (u < BM * NB) {
+        const int row = u / NB, blk = u - row * NB;
+        const float m = absmax8(qv[i][3], absmax8(qv[i][2], absmax8(qv[i][1], absmax8(qv[i][0], 0.f))));
+        const int e = e4m3_scale_exponent(m);
+        const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+        const int rb = row >> 4, r16 = row & 15;
+        const u32x2 c0 = e4m3x8(qv[i][0], sc), c1 = e4m3x8(qv[i][1], sc), c2 = e4m3x8(qv[i][2], sc),
+                    c3 = e4m3x8(qv[i][3], sc);
+        const u32x4 lo = u32x4{c0[0], c0[1], c1[0], c1[1]}, hi = u32x4{c2[0], c2[1], c3[0], c3[1]};
+        if (blk < DA / 32) {
+          const int ks = blk >> 2, j = blk & 3;
+          const int fl = 64 * (rb * KS + ks);
+          const int ga = 2 * (j & 1), hb = 16 * (j >> 1);
+          st16(buf1 + 32 * (fl + 16 * ga + r16) + hb, lo);
+          st16(buf1 + 32 * (fl + 16 * (ga + 1) + r16) + hb, hi);
+          qsl[64 * (rb * NQ + ks) + 16 * j + r16] = e + 127;
+        } else {
+          const int j = blk - DA / 32;
+          st16(buf1 + ROPE_OFF + 16 * (64 * rb + 16 * (2 * j) + r16), lo);
+          st16(buf1 + ROPE_OFF + 16 * (64 * rb + 16 * (2 * j + 1) + r16), hi);
+          qsl[64 * (rb * NQ + NQ - 1) + 16 * j + r16] = e + 127;
+          qsl[64 * (rb * NQ + NQ - 1) + 16 * (j + 2) + r16] = 127;
+        }
+      }
+    }
+    lgkm_barrier();
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int fl = 64 * (rb * KS + ks) + lane;
+        const u32x4 x0 = ld16(buf1 + 32 * fl), x1 = ld16(buf1 + 32 * fl + 16);
+        qf[rb][ks] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
+      if (DR > 0) {
+        const u32x4 x0 = ld16(buf1 + ROPE_OFF + 16 * (64 * rb + lane));
+        qf[rb][NQ - 1] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int k4 = 0; k4 < (NQ + 3) / 4; ++k4) {
+        int v = 0;
+#pragma unroll
+        for (int ks = 4 * k4; ks < min(NQ, 4 * k4 + 4); ++ks) v |= qsl[64 * (rb * NQ + ks) + lane] << (8 * (ks % 4));
+        qs[rb][k4] = v;
+      }
+    }
+    // buf1 and pl are written again only after barrier (A) of the first tile
+  }
+
+  // ---- running state (score layout: row 16 rb + l16) -----------------------
+  float m_ref[NRB], l_part[NRB], t_max[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) { m_ref[rb] = -INFINITY; l_part[rb] = 0.f; t_max[rb] = -INFINITY; }
+  bool rerun = false;
+  f32x16 O[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[cb][i] = 0.f;
+
+  // score A fragment of key 16 w + l16: logical chunk 8 ks + lg (+ 4) is stored
+  // at (8 ks + lg) ^ l16 = (lg ^ l16) ^ 8 ks (the bits do not overlap)
+  const int ka_row = (16 * w + l16) * DA + 16 * (lg ^ l16);
+  const int kr_off = ROPE + (16 * w + l16) * DR + 16 * (lg ^ (l16 & 3));
+  const int G = lane >> 4, s16 = lane & 15;
+  // V^T fragment of the 32x32x16 MFMA (col 32 cb + l32, keys 16 kc + 8 half ..):
+  // source lane s16 of group G reads key 8 (G >> 1) + s16 / 2, 8 codes at column
+  // 16 (G & 1) + 8 (s16 & 1); the read hands lane s16 column s16 of the 8 keys.
+  // The key's low 4 bits (the swizzle) do not depend on kc.
+  // (logical chunk 8 w + 2 cb + (G & 1) is stored at ((8 w + (G & 1)) ^ key) ^ 2 cb)
+  const int tr_key = 8 * (G >> 1) + (s16 >> 1);
+  const int tr_base = tr_key * DA + 8 * (s16 & 1);
+  const int tr_sw = (8 * w + (G & 1)) ^ tr_key;
+  const int pa_off = l32 * PRB + 16 * half;                              // P^T fragment: + 32 kc
+  const int pw_off = l16 * PRB + (16 * w + 4 * lg) * 2;                  // + 16 rb PRB
+
+  // Cache lines of tile ta (its codes, then its scales) -> L2 ahead of its
+  // copy: the split's row tiles (one XCD, one L2) take pf_lines lines each, tile
+  // rt the slice from rt pf_lines, one 4-byte load per line into a dummy LDS slot.
+  const int kPfAhead = p.pf_ahead;
+  auto prefetch_tile = [&](int ta) {
+    if (SEL || ta >= k1 || tid >= p.pf_lines) return;
+    const int npos = min(BN, k1 - ta);
+    const int code_lines = (npos * DW + 127) / 128;
+    const int ln = rt * p.pf_lines + tid;
+    const void* src = ln < code_lines ? (const void*)(cbase + (long long)ta * DW + 128 * ln)
+                                      : (const void*)(sbase + ta + min(32 * (ln - code_lines), npos - 1));
+    if (ln < code_lines + 2) dma<4>(src, pfd);
+  };
+
+  auto step = [&](int t0, const uint8_t* cur, uint8_t* nxt, bool pf) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // (A) tile t visible; PV(t-1) done, so the other buffer and pl are free
+    if (!rerun) {
+      if (t0 == k0) {
+        for (int d = 1; d <= kPfAhead; ++d) prefetch_tile(t0 + d * BN);
+      } else {
+        prefetch_tile(t0 + kPfAhead * BN);
+      }
+    }
+
+    // ---- scores: S^T [16 keys x 32 rows] on the scaled fp8 MFMA ---------------
+    f32x4 acc[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      const int ksc = (int)(__float_as_uint(*reinterpret_cast<const float*>(cur + SOFF + 4 * (16 * w + l16))) >> 23);
+      auto afrag = [&](int ks) {
+        if (ks == KS) {   // rope: lower half only
+          const u32x4 x0 = ld16(cur + kr_off);
+          return i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], 0, 0, 0, 0};
+        }
+        const u32x4 x0 = ld16(cur + (ka_row ^ (16 * 8 * ks)));
+        const u32x4 x1 = ld16(cur + (ka_row ^ (16 * (8 * ks + 4))));
+        return i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      };
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < NQ; ++ks) {
+        const i32x8 af = afrag(ks);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          acc[rb] = mfma16_f8_sel(af, qf[rb][ks], acc[rb], ksc, qs[rb][ks / 4], ks % 4);
+        if (pf) {
+#pragma unroll
+          for (int x = (ks * NC) / NQ; x < ((ks + 1) * NC) / NQ; ++x) issue_latent(t0 + BN, nxt, x);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // acc[rb][i] = q . k for key t0 + 16 w + 4 lg + i, row 16 rb + l16.
+    if (t0 + BN > kfull) {   // a tile past some row's causal end (uniform branch)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + 16 * w + 4 * lg + i >= kend[rb]) acc[rb][i] = -INFINITY;
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      t_max[rb] = fmaxf(fmaxf(t_max[rb], fmaxf(acc[rb][0], acc[rb][1])), fmaxf(acc[rb][2], acc[rb][3]));
+    // The first tile of the split sets each row's reference (a row sees a prefix
+    // of the split's positions, so its first finite scores are in this tile).
+    if (t0 == k0 && !rerun) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float mx = group_max(fmaxf(fmaxf(acc[rb][0], acc[rb][1]), fmaxf(acc[rb][2], acc[rb][3])));
+        if (lg == 0) red(16 * rb + l16)[w] = mx * p.sl2;
+      }
+      lgkm_barrier();
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const f32x4 r4 = *reinterpret_cast<const f32x4*>(red(16 * rb + l16));
+        m_ref[rb] = fmaxf(fmaxf(r4[0], r4[1]), fmaxf(r4[2], r4[3]));
+      }
+    }
+    // P = 2^(s - m) in bf16; PV takes P x (key scale), the row sums P
+    {
+      const f32x4 ksc4 = *reinterpret_cast<const f32x4*>(cur + SOFF + 4 * (16 * w + 4 * lg));
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float mb = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(acc[rb][i], p.sl2, -mb));
+        const uint32_t v0 = pack_bf16(e[0], e[1]), v1 = pack_bf16(e[2], e[3]);
+        l_part[rb] = add_bf16x2(v1, add_bf16x2(v0, l_part[rb]));
+        u32x2 v;
+        v[0] = pack_bf16(e[0] * ksc4[0], e[1] * ksc4[1]);
+        v[1] = pack_bf16(e[2] * ksc4[2], e[3] * ksc4[3]);
+        *reinterpret_cast<u32x2*>(pl + pw_off + 16 * rb * PRB) = v;
+      }
+    }
+    lgkm_barrier();  // (B) P visible (the next tile's copy stays in flight)
+
+    // ---- PV: O^T [CPW columns x 32 rows] for this wave's columns --------------
+    {
+      const uint8_t* pa = pl + pa_off;
+      auto vfrag = [&](int kc, int cb) {
+        typedef int i32x2 __attribute__((ext_vector_type(2)));
+        const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(cur + tr_base + 16 * kc * DA + 16 * (tr_sw ^ (2 * cb))));
+        u32x4 bv;
+        bv[0] = e4m3x2_bf16<false>((uint32_t)r[0]);
+        bv[1] = e4m3x2_bf16<true>((uint32_t)r[0]);
+        bv[2] = e4m3x2_bf16<false>((uint32_t)r[1]);
+        bv[3] = e4m3x2_bf16<true>((uint32_t)r[1]);
+        return bv;
+      };
+      constexpr int NSTEP = (BN / 16) * NCB;
+      constexpr int VPF = 2;
+      u32x4 a[BN / 16];
+      u32x4 vq[VPF];
+#pragma unroll
+      for (int kc = 0; kc < BN / 16; ++kc) a[kc] = *reinterpret_cast<const u32x4*>(pa + 32 * kc);
+#pragma unroll
+      for (int st = 0; st < VPF; ++st) vq[st] = vfrag(st / NCB, st % NCB);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        const int kc = st / NCB, cb = st % NCB;
+        const u32x4 bcur = vq[st % VPF];
+        const int sn = st + VPF;
+        if (sn < NSTEP) vq[st % VPF] = vfrag(sn / NCB, sn % NCB);
+        O[cb] = mfma32(bcur, a[kc], O[cb]);   // O^T += V^T P^T
+        // the rest of the next tile's copies: latent pairs NC .. NLW - 1, then the
+        // rope block / scales, one every other MFMA step
+        if (pf && (st & 1) && NC + st / 2 <= NLW) issue_part(t0 + BN, nxt, NC + st / 2);
+        if (pf && NRI == 4 && st == 0 && wu == 0) issue_scales(t0 + BN, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    load_idx(t0 + 2 * BN);
+  };
+
+  for (;;) {
+    for (int t0 = k0; t0 < k1; t0 += 2 * BN) {
+      step(t0, buf0, buf1, t0 + BN < k1);
+      if (t0 + BN < k1) step(t0 + BN, buf1, buf0, t0 + 2 * BN < k1);
+    }
+    // Did some row's scores exceed its reference by more than 2^kRefSlack?  Then
+    // its P, O and l may have overflowed: raise every reference to the row's
+    // maximum over the whole split and run the split again (the second pass
+    // cannot trigger another: its references bound every score).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // every wave is done with red and the tile buffers
+    float tm[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float mx = group_max(t_max[rb]);
+      if (lg == 0) red(16 * rb + l16)[w] = mx * p.sl2;
+    }
+    lgkm_barrier();
+    bool over = false;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const f32x4 r4 = *reinterpret_cast<const f32x4*>(red(16 * rb + l16));
+      tm[rb] = fmaxf(fmaxf(r4[0], r4[1]), fmaxf(r4[2], r4[3]));
+      over = over || (m_ref[rb] != -INFINITY && tm[rb] > m_ref[rb] + kRefSlack);
+    }
+    // every wave holds all of the block's rows, so the decision is uniform over
+    // the workgroup; checked explicitly so that no input, NaN included, loops
+    if (rerun || __ballot(over) == 0) break;
+    rerun = true;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      m_ref[rb] = m_ref[rb] == -INFINITY ? m_ref[rb] : fmaxf(m_ref[rb], tm[rb]);
+      l_part[rb] = 0.f;
+      t_max[rb] = -INFINITY;
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[cb][i] = 0.f;
+    __syncthreads();   // the maxima are read before red is written again
+    load_idx(k0);
+    issue_tile(k0, buf0);
+    load_idx(k0 + BN);
+  }
+
+  // ---- epilogue: row sums, partial results ---------------------------------
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();   // every wave is done with the tile buffers and red
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const float s = group_sum(l_part[rb]);
+    if (lg == 0) red(16 * rb + l16)[w] = s;
+  }
+  {
+    // lane holds row l32, columns col0 + 32 cb + 8 q + 4 half + (0..3)
+    const int col0 = w * CPW;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint8_t* dst = buf0 + l32 * SROW + (col0 + 32 * cb + 8 * q + 4 * half) * 2;
+        const f32x16& o = O[cb];
+        u32x2 v;
+        v[0] = pack_bf16(o[4 * q], o[4 * q + 1]);
+        v[1] = pack_bf16(o[4 * q + 2], o[4 * q + 3]);
+        *reinterpret_cast<u32x2*>(dst) = v;
+      }
+  }
+  __syncthreads();
+  const long long gro = (long long)g * p.rows;
+  if (w == 0 && lg == 0) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int row = 16 * rb + l16;
+      if (row < nrows) {
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(red(row));
+        *reinterpret_cast<f32x2*>(p.ws_ml + (gro + idx0 + row) * 2) = f32x2{m_ref[rb], (s4[0] + s4[1]) + (s4[2] + s4[3])};
+      }
+    }
+  }
+  {
+    constexpr int V16 = DV * 2 / 16;
+    constexpr int NST = BM * V16 / 256;
+    uint8_t* wso = reinterpret_cast<uint8_t*>(p.ws_o);
+    u32x4 v[NST];
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int e = tid + 256 * j;
+      v[j] = *reinterpret_cast<const u32x4*>(buf0 + (e / V16) * SROW + 16 * (e % V16));
+    }
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int e = tid + 256 * j;
+      const int row = e / V16;
+      if (row < nrows) st16(wso + ((gro + idx0 + row) * DV) * 2 + 16 * (e % V16), v[j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 namespace {
@@ -597,6 +1160,46 @@ hipError_t absorbed_attn_bf16(const AbsorbedLaunch& q, hipStream_t st) {
   switch (q.rope) {
     case 0:  hipLaunchKernelGGL((absorbed_split_kernel<0, false>), grid, dim3(256), 0, st, a); break;
     case 64: hipLaunchKernelGGL((absorbed_split_kernel<64, false>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The fp8 kernel takes 32 query rows per workgroup (two workgroups per CU), the
+// plan's splits with twice its 64-row tiles.
+void f8_rows(SplitArgs& a, int rope) {
+  a.row_tiles = (a.rows + 31) / 32;
+  a.n_items = (a.n_items / ((a.rows + 63) / 64)) * a.row_tiles;
+  a.pf_ahead = std::min(16, std::max(2, a.row_tiles / 2));
+  const int lines = (64 * (512 + rope) + 127) / 128 + 2;   // a tile's code lines and its scales' lines
+  a.pf_lines = std::min(256, (lines + a.row_tiles - 1) / a.row_tiles);
+}
+
+hipError_t absorbed_attn_fp8(const AbsorbedLaunch& q, const void* codes, const float* scales, hipStream_t st) {
+  SplitArgs a = split_args(q);
+  a.c8 = (const uint8_t*)codes; a.s8 = scales;
+  f8_rows(a, q.rope);
+  if (q.r != 512) return hipErrorInvalidValue;
+  const dim3 grid(grid_of(a.n_items));
+  switch (q.rope) {
+    case 0:  hipLaunchKernelGGL((absorbed_split_f8_kernel<0, false>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((absorbed_split_f8_kernel<64, false>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t absorbed_attn_sparse_fp8(const AbsorbedLaunch& q, const void* codes, const float* scales,
+                                    const int32_t* sel, const int32_t* koff_dev, int koff0, int kvt1, hipStream_t st) {
+  SplitArgs a = split_args(q);
+  a.c8 = (const uint8_t*)codes; a.s8 = scales;
+  a.sel = sel; a.koff = koff_dev; a.koff0 = koff0; a.kvt1 = kvt1;
+  f8_rows(a, q.rope);
+  if (q.r != 512) return hipErrorInvalidValue;
+  const dim3 grid(grid_of(a.n_items));
+  switch (q.rope) {
+    case 0:  hipLaunchKernelGGL((absorbed_split_f8_kernel<0, true>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((absorbed_split_f8_kernel<64, true>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
