@@ -1,16 +1,16 @@
 // attn.hip -- split-KV attention kernels of libmla and their combine passes.
 //
-// One kernel template serves both MLA routes (pages: "One guard, 110x off the
-// verify step", section "The defect"):
+// The two MLA routes (pages: "One guard, 110x off the verify step", section
+// "The defect"):
 //   absorbed     : every (row, head) pair of a sequence is a query of width
 //                  r + rope = [q_lat | q_pe] against the shared keys
-//                  [c_kv | k_pe]; the values are c_kv itself, so one latent
-//                  tile, read once into LDS, serves the scores and the
-//                  weighted sum of all L*H pairs (multi-query attention with a
-//                  single shared key/value head);
+//                  [c_kv | k_pe]; the values are c_kv itself (multi-query
+//                  attention with a single shared key/value head).  Its bf16
+//                  and fp8 split kernels are in split_absorbed.hip; this file
+//                  holds its float32 kernel and its merge + up-projection;
 //   materialised : each head attends over its own expanded K [T, H, n+rope]
-//                  and V [T, H, v].
-// Positions of a sequence are cut into splits; each workgroup takes 64 query
+//                  and V [T, H, v] (the bf16 kernel below, float32 kernel).
+// Positions of a sequence are cut into splits; each workgroup takes query
 // rows x one split and leaves unnormalised partial results (o, running max m,
 // running sum l, base-2 logits) in a workspace.  A second pass merges the
 // splits with a log-sum-exp combine; on the absorbed route it also applies
@@ -31,8 +31,7 @@
 //           tile with ds_read_b64_tr_b16.
 // LDS holds two tile buffers (tile t is computed while tile t+1 is copied in
 // by direct-to-LDS loads issued between the score MFMAs), P and small
-// exchange arrays.  Variants of the same template read an fp8 cache (codes
-// expanded to bf16 in LDS) or only selected cache positions.
+// exchange arrays.
 
 #include <algorithm>
 #include <type_traits>
@@ -48,22 +47,15 @@ namespace mla {
 struct AttnArgs {
   const uint16_t* qa;   // query part a: [B, L, H, DA]
   const uint16_t* qb;   // query part b: [B, L, H, DR]
-  const uint16_t* ka;   // key-only source (see KW), row for position p at ka + p*ka_ks + head*ka_hs
-  const uint16_t* vv;   // value source, row for position p at vv + p*vv_ks + head*vv_hs
-  const uint8_t* c8;    // fp8 latent cache (F8): E4M3 codes [T, DA + DR] (latent | rope) ...
-  const float* c8s;     // ... and one power-of-two scale per position [T]
-  const int32_t* sel;   // SEL: selected positions per sequence (packed by off; relative, increasing)
-  const int32_t* koff;  // SEL: cache offsets [B+1] (off then indexes the selection)
-  int koff0, kvt1;      // SEL, B == 1: koff[0] and koff[1] - koff[0]
+  const uint16_t* ka;   // keys, row for position p at ka + p*ka_ks + head*ka_hs
+  const uint16_t* vv;   // values, row for position p at vv + p*vv_ks + head*vv_hs
   long long ka_ks, ka_hs, vv_ks, vv_hs;
   const int32_t* off;   // [B+1] device offsets
   int off0, kv1;        // B == 1: off[0] and off[1] - off[0]
-  void* ws_o;           // [G][rows_total][DV] unnormalised partial sums: bf16 (absorbed), float32 (materialised)
+  float* ws_o;          // [G][rows_total][DV] unnormalised partial sums (float32)
   float* ws_ml;         // [G][rows_total][2]
   int B, L, H;
-  int hpr;              // heads per row slot (absorbed: H, materialised: 1)
-  int rows_slot;        // query rows per (sequence, head slot)
-  int head_slots;       // absorbed: 1, materialised: H
+  int rows_slot;        // query rows per (sequence, head) = L
   int row_tiles;        // ceil(rows_slot / 64)
   int chunk;            // positions per split (multiple of 64)
   int n_items;
@@ -74,8 +66,8 @@ struct AttnArgs {
 // Headroom of the fixed softmax reference (log2 units): P = 2^(s - m) <= 2^64.
 constexpr float kRefSlack = 64.f;
 
-// DA: width of query part a (= width of the V source when VK); DR: query part
-// b width; DV: value width; VK: values are the first DA key columns (absorbed).
+// DA: width of query part a (q_nope, n); DR: query part b width (rope); DV:
+// value width.
 //
 // Tiles of 64 positions are copied global -> LDS by direct-to-LDS loads (each
 // wave instruction fills 1 KB of LDS, lane l at +16*l), double-buffered: tile
@@ -86,7 +78,7 @@ constexpr float kRefSlack = 64.f;
 // fragments straight from the row-major tile with ds_read_b64_tr_b16 (lane l
 // of each 16-lane group receives column l%16 of the 4 rows its group
 // addressed), so there is no transposed copy of V.
-template <int DA, int DR, int DV, bool VK, bool F8 = false, bool SEL = false>
+template <int DA, int DR, int DV>
 __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   constexpr int D = DA + DR;
   constexpr int BM = 64, BN = 64;
@@ -96,22 +88,20 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   constexpr int KRB = (KCH + 1) * 16;     // padded LDS row stride (bytes)
   constexpr int VRB = (VCH + 1) * 16;
   constexpr int KBYTES = BN * KRB;
-  constexpr int VBYTES = VK ? 0 : BN * VRB;
+  constexpr int VBYTES = BN * VRB;
   constexpr int BUF = KBYTES + VBYTES;
   constexpr int KINST = KCH + 1;          // direct-load wave instructions per key tile (64 slots each)
-  constexpr int VINST = VK ? 0 : VCH + 1;
+  constexpr int VINST = VCH + 1;
   constexpr int PRB = 9 * 16;             // P row: 64 keys (8 chunks) + pad
   constexpr int CPW = DV / 4;             // value columns per wave
   constexpr int NCB = CPW / 32;           // 32-column MFMA blocks per wave
-  constexpr int VRBX = VK ? KRB : VRB;
-  static_assert(D % 16 == 0 && DV % 128 == 0 && (!VK || DA == DV), "unsupported geometry");
+  static_assert(D % 16 == 0 && DV % 128 == 0, "unsupported geometry");
 
   // two distinct LDS objects, so that alias analysis can tell the tile being
   // read from the tile being copied in (no spurious waits on the copy)
   __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
   __shared__ __attribute__((aligned(16))) uint8_t pl[BM * PRB];
-  __shared__ uint32_t pfd[kWave];   // landing slot of the L2 prefetch (never read)
   __shared__ __attribute__((aligned(16))) float red[BM * 4];   // per row: 4 partial values (2 key halves x 2 lane halves)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -121,8 +111,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   if (item >= p.n_items) return;
   const int rt = __builtin_amdgcn_readfirstlane(item % p.row_tiles);
   const int tmp = __builtin_amdgcn_readfirstlane(item / p.row_tiles);
-  const int hs = __builtin_amdgcn_readfirstlane(tmp % p.head_slots);
-  const int g = __builtin_amdgcn_readfirstlane(tmp / p.head_slots);
+  const int hs = __builtin_amdgcn_readfirstlane(tmp % p.H);   // head
+  const int g = __builtin_amdgcn_readfirstlane(tmp / p.H);
   // the split is the same for the whole workgroup: keep its bounds in scalar registers
   // (one sequence: its start and length come from the host, no load of the offsets)
   int b = 0, ps = g, off_b = p.off0, Kv = p.kv1;
@@ -133,83 +123,27 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     off_b = __builtin_amdgcn_readfirstlane(p.off[b]);
     Kv = __builtin_amdgcn_readfirstlane(p.off[b + 1]) - off_b;
   }
-  // SEL: the split runs over the sequence's selected positions: off_b / Kv index
-  // the packed selection, the cache rows start at koff[b], and the causal bound
-  // comes from the cache length Kt.  Selected entries are clamped into the cache.
-  long long pcache = off_b;
-  int Kt = Kv;
-  if (SEL) {
-    pcache = p.B > 1 ? (long long)__builtin_amdgcn_readfirstlane(p.koff[b]) : (long long)p.koff0;
-    Kt = p.B > 1 ? __builtin_amdgcn_readfirstlane(p.koff[b + 1]) - (int)pcache : p.kvt1;
-  }
-  const long long p0 = pcache;
-  const int sel0 = off_b;
-  auto kpos = [&](int j) -> int {   // cache position (from the sequence start) of split index j
-    if (!SEL) return j;
-    return min(max(p.sel[sel0 + j], 0), Kt - 1);
-  };
+  const long long p0 = off_b;
   const int k0 = __builtin_amdgcn_readfirstlane(ps * p.chunk);
   const int k1 = __builtin_amdgcn_readfirstlane(min(Kv, k0 + p.chunk));
-  // SEL: the entries at or above a row's bound Kt - L + i + 1 are among the
-  // selection's last L - 1 (they are distinct positions above Kt - L): count them
-  // from a register holding that tail (lane j: the j-th entry from the end).
-  const int ntail = min(p.L - 1, Kv);
-  int tailv = -1;
-  if (SEL && ntail <= kWave && lane < ntail) tailv = p.sel[sel0 + Kv - 1 - lane];
-  auto visible = [&](int i) -> int {   // split indices query row i may see: positions < Kt - L + i + 1
-    const int bound = Kt - p.L + i + 1;
-    if (!SEL) return bound;
-    if (ntail <= kWave) {
-      int above = 0;
-      for (int j = 0; j < ntail; ++j) above += __builtin_amdgcn_readlane(tailv, j) >= bound ? 1 : 0;
-      return Kv - above;
-    }
-    int lo = 0, hi = Kv;               // long blocks: binary search of the increasing selection
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (p.sel[sel0 + mid] < bound) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-  };
-  // SEL: cache positions of the 64 keys of the next tile to copy, lane j -> key j;
-  // loaded one step ahead so the copy's row addresses wait for nothing
-  int sidx = 0;
-  auto load_idx = [&](int t0) {
-    if (SEL) sidx = kpos(min(t0 + lane, k1 - 1));
-  };
+  auto visible = [&](int i) -> int { return Kv - p.L + i + 1; };   // positions query row i may see
   const int idx0 = rt * BM;
   const int nrows = min(BM, p.rows_slot - idx0);
 
-  // key-only source: absorbed k_pe (chunks DA/8..), materialised K (all chunks)
   const uint16_t* kab = p.ka + (long long)hs * p.ka_hs;
   const uint16_t* vvb = p.vv + (long long)hs * p.vv_hs;
-  // absorbed: latent row 0 of the sequence (rows are DA wide), in scalar registers
-  const uint16_t* lbase = uniform_ptr(vvb + p0 * DA);
 
   // ---- tile copy: global -> LDS --------------------------------------------
-  // absorbed: each latent row (r = 512 bf16 = 1 KB) is one wave instruction
-  // (uniform row address, lane l copies bytes 16l..16l+15); the rope key
-  // (rope/8 chunks per row) is staged through registers and written after
-  // the tile's PV product.  materialised: slot -> (row, chunk) mapping.
-  constexpr int RCH = VK ? DR / 8 : 0;                      // rope chunks per row
-  constexpr int RP_T = VK ? (BN * RCH + 255) / 256 : 0;     // staged rope chunks per thread
-  u32x4 rst[RP_T > 0 ? RP_T : 1];
+  // Each wave instruction fills 1 KB of LDS: slot (64 j + lane) -> (row, chunk)
+  // of the padded tile; the pad slot of a row copies any valid chunk.
   // Load instructions of one wave for a tile, numbered 0..NLW-1, so that the
   // copy can be spread over the score MFMAs instead of stalling the wave.
-  constexpr int NLW_K = VK ? BN / 4 : (KINST + 3) / 4;
-  constexpr int NLW_V = VK ? 0 : (VINST + 3) / 4;
+  constexpr int NLW_K = (KINST + 3) / 4;
+  constexpr int NLW_V = (VINST + 3) / 4;
   constexpr int NLW = NLW_K + NLW_V;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto issue_part = [&](int t0, uint8_t* kdst, int x) {
-    if (VK) {
-      static_assert(!VK || DA == 512, "absorbed path loads 1 KB latent rows");
-      // one latent row per instruction: uniform row address + constant lane offset
-      const int key = wu + 4 * x;
-      const int kr = SEL ? __builtin_amdgcn_readlane(sidx, key) : __builtin_amdgcn_readfirstlane(min(t0 + key, k1 - 1));
-      // 64-bit row offset: kr * DA passes 2^31 at 2^22 positions
-      __builtin_amdgcn_global_load_lds(lbase + (long long)kr * DA + 8 * lane,
-                                       (__attribute__((address_space(3))) void*)(kdst + key * KRB), 16, 0, 0);
-    } else if (x < NLW_K) {
+    if (x < NLW_K) {
       const int j = wu + 4 * x;
       if (j < KINST) {
         const int pos = 64 * j + lane;            // chunk slot in the tile
@@ -234,76 +168,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
       }
     }
   };
-  auto issue_rope = [&](int t0) {
-    const uint16_t* rseq = kab + p0 * p.ka_ks;
-#pragma unroll
-    for (int x = 0; x < RP_T; ++x) {
-      const int C = tid + 256 * x;
-      if (C < BN * RCH) {
-        const int key = C / RCH, ch = C % RCH;
-        const int kr = SEL ? __shfl(sidx, key, kWave) : min(t0 + key, k1 - 1);
-        rst[x] = ld16(rseq + (long long)kr * DR + 8 * ch);
-      }
-    }
-  };
-  // F8: the tile's code rows (DA + DR bytes each) come into registers, four
-  // threads per position (thread t: position t / 4, 16-code chunks t % 4 + 4 x),
-  // and are expanded into the same bf16 tile layout after the tile's PV:
-  // code x 2^k is exact in bf16, so the tile holds the dequantised cache.
-  constexpr int F8C = F8 ? (DA + DR) / 16 : 4;           // 16-code chunks per position
-  constexpr int F8X = (F8C + 3) / 4;                      // chunks per thread
-  static_assert(!F8 || (VK && (DA + DR) % 64 == 0 && BN * 4 == 256), "fp8 rows: four threads per position");
-  static_assert(!SEL || VK, "selection only on the absorbed route");
-  u32x4 f8r[F8 ? F8X : 1];
-  float f8s = 0.f;
-  auto issue_f8 = [&](int t0, int x) {
-    const int key = tid >> 2, j = (tid & 3) + 4 * x;
-    // SEL: the cache position of key `key` sits in lane `key` of sidx
-    const long long kr = p0 + (SEL ? (long long)__shfl(sidx, key, kWave) : (long long)min(t0 + key, k1 - 1));
-    f8r[x] = ld16(p.c8 + kr * (DA + DR) + 16 * j);
-    if (x == 0) f8s = p.c8s[kr];
-  };
-  auto store_f8 = [&](uint8_t* kdst) {
-    const int key = tid >> 2;
-#pragma unroll
-    for (int x = 0; x < F8X; ++x) {
-      const int j = (tid & 3) + 4 * x;
-      u32x4 lo, hi;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8r[x][q], f8s, false);   // codes 4q, 4q+1
-        const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f8r[x][q], f8s, true);    // codes 4q+2, 4q+3
-        if (q < 2) {
-          lo[2 * q] = __builtin_bit_cast(uint32_t, a);
-          lo[2 * q + 1] = __builtin_bit_cast(uint32_t, b);
-        } else {
-          hi[2 * q - 4] = __builtin_bit_cast(uint32_t, a);
-          hi[2 * q - 3] = __builtin_bit_cast(uint32_t, b);
-        }
-      }
-      st16(kdst + key * KRB + 32 * j, lo);
-      st16(kdst + key * KRB + 32 * j + 16, hi);
-    }
-  };
   auto issue_tile = [&](int t0, uint8_t* kdst) {
-    if (F8) {
-#pragma unroll
-      for (int x = 0; x < F8X; ++x) issue_f8(t0, x);
-      return;
-    }
-    if (VK) issue_rope(t0);
 #pragma unroll
     for (int x = 0; x < NLW; ++x) issue_part(t0, kdst, x);
-  };
-  auto store_rope = [&](uint8_t* kdst) {
-#pragma unroll
-    for (int x = 0; x < RP_T; ++x) {
-      const int C = tid + 256 * x;
-      if (C < BN * RCH) {
-        const int key = C / RCH, ch = C % RCH;
-        st16(kdst + key * KRB + (DA / 8 + ch) * 16, rst[x]);
-      }
-    }
   };
 
   // ---- score-phase identity: wave (wk, wr), query row rq of the tile -------
@@ -313,76 +180,13 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   int kend = 0;   // positions this row may see within the split (relative to sequence start)
   u32x4 qf[DCH];
 
-  load_idx(k0);
   issue_tile(k0, buf0);   // first tile in flight while the queries load
-  load_idx(k0 + BN);
-  {
-    const int idx = idx0 + rq;
-    const int i = idx / p.hpr;
-    kend = min(k1, visible(i));
-  }
+  kend = min(k1, visible(idx0 + rq));
   // positions every row of the tile may see (rows are in increasing query order)
-  const int kfull = __builtin_amdgcn_readfirstlane(min(k1, visible(idx0 / p.hpr)));
-  if (VK) {
-    // absorbed: the rows of the tile are consecutive in q_lat / q_pe.  The query
-    // block goes to the idle tile buffer once (q_lat row = one 1 KB direct load,
-    // q_pe staged through registers), then every wave reads its fragments.
-    // Rows past the last query row repeat it (their results are never stored).
-    constexpr int QP_T = (BM * RCH + 255) / 256;
-    u32x4 qst[QP_T > 0 ? QP_T : 1];
-    const long long qflat0 = (long long)b * p.L * p.H + idx0;   // flat row of tile row 0
-    const uint16_t* qlseq = p.qa + qflat0 * DA + 8 * lane;
-#pragma unroll
-    for (int x = 0; x < BM / 4; ++x) {
-      const int row = wu + 4 * x;
-      __builtin_amdgcn_global_load_lds(qlseq + (unsigned)min(row, nrows - 1) * (unsigned)DA,
-                                       (__attribute__((address_space(3))) void*)(buf1 + row * KRB), 16, 0, 0);
-    }
-#pragma unroll
-    for (int x = 0; x < QP_T; ++x) {
-      const int C = tid + 256 * x;
-      if (C < BM * RCH) {
-        const int row = C / RCH, ch = C % RCH;
-        qst[x] = ld16(p.qb + (qflat0 + min(row, nrows - 1)) * DR + 8 * ch);
-      }
-    }
-    // This workgroup's share of the split's cache lines -> L2: positions
-    // k0 + rt + row_tiles * j, one 4-byte load per 128-byte line (8 latent lines,
-    // 1 rope line per position) into a dummy LDS slot.  The row tiles of a split
-    // run on one XCD, so the tile copies of the loop then hit L2.
-    if (!F8 && !SEL) {
-      constexpr int LPP = DA / 64 + (DR > 0 ? 1 : 0);   // 128-byte lines per position
-      const int cnt = max(0, (k1 - k0 - rt + p.row_tiles - 1) / p.row_tiles);
-      const int nl = cnt * LPP;
-      for (int e0 = 0; e0 < nl; e0 += 256) {
-        const int e = min(e0 + tid, nl - 1);
-        const int j = e / LPP, ln = e - (e / LPP) * LPP;
-        const long long pos = p0 + k0 + rt + (long long)p.row_tiles * j;
-        const uint16_t* src = ln < DA / 64 ? vvb + pos * p.vv_ks + 64 * ln : kab + pos * p.ka_ks;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)pfd, 4, 0, 0);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int x = 0; x < QP_T; ++x) {
-      const int C = tid + 256 * x;
-      if (C < BM * RCH) {
-        const int row = C / RCH, ch = C % RCH;
-        st16(buf1 + row * KRB + (DA / 8 + ch) * 16, qst[x]);
-      }
-    }
-    if (F8) store_f8(buf0); else store_rope(buf0);
-    __syncthreads();   // query block (and tile 0) in LDS
-    const uint8_t* qrow = buf1 + rq * KRB + 16 * half;
-#pragma unroll
-    for (int c = 0; c < DCH; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qrow + 32 * c);
-    // buf1 receives tile 1 after the first barrier of the loop: finish reading it first
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  } else {
-    const int idx = idx0 + rq;
-    const int i = idx / p.hpr;
-    const int h = hs + idx % p.hpr;
-    const long long flat = ((long long)b * p.L + i) * p.H + h;
+  const int kfull = __builtin_amdgcn_readfirstlane(min(k1, visible(idx0)));
+  {
+    const int i = idx0 + rq;
+    const long long flat = ((long long)b * p.L + i) * p.H + hs;
 #pragma unroll
     for (int c = 0; c < DCH; ++c) {
       const int dim = 16 * c + 8 * half;
@@ -410,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
   // per-lane LDS offsets (bytes) within a buffer; the rest are immediates
   const int qk_off = (32 * wk + l32) * KRB + 16 * half;                   // + 32 c
   const int G = lane >> 4, s16 = lane & 15;
-  const int tr_off = (8 * (G >> 1) + (s16 >> 2)) * VRBX                    // key part
+  const int tr_off = (8 * (G >> 1) + (s16 >> 2)) * VRB                    // key part
                      + (w * CPW + 16 * (G & 1) + 4 * (s16 & 3)) * 2;      // column part
   const int pa_off = l32 * PRB + 16 * half;                               // + rb*32*PRB + 32 kc
 
@@ -425,9 +229,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
     // The next tile is copied unconditionally (branch-free code keeps the LDS
     // wait counts exact): past the end of the split every row clamps to the
     // last position and lands in the idle buffer, which nothing reads again.
-    if (VK && !F8 && pf) issue_rope(t0 + BN);
     const uint8_t* kt = cur;
-    const uint8_t* vt = VK ? kt : kt + KBYTES;
+    const uint8_t* vt = kt + KBYTES;
 
     // ---- scores: S^T block [32 keys x 32 rows] --------------------------
     f32x16 acc;
@@ -449,13 +252,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         acc = mfma32(a, qf[c], acc);
         // next tile's copy, spread over the score MFMAs (NLW instructions)
         if (pf) {
-          if (F8) {
 #pragma unroll
-            for (int x = (c * F8X) / DCH; x < ((c + 1) * F8X) / DCH; ++x) issue_f8(t0 + BN, x);
-          } else {
-#pragma unroll
-            for (int x = (c * NLW) / DCH; x < ((c + 1) * NLW) / DCH; ++x) issue_part(t0 + BN, nxt, x);
-          }
+          for (int x = (c * NLW) / DCH; x < ((c + 1) * NLW) / DCH; ++x) issue_part(t0 + BN, nxt, x);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the read of step c+PF ahead of MFMA c
       }
@@ -546,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         u32x4 bv;
 #pragma unroll
         for (int ld = 0; ld < 2; ++ld) {
-          const uint8_t* src = vb + (16 * kc + 4 * ld) * VRBX + 64 * cb;
+          const uint8_t* src = vb + (16 * kc + 4 * ld) * VRB + 64 * cb;
           const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src));
           const u32x2 rr = __builtin_bit_cast(u32x2, r);
           bv[2 * ld] = rr[0];
@@ -590,10 +388,6 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         __builtin_amdgcn_sched_barrier(0);   // later steps' reads stay ahead of this step's MFMAs
       }
     }
-    if (pf) {   // the other buffer is not read until barrier (A)
-      if (F8) store_f8(nxt); else if (VK) store_rope(nxt);
-    }
-    load_idx(t0 + 2 * BN);   // keys of the tile the next step copies
   };
   // Tiles go in pairs (one per buffer); an odd tile count skips the second
   // step of the last pair.  No copy follows the last tile.
@@ -624,18 +418,12 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         for (int i = 0; i < 16; ++i) O[rb][cb][i] = 0.f;
     l_run = 0.f;
     t_max = -INFINITY;
-    load_idx(k0);
     issue_tile(k0, buf0);
-    load_idx(k0 + BN);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (F8) store_f8(buf0); else if (VK) store_rope(buf0);
   }
 
   // ---- epilogue: row sums, partial results ---------------------------------
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  // absorbed: bf16 partials (its merge keeps the merged latent as a hi/lo
-  // pair, which leaves room for this rounding); materialised: float32
-  constexpr int PB = VK ? 2 : 4;                    // bytes per partial element
+  constexpr int PB = 4;                             // bytes per partial element (float32)
   constexpr int SROW = DV * PB + 16;                // padded staging row (bytes)
   static_assert((BM / 2) * SROW <= BUF, "O staging must fit in the tile buffers");
   // rows 0..31 staged in buf0, rows 32..63 in buf1
@@ -653,14 +441,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs p) {
         for (int q = 0; q < 4; ++q) {
           uint8_t* dst = srow(32 * rb + l32) + (col0 + 32 * cb + 8 * q + 4 * half) * PB;
           const f32x16& o = O[rb][cb];
-          if (VK) {
-            u32x2 v;
-            v[0] = pack_bf16(o[4 * q], o[4 * q + 1]);
-            v[1] = pack_bf16(o[4 * q + 2], o[4 * q + 3]);
-            *reinterpret_cast<u32x2*>(dst) = v;
-          } else {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
-          }
+          *reinterpret_cast<f32x4*>(dst) = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
         }
   }
   __syncthreads();
@@ -1193,9 +974,9 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(MergeUpArgs p) {
 // ---------------------------------------------------------------------------
 static inline unsigned grid_xcd(int n_items) { return (unsigned)(((n_items + kXcds - 1) / kXcds) * kXcds); }
 
-template <int DA, int DR, int DV, bool VK>
+template <int DA, int DR, int DV>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_bf16_kernel<DA, DR, DV, VK>), dim3(grid_xcd(a.n_items)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_bf16_kernel<DA, DR, DV>), dim3(grid_xcd(a.n_items)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1205,14 +986,14 @@ hipError_t materialized_attn_bf16(const MaterializedLaunch& q, hipStream_t st) {
   a.qa = (const uint16_t*)q.q_nope; a.qb = (const uint16_t*)q.q_pe;
   a.ka = (const uint16_t*)q.k; a.ka_ks = (long long)q.H * D; a.ka_hs = D;
   a.vv = (const uint16_t*)q.v; a.vv_ks = (long long)q.H * q.v_dim; a.vv_hs = q.v_dim;
-  a.off = q.off_dev; a.off0 = q.off0; a.kv1 = q.kv1; a.ws_o = q.ws_o; a.ws_ml = q.ws_ml;
-  a.B = q.B; a.L = q.L; a.H = q.H; a.hpr = 1; a.rows_slot = q.L; a.head_slots = q.H;
+  a.off = q.off_dev; a.off0 = q.off0; a.kv1 = q.kv1; a.ws_o = (float*)q.ws_o; a.ws_ml = q.ws_ml;
+  a.B = q.B; a.L = q.L; a.H = q.H; a.rows_slot = q.L;
   a.row_tiles = q.plan.row_tiles; a.chunk = q.plan.chunk; a.n_items = q.plan.n_items;
   a.rows_total = q.L * q.H; a.sl2 = q.scale * 1.4426950408889634f;
   // The kernel sees the query as [q_nope | q_pe] of width n + rope and K rows
   // of the same width; DA = n, DR = rope.
 #define MLA_MAT(N, RP, VD) \
-  if (q.n == N && q.rope == RP && q.v_dim == VD) return launch_attn<N, RP, VD, false>(a, st);
+  if (q.n == N && q.rope == RP && q.v_dim == VD) return launch_attn<N, RP, VD>(a, st);
   MLA_MAT(128, 64, 128) MLA_MAT(128, 64, 256) MLA_MAT(192, 64, 128) MLA_MAT(192, 64, 256)
   MLA_MAT(256, 64, 128) MLA_MAT(256, 64, 256) MLA_MAT(128, 0, 128) MLA_MAT(256, 0, 256)
   MLA_MAT(192, 0, 256) MLA_MAT(128, 0, 256) MLA_MAT(256, 0, 128) MLA_MAT(192, 0, 128)
