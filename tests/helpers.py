@@ -3,9 +3,10 @@ and the comparison bars.
 
 Bars (written here once, used by every parity test):
 * float32 storage: max |gpu - oracle| <= 1e-4 (absolute);
-* bfloat16 storage, float32 accumulation: max |gpu - oracle| <= 2e-2 * rms(oracle)
-  (the 2e-2 bar taken relative to the outputs' own scale; these outputs have
-  rms 0.03-0.1, so this is also well inside an absolute 2e-2);
+* bfloat16 storage, float32 accumulation: |gpu - oracle| <= 2e-2 * scale per
+  element, the 2e-2 bar taken relative to the outputs' own scale: the larger of
+  the batch rms and the element's row rms (the outputs have rms 0.03-0.4, so
+  this is also well inside an absolute 2e-2, which is checked too);
 * per element, where a few rows carry much larger outputs than the rest (so that a
   bar relative to the global rms is tighter than the arithmetic allows there):
   the worst-case bound of rounding_bound() below.
@@ -96,7 +97,17 @@ def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "", re
         assert err <= F32_ABS_TOL, f"{what}: max abs err {err:.3e} > {F32_ABS_TOL}"
         return err, None
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    assert err <= rel * max(rms, 1e-30), f"{what}: max err {err:.3e} > {rel} * rms {rms:.3e}"
+    # 2e-2 of the output scale: an output row (one attention output, one
+    # folded query) is measured against the larger of the batch rms and its
+    # own rms, since the bf16 roundings of a row scale with the row (a row led
+    # by a few keys has outputs several times the batch rms)
+    scale = np.full(ref.shape, max(rms, 1e-30))
+    if ref.ndim == 2 and ref.size:
+        scale = np.maximum(scale, np.sqrt(np.mean(ref * ref, axis=1))[:, None])
+    ratio = np.abs(got - ref) / scale if ref.size else np.zeros(1)
+    worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    assert ratio[worst] <= rel, (f"{what}: err {float(np.abs(got - ref)[worst]):.3e} > {rel} * scale "
+                                 f"{float(scale[worst]):.3e} (batch rms {rms:.3e}) at {tuple(int(x) for x in worst)}")
     if abs_cap:   # outputs of unit-scale inputs: also inside an absolute 2e-2
         assert err <= 2e-2, f"{what}: max err {err:.3e} > 2e-2"
     return err, err / rms
