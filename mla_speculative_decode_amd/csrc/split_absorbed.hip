@@ -1,37 +1,31 @@
-// split_absorbed.hip -- the split-KV kernel of the absorbed MLA route over a
-// bf16 latent cache (pages: "One guard, 110x off the verify step", section
-// "The defect": attend directly against the compressed latent and accumulate
-// in latent space).
+// split_absorbed.hip -- the split-KV kernels of the absorbed MLA route over the
+// latent cache (pages: "One guard, 110x off the verify step", section "The
+// defect": attend directly against the compressed latent and accumulate in
+// latent space).
 //
 // The absorbed route is multi-query attention with one shared key/value head:
 // every (row, head) pair of a sequence is a query of width 512 + rope against
 // the keys [c_kv | k_pe], and the values are c_kv itself.  A workgroup takes 64
-// query rows x one split of the sequence's positions, in tiles of 64 positions
-// held in LDS, and leaves unnormalised partial results (latent sums in bf16, the
-// row's base-2 reference and sum in float32) for the merge pass.
+// query rows x one split of the sequence's positions and leaves unnormalised
+// partial results (latent sums in bf16, the row's base-2 reference and sum in
+// float32) for the merge pass.
 //
-// Layout of the four waves:
-//   scores  wave w computes S^T for keys 16w .. 16w+15 of the tile against all
-//           64 query rows with 16x16x32 bf16 MFMAs: the query block of all 64
-//           rows stays in registers (B operand), and each key fragment read from
-//           LDS feeds four MFMAs (one per block of 16 rows);
-//   softmax base 2 against a fixed reference per row (the row's maximum over the
-//           split's first tile); a lane holds 4 keys of 4 rows, so P, the row
-//           sums and the running maxima need no exchange between lanes inside
-//           the tile loop; a split whose later scores exceed the reference by
-//           more than 2^64 runs again with the references raised;
-//   PV      O^T[512 x 64 rows] += V^T P^T with 32x32x16 MFMAs, wave w owning
-//           latent columns 128w .. 128w+127; P (bf16) comes from LDS, V^T
-//           fragments are read transposed from the row-major tile with
-//           ds_read_b64_tr_b16.
-// LDS: two latent tile buffers (the tile being scored and the next one, copied
-// in by direct global -> LDS loads spread over the score MFMAs, one 1 KB latent
-// row per wave instruction), one rope-key buffer (the next tile's rope keys are
-// copied in during PV, after every wave has scored the current ones), the rope
-// part of the query block (its latent part lives in registers), and P with
-// the per-row exchange slots in its pad column.  The selected-position form
-// (SEL) runs over a per-sequence list of cache positions instead of all of
-// them.
+// bf16 cache (absorbed_split_kernel): eight waves, two per SIMD, in two roles
+// that form a pipeline over tiles of 32 positions.  The scoring waves hold the
+// query block in registers and compute S^T with 16x16x32 bf16 MFMAs, then the
+// weights P = 2^(s - m) against a fixed reference per row (the row's maximum
+// over the split's first tile; a split whose later scores exceed it by more
+// than 2^64 runs again with raised references, so O is never rescaled); the PV
+// waves accumulate O^T = V^T P^T with 32x32x16 MFMAs, V^T read transposed from
+// the row-major tile (ds_read_b64_tr_b16), and copy the next tile in.  Scores
+// of tile k, PV of tile k - 1 and the copy of tile k + 1 share a phase.
+//
+// fp8 cache (absorbed_split_f8_kernel): the scores on the scaled fp8 matrix
+// cores with the queries block-quantised in the kernel; 32 query rows per
+// workgroup, two workgroups per CU.
+//
+// Both have a selected-position form (SEL) that runs over a per-sequence list
+// of cache positions instead of all of them.
 
 #include <algorithm>
 #include <type_traits>
@@ -88,491 +82,8 @@ __device__ __forceinline__ float group_sum(float x) {
 
 }  // namespace
 
-template <int DR, bool SEL>
-__global__ __launch_bounds__(256, 1) void absorbed_split_kernel(SplitArgs p) {
-  constexpr int DA = 512, DV = 512;
-  constexpr int BM = 64, BN = 64;
-  constexpr int KL = DA / 32;             // 32-wide k steps of the score MFMA over the latent part
-  constexpr int KR = DR / 32;             // ... over the rope part
-  // Latent LDS row: 1 KB + 48 B of pad, a stride of 48 mod 256 bytes: the 16
-  // rows a score fragment reads fall in 16 distinct bank groups, and the rows
-  // of a transposed V read in 4 distinct 64-byte windows.
-  constexpr int LRB = DA * 2 + 48;
-  constexpr int RCH = DR / 8;             // 16-byte rope chunks per row (8 at rope 64)
-  constexpr int RRB = RCH * 16;           // rope LDS row: unpadded, chunk c of row r stored at c ^ (r & 7)
-  constexpr int RINST = BN * RCH / kWave; // rope direct-load wave instructions per tile (8 rows each)
-  constexpr int BUF = BN * LRB;
-  constexpr int RBUF = DR > 0 ? BN * RRB : 16;
-  constexpr int PRB = 9 * 16;             // P row: 64 keys (8 chunks) + one chunk holding 4 exchange floats
-  constexpr int CPW = DV / 4;             // value columns per wave
-  constexpr int NCB = CPW / 32;           // 32-column MFMA blocks per wave
-  constexpr int NLW = BN / 4;             // latent-row copy instructions per wave per tile
-  static_assert(DR % 32 == 0 && (DR == 0 || RCH == 8), "rope width 0 or 64");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
-  __shared__ __attribute__((aligned(16))) uint8_t krope[RBUF];   // rope keys of the tile being scored
-  __shared__ __attribute__((aligned(16))) uint8_t qrope[RBUF];   // rope part of the query block
-  __shared__ __attribute__((aligned(16))) uint8_t pl[BM * PRB];
-  __shared__ uint32_t pfd[kWave];   // landing slot of the L2 prefetch (never read)
-  // per-row exchange slots: row r's four floats (one per wave) in P's pad chunk
-  auto red = [&](int row) -> float* { return reinterpret_cast<float*>(pl + row * PRB + 128); };
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;          // score layout: row block lane, key group
-  const int half = lane >> 5, l32 = lane & 31;        // PV layout
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int item = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, p.n_items));
-  if (item >= p.n_items) return;
-  const int rt = __builtin_amdgcn_readfirstlane(item % p.row_tiles);
-  const int g = __builtin_amdgcn_readfirstlane(item / p.row_tiles);
-  int b = 0, ps = g, off_b = p.off0, Kv = p.kv1;
-  if (p.B > 1) {
-    const SplitPos sp = decode_split(g, p.off, p.B, p.chunk);
-    b = __builtin_amdgcn_readfirstlane(sp.b);
-    ps = __builtin_amdgcn_readfirstlane(sp.s);
-    off_b = __builtin_amdgcn_readfirstlane(p.off[b]);
-    Kv = __builtin_amdgcn_readfirstlane(p.off[b + 1]) - off_b;
-  }
-  // SEL: off_b / Kv index the packed selection; cache rows start at koff[b] and
-  // the causal bound comes from the cache length Kt.
-  long long p0 = off_b;
-  int Kt = Kv;
-  if (SEL) {
-    p0 = p.B > 1 ? (long long)__builtin_amdgcn_readfirstlane(p.koff[b]) : (long long)p.koff0;
-    Kt = p.B > 1 ? __builtin_amdgcn_readfirstlane(p.koff[b + 1]) - (int)p0 : p.kvt1;
-  }
-  const int sel0 = off_b;
-  const int k0 = __builtin_amdgcn_readfirstlane(ps * p.chunk);
-  const int k1 = __builtin_amdgcn_readfirstlane(min(Kv, k0 + p.chunk));
-  // SEL: entries at or above a row's bound Kt - L + i + 1 are among the
-  // selection's last L - 1; lane j holds the j-th entry from the end.
-  const int ntail = min(p.L - 1, Kv);
-  int tailv = -1;
-  if (SEL && ntail <= kWave && lane < ntail) tailv = p.sel[sel0 + Kv - 1 - lane];
-  auto visible = [&](int i) -> int {   // split indices query row i may see
-    const int bound = Kt - p.L + i + 1;
-    if (!SEL) return bound;
-    if (ntail <= kWave) {
-      int above = 0;
-      for (int j = 0; j < ntail; ++j) above += __builtin_amdgcn_readlane(tailv, j) >= bound ? 1 : 0;
-      return Kv - above;
-    }
-    int lo = 0, hi = Kv;               // long blocks: binary search of the increasing selection
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (p.sel[sel0 + mid] < bound) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-  };
-  // SEL: cache positions of the 64 keys of the next tile to copy (lane j: key j)
-  int sidx = 0;
-  auto load_idx = [&](int t0) {
-    if (SEL) sidx = min(max(p.sel[sel0 + min(t0 + lane, k1 - 1)], 0), Kt - 1);
-  };
-  const int idx0 = rt * BM;
-  const int nrows = min(BM, p.rows - idx0);
-
-  const uint16_t* lbase = uniform_ptr(p.c_kv + p0 * DA);
-  const uint16_t* rseq = p.k_pe + p0 * DR;
-
-  // ---- tile copy: global -> LDS --------------------------------------------
-  // latent row `key` of the tile: one wave instruction (uniform row address,
-  // lane l copies bytes 16 l .. 16 l + 15)
-  auto issue_part = [&](int t0, uint8_t* kdst, int x) {
-    const int key = wu + 4 * x;
-    const int kr = SEL ? __builtin_amdgcn_readlane(sidx, key) : __builtin_amdgcn_readfirstlane(min(t0 + key, k1 - 1));
-    __builtin_amdgcn_global_load_lds(lbase + (long long)kr * DA + 8 * lane,
-                                     (__attribute__((address_space(3))) void*)(kdst + key * LRB), 16, 0, 0);
-  };
-  // rope keys of the tile into krope: instruction j fills rows 8 j .. 8 j + 7;
-  // lane l lands in row 8 j + l / 8, physical chunk l % 8, so it loads logical
-  // chunk (l % 8) ^ (l / 8) of that row
-  const int rsw = (lane & 7) ^ (lane >> 3);
-  auto issue_rope = [&](int t0) {
-#pragma unroll
-    for (int x = 0; x < RINST / 4; ++x) {
-      const int j = wu + 4 * x;
-      const int key = 8 * j + (lane >> 3);
-      const int kr = SEL ? __shfl(sidx, key, kWave) : min(t0 + key, k1 - 1);
-      __builtin_amdgcn_global_load_lds(rseq + (long long)kr * DR + 8 * rsw,
-                                       (__attribute__((address_space(3))) void*)(krope + 1024 * j), 16, 0, 0);
-    }
-  };
-  auto issue_tile = [&](int t0, uint8_t* kdst) {
-    if (DR > 0) issue_rope(t0);
-#pragma unroll
-    for (int x = 0; x < NLW; ++x) issue_part(t0, kdst, x);
-  };
-
-  // ---- rows of this lane in the score layout: 16 rb + l16, rb < 4 ----------
-  int kend[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int idx = idx0 + min(16 * rb + l16, nrows - 1);
-    kend[rb] = min(k1, visible(idx / p.H));
-  }
-  const int kfull = __builtin_amdgcn_readfirstlane(min(k1, visible(idx0 / p.H)));   // every row sees these
-
-  load_idx(k0);
-  issue_tile(k0, buf0);   // first tile in flight while the queries load
-  load_idx(k0 + BN);
-
-  // ---- query block: latent part -> buf1 -> registers; rope part -> qrope -----
-  // Rows past the last query row repeat it (their results are never stored).
-  u32x4 qf[4][KL];
-  {
-    const long long qflat0 = (long long)b * p.rows + idx0;
-    const uint16_t* qlseq = p.q_lat + qflat0 * DA + 8 * lane;
-#pragma unroll
-    for (int x = 0; x < BM / 4; ++x) {
-      const int row = wu + 4 * x;
-      __builtin_amdgcn_global_load_lds(qlseq + (long long)min(row, nrows - 1) * DA,
-                                       (__attribute__((address_space(3))) void*)(buf1 + row * LRB), 16, 0, 0);
-    }
-    if (DR > 0) {   // same swizzled layout as the rope keys
-#pragma unroll
-      for (int x = 0; x < RINST / 4; ++x) {
-        const int j = wu + 4 * x;
-        const int row = 8 * j + (lane >> 3);
-        __builtin_amdgcn_global_load_lds(p.q_pe + (qflat0 + min(row, nrows - 1)) * DR + 8 * rsw,
-                                         (__attribute__((address_space(3))) void*)(qrope + 1024 * j), 16, 0, 0);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // the query fragments are read from buf1 by the first tile's score loop
-    // (each as its MFMAs need it); tile 1 is copied into buf1 after that
-  }
-
-  // ---- running state (score layout: row 16 rb + l16) -----------------------
-  float m_ref[4], l_part[4], t_max[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) { m_ref[rb] = -INFINITY; l_part[rb] = 0.f; t_max[rb] = -INFINITY; }
-  bool rerun = false;
-  f32x16 O[2][NCB];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) O[rb][cb][i] = 0.f;
-
-  // per-lane LDS offsets (bytes) within a buffer; the rest are immediates
-  const int kq_off = (16 * w + l16) * LRB + 16 * lg;                     // + 64 ks
-  // rope rows (row & 7 == l16 & 7 in both): chunk c at (c ^ (l16 & 7)), c = 4 ks + lg
-  auto rope_off = [&](int ks) { return 16 * ((4 * ks + lg) ^ (l16 & 7)); };
-  const int kr_off = (16 * w + l16) * RRB;                               // rope keys
-  const int qr_off = l16 * RRB;                                          // rope queries: + 16 rb RRB
-  const int G = lane >> 4, s16 = lane & 15;
-  const int tr_off = (8 * (G >> 1) + (s16 >> 2)) * LRB + (w * CPW + 16 * (G & 1) + 4 * (s16 & 3)) * 2;
-  const int pa_off = l32 * PRB + 16 * half;                              // + rb*32*PRB + 32 kc
-  const int pw_off = l16 * PRB + (16 * w + 4 * lg) * 2;                  // + 16 rb * PRB
-
-  // Cache lines of the split's positions [ta, tb) -> L2 ahead of their tile
-  // copies: this workgroup takes the positions p with (p - k0) % row_tiles == rt,
-  // one 4-byte load per 128-byte line into a dummy LDS slot (the row tiles of a
-  // split run on one XCD and share its L2).  Each tile fetches the lines of the
-  // tile pf_ahead tiles on; the first one fetches the tiles up to there.
-  const int kPfAhead = p.pf_ahead;
-  auto prefetch_range = [&](int ta, int tb) {
-    if (SEL) return;
-    constexpr int LPP = DA / 64 + (DR > 0 ? 1 : 0);   // 128-byte lines per position
-    tb = min(tb, k1);
-    const int rel = ta - k0;
-    const int first = ta + ((rt - rel % p.row_tiles) + p.row_tiles) % p.row_tiles;
-    const int cnt = first < tb ? (tb - 1 - first) / p.row_tiles + 1 : 0;
-    const int nl = cnt * LPP;
-    for (int e0 = 0; e0 < nl; e0 += 256) {
-      const int e = min(e0 + tid, nl - 1);
-      const int j = e / LPP, ln = e - j * LPP;
-      const long long pos = p0 + first + (long long)p.row_tiles * j;
-      const uint16_t* src = ln < DA / 64 ? p.c_kv + pos * DA + 64 * ln : p.k_pe + pos * DR;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)pfd, 4, 0, 0);
-    }
-  };
-
-  // Scores of one tile over the latent part.  LQ: the first tile, whose query
-  // fragments are read from buf1 as the MFMAs need them (two k steps ahead).
-  // NC: how many of the next tile's 16 latent-row copies to issue here (the
-  // rest go with PV, so that neither phase carries all of the copy's LDS writes).
-  auto latent_scores = [&](f32x4* acc, const uint8_t* cur, uint8_t* nxt, int t1, auto lq, auto nc) {
-    constexpr bool LQ = decltype(lq)::value;
-    constexpr int NC = decltype(nc)::value;
-    constexpr int PF = 4, QPF = 2;
-    const uint8_t* kq = cur + kq_off;
-    const uint8_t* qsrc = buf1 + l16 * LRB + 16 * lg;
-    u32x4 ka[PF];
-    if (LQ) {
-#pragma unroll
-      for (int ks = 0; ks < QPF; ++ks)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) qf[rb][ks] = *reinterpret_cast<const u32x4*>(qsrc + 16 * rb * LRB + 64 * ks);
-    }
-#pragma unroll
-    for (int c = 0; c < PF; ++c) ka[c] = *reinterpret_cast<const u32x4*>(kq + 64 * c);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < KL; ++ks) {
-      const u32x4 a = ka[ks % PF];
-      if (ks + PF < KL) ka[ks % PF] = *reinterpret_cast<const u32x4*>(kq + 64 * (ks + PF));
-      if (LQ && ks + QPF < KL) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          qf[rb][ks + QPF] = *reinterpret_cast<const u32x4*>(qsrc + 16 * rb * LRB + 64 * (ks + QPF));
-      }
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[rb] = mfma16(a, qf[rb][ks], acc[rb]);
-      if (NC > 0) {
-#pragma unroll
-        for (int x = (ks * NC) / KL; x < ((ks + 1) * NC) / KL; ++x) issue_part(t1, nxt, x);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // one 64-position tile: scores from `cur`, copy of the next tile into `nxt`
-  auto step = [&](int t0, const uint8_t* cur, uint8_t* nxt, bool pf) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // (A) tile t visible; PV(t-1) done, so the other buffer and pl are free
-    // the split's first tile on the first pass: the query fragments come from
-    // buf1 during its scores, so the next tile's copy waits for PV
-    const bool first = t0 == k0 && !rerun;
-    if (!rerun) {
-      if (first) prefetch_range(t0 + BN, t0 + (kPfAhead + 1) * BN);
-      else prefetch_range(t0 + kPfAhead * BN, t0 + (kPfAhead + 1) * BN);
-    }
-
-    // ---- scores: S^T [16 keys x 64 rows] -----------------------------------
-    f32x4 acc[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // rope part first, from LDS on both sides (its registers are free again for the latent part)
-#pragma unroll
-    for (int ks = 0; ks < KR; ++ks) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(krope + kr_off + rope_off(ks));
-      u32x4 bq[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) bq[rb] = *reinterpret_cast<const u32x4*>(qrope + qr_off + 16 * rb * RRB + rope_off(ks));
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[rb] = mfma16(a, bq[rb], acc[rb]);
-    }
-    using I0 = std::integral_constant<int, 0>;
-    using IH = std::integral_constant<int, NLW / 2>;
-    if (first) latent_scores(acc, cur, nxt, t0 + BN, std::true_type{}, I0{});
-    else if (pf) latent_scores(acc, cur, nxt, t0 + BN, std::false_type{}, IH{});
-    else latent_scores(acc, cur, nxt, t0 + BN, std::false_type{}, I0{});
-    // latent-row copies of the next tile still to issue (during PV): x0 .. NLW - 1
-    const int x0 = first ? 0 : NLW / 2;
-    // acc[rb][i] = q . k for key t0 + 16 w + 4 lg + i, row 16 rb + l16.
-    if (t0 + BN > kfull) {   // a tile past some row's causal end (uniform branch)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t0 + 16 * w + 4 * lg + i >= kend[rb]) acc[rb][i] = -INFINITY;
-    }
-    // raw maxima (scaled once at the end: the scale is positive)
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-      t_max[rb] = fmaxf(fmaxf(t_max[rb], fmaxf(acc[rb][0], acc[rb][1])), fmaxf(acc[rb][2], acc[rb][3]));
-    // The first tile of the split sets each row's reference (a row sees a prefix
-    // of the split's positions, so its first finite scores are in this tile).
-    if (t0 == k0 && !rerun) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const float mx = group_max(fmaxf(fmaxf(acc[rb][0], acc[rb][1]), fmaxf(acc[rb][2], acc[rb][3])));
-        if (lg == 0) red(16 * rb + l16)[w] = mx * p.sl2;
-      }
-      lds_barrier();
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const f32x4 r4 = *reinterpret_cast<const f32x4*>(red(16 * rb + l16));
-        m_ref[rb] = fmaxf(fmaxf(r4[0], r4[1]), fmaxf(r4[2], r4[3]));
-      }
-    }
-    // P = 2^(s - m) in bf16 (rows without a finite reference use 0: their masked
-    // keys give 0); the row sums add the rounded weights that PV uses
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const float mb = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
-      float e[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(acc[rb][i], p.sl2, -mb));
-      u32x2 v;
-      v[0] = pack_bf16(e[0], e[1]);
-      v[1] = pack_bf16(e[2], e[3]);
-      *reinterpret_cast<u32x2*>(pl + pw_off + 16 * rb * PRB) = v;
-      l_part[rb] = add_bf16x2(v[1], add_bf16x2(v[0], l_part[rb]));
-    }
-    lds_barrier();  // (B) P visible (the next tile's copy stays in flight)
-    // every wave has scored this tile's rope keys: copy the next tile's in
-    if (DR > 0 && pf) issue_rope(t0 + BN);
-
-    // ---- PV: O^T [CPW columns x 64 rows] for this wave's columns --------------
-    {
-      const uint8_t* pa = pl + pa_off;
-      const uint8_t* vb = cur + tr_off;
-      auto vfrag = [&](int kc, int cb) {
-        u32x4 bv;
-#pragma unroll
-        for (int ld = 0; ld < 2; ++ld) {
-          const uint8_t* src = vb + (16 * kc + 4 * ld) * LRB + 64 * cb;
-          const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src));
-          const u32x2 rr = __builtin_bit_cast(u32x2, r);
-          bv[2 * ld] = rr[0];
-          bv[2 * ld + 1] = rr[1];
-        }
-        return bv;
-      };
-      constexpr int NSTEP = (BN / 16) * NCB;
-      constexpr int VPF = 3;
-      u32x4 a[BN / 16][2];
-      u32x4 vq[VPF];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) a[0][rb] = *reinterpret_cast<const u32x4*>(pa + rb * 32 * PRB);
-#pragma unroll
-      for (int st = 0; st < VPF; ++st) {
-        if (st > 0 && st % NCB == 0) {
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            a[st / NCB][rb] = *reinterpret_cast<const u32x4*>(pa + rb * 32 * PRB + 32 * (st / NCB));
-        }
-        vq[st] = vfrag(st / NCB, st % NCB);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
-        const int kc = st / NCB, cb = st % NCB;
-        const u32x4 bcur = vq[st % VPF];
-        const int sn = st + VPF;
-        if (sn < NSTEP) {
-          if (sn % NCB == 0) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-              a[sn / NCB][rb] = *reinterpret_cast<const u32x4*>(pa + rb * 32 * PRB + 32 * (sn / NCB));
-          }
-          vq[st % VPF] = vfrag(sn / NCB, sn % NCB);
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) O[rb][cb] = mfma32(bcur, a[kc][rb], O[rb][cb]);   // O^T += V^T P^T
-        // this PV step's share of the next tile's remaining latent-row copies
-        // (copy x at PV step x; the first tile's at every step, later ones' at steps 8 ..)
-        if (pf && st >= x0) issue_part(t0 + BN, nxt, st);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    load_idx(t0 + 2 * BN);
-  };
-
-  for (;;) {
-    for (int t0 = k0; t0 < k1; t0 += 2 * BN) {
-      step(t0, buf0, buf1, t0 + BN < k1);
-      if (t0 + BN < k1) step(t0 + BN, buf1, buf0, t0 + 2 * BN < k1);
-    }
-    // Did some row's scores exceed its reference by more than 2^kRefSlack?  Then
-    // its P, O and l may have overflowed: raise every reference to the row's
-    // maximum over the whole split and run the split again (the second pass
-    // cannot trigger another: its references bound every score).
-    __syncthreads();   // every wave is done with red and the tile buffers
-    float tm[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const float mx = group_max(t_max[rb]);
-      if (lg == 0) red(16 * rb + l16)[w] = mx * p.sl2;
-    }
-    lds_barrier();
-    bool over = false;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const f32x4 r4 = *reinterpret_cast<const f32x4*>(red(16 * rb + l16));
-      tm[rb] = fmaxf(fmaxf(r4[0], r4[1]), fmaxf(r4[2], r4[3]));
-      over = over || (m_ref[rb] != -INFINITY && tm[rb] > m_ref[rb] + kRefSlack);
-    }
-    // every wave holds all 64 rows, so the decision is uniform over the
-    // workgroup; the second pass never runs a third (its references bound every
-    // score; checked explicitly so that no input, NaN included, loops)
-    if (rerun || __ballot(over) == 0) break;
-    rerun = true;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      m_ref[rb] = m_ref[rb] == -INFINITY ? m_ref[rb] : fmaxf(m_ref[rb], tm[rb]);
-      l_part[rb] = 0.f;
-      t_max[rb] = -INFINITY;
-    }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) O[rb][cb][i] = 0.f;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();   // the maxima are read before red is written again
-    load_idx(k0);
-    issue_tile(k0, buf0);
-    load_idx(k0 + BN);
-  }
-
-  // ---- epilogue: row sums, partial results ---------------------------------
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  constexpr int SROW = LRB;                         // padded staging row (bytes), bf16
-  static_assert((BM / 2) * SROW <= BUF, "O staging must fit in the tile buffers");
-  auto srow = [&](int row) -> uint8_t* { return row < BM / 2 ? buf0 + row * SROW : buf1 + (row - BM / 2) * SROW; };
-  __syncthreads();   // every wave is done with the tile buffers and red
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const float s = group_sum(l_part[rb]);
-    if (lg == 0) red(16 * rb + l16)[w] = s;
-  }
-  {
-    // lane holds row 32 rb + l32, columns col0 + 32 cb + 8 q + 4 half + (0..3)
-    const int col0 = w * CPW;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint8_t* dst = srow(32 * rb + l32) + (col0 + 32 * cb + 8 * q + 4 * half) * 2;
-          const f32x16& o = O[rb][cb];
-          u32x2 v;
-          v[0] = pack_bf16(o[4 * q], o[4 * q + 1]);
-          v[1] = pack_bf16(o[4 * q + 2], o[4 * q + 3]);
-          *reinterpret_cast<u32x2*>(dst) = v;
-        }
-  }
-  __syncthreads();
-  const long long gro = (long long)g * p.rows;
-  if (w == 0 && lg == 0) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int row = 16 * rb + l16;
-      if (row < nrows) {
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(red(row));
-        *reinterpret_cast<f32x2*>(p.ws_ml + (gro + idx0 + row) * 2) = f32x2{m_ref[rb], (s4[0] + s4[1]) + (s4[2] + s4[3])};
-      }
-    }
-  }
-  {
-    constexpr int V16 = DV * 2 / 16;                // 16-byte chunks per row
-    constexpr int NST = BM * V16 / 256;
-    uint8_t* wso = reinterpret_cast<uint8_t*>(p.ws_o);
-    u32x4 v[NST];
-#pragma unroll
-    for (int j = 0; j < NST; ++j) {
-      const int e = tid + 256 * j;
-      v[j] = *reinterpret_cast<const u32x4*>(srow(e / V16) + 16 * (e % V16));
-    }
-#pragma unroll
-    for (int j = 0; j < NST; ++j) {
-      const int e = tid + 256 * j;
-      const int row = e / V16;
-      if (row < nrows) st16(wso + ((gro + idx0 + row) * DV) * 2 + 16 * (e % V16), v[j]);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// The same split over the fp8 form of the latent cache (E4M3 codes of each
+// The split over the fp8 form of the latent cache (E4M3 codes of each
 // position's row [c_kv | k_pe] with one power-of-two scale per position).
 //
 //   scores  on the scaled fp8 MFMA (16x16x128): the query block is quantised
@@ -581,15 +92,21 @@ __global__ __launch_bounds__(256, 1) void absorbed_split_kernel(SplitArgs p) {
 //           |q| <= 448 x scale; the keys' codes come straight from LDS, with
 //           their position's scale as the A-side block scale.  The rope part
 //           is one more k step whose upper half is zero.
-//   softmax as above; each weight is then multiplied by its key's scale (a
-//           power of two, so bf16(P) x 2^k is exact) before it goes to LDS, and
-//           the row sums add the unscaled weights.
-//   PV      bf16 MFMAs as above; a V^T fragment is one transposed byte read
-//           (ds_read_b64_tr_b8: 8 keys of one column) widened to bf16 (codes are
-//           exact in bf16), the scale having gone into P.
-// LDS: two tile buffers of 64 code rows (row stride DW + 16 bytes: the 16 rows a
-// score fragment reads fall in distinct 16-byte bank groups) followed by the
-// tile's 64 scales, then P; the epilogue stages O in the two buffers.
+//   softmax base 2 against a fixed reference per row (the row's maximum over
+//           the split's first tile; a split whose later scores exceed it by
+//           more than 2^64 runs again with raised references); each weight is
+//           then multiplied by its key's scale (a power of two, so bf16(P) x 2^k
+//           is exact) before it goes to LDS, and the row sums add the unscaled
+//           weights.
+//   PV      O^T += V^T P^T on bf16 32x32x16 MFMAs; a V^T fragment is one
+//           transposed byte read (ds_read_b64_tr_b8: 8 keys of one column)
+//           widened to bf16 (codes are exact in bf16), the scale having gone
+//           into P.
+// A workgroup takes 32 query rows (two workgroups share a CU, so one's softmax
+// and barriers overlap the other's MFMAs).  LDS: two tile buffers, each 64
+// latent code rows (512 bytes, unpadded, 16-byte chunks XOR-swizzled by row),
+// 64 rope code rows and the tile's 64 scales; then P; the epilogue stages O
+// in a tile buffer.
 // ---------------------------------------------------------------------------
 namespace {
 // x -> E4M3 codes of x / s (nearest, ties to even; |x| <= 448 s), four per word
@@ -613,6 +130,26 @@ __device__ __forceinline__ void dma(const void* gsrc, const void* lds_dst) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m) : "memory");
   else
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(m) : "memory");
+}
+// the same with the LDS destination given as an LDS address (uniform)
+template <int BYTES>
+__device__ __forceinline__ void dma_to(const void* gsrc, uint32_t lds_addr) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
+  if (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(m) : "memory");
+}
+// the same with an immediate byte offset on the global address; the
+// instruction adds it to the LDS address as well, so M0 is set OFF lower
+template <int OFF>
+__device__ __forceinline__ void dma16_off(const void* gsrc, uint32_t lds_addr) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr - OFF);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(gsrc), "s"(m), "i"(OFF)
+               : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 // mfma16_f8 with B's scale in byte `sel` of scale_b (sel known once the caller's
 // loop is unrolled)
@@ -1132,6 +669,518 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
 }
 
 // ---------------------------------------------------------------------------
+// The bf16 split with specialised waves, two per SIMD.  Waves 0..3 score:
+// wave (kw, rw) takes 16 of a 32-position tile's keys (16 kw ..) against 32 of
+// the query rows (32 rw ..), query block in registers, and writes P; waves 4..7
+// form O^T for latent columns 128 (w - 4) .. + 127 of all 64 rows from the
+// previous tile's P.  Phase k of a split scores tile k, runs PV of tile k - 1
+// and copies tile k + 1, so the scoring and PV work of a phase overlap and each
+// phase ends with one barrier; each SIMD holds one scoring and one PV wave, so
+// it interleaves the two instruction streams (a single wave issues at most one
+// instruction every four cycles).  LDS: three latent tile buffers (tile k is
+// scored in phase k, multiplied in phase k + 1, and its buffer refilled with
+// tile k + 3 in phase k + 2), two rope-key buffers and two P buffers (each read
+// in one phase only), the rope part of the query block.  The PV waves copy the
+// next tile (direct global -> LDS loads issued as inline asm, which the
+// compiler does not track, spread over their MFMAs) and wait for their copies
+// (vmcnt) before the barrier that ends the phase; the scoring waves fetch the
+// split's cache lines into L2 ahead of the copies (one load instruction a
+// phase) and never wait for those loads inside the tile loop, so the fetches
+// run many phases ahead.
+// ---------------------------------------------------------------------------
+template <int DR, bool SEL>
+__global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
+  constexpr int DA = 512, DV = 512;
+  constexpr int BM = 64, BN = 32;
+  constexpr int KL = DA / 32;             // 32-wide k steps of the score MFMA over the latent part
+  constexpr int KR = DR / 32;             // ... over the rope part
+  constexpr int LRB = DA * 2 + 48;        // latent LDS row (48 mod 256 bytes: conflict-free fragment reads)
+  constexpr int RCH = DR / 8;             // 16-byte rope chunks per row
+  constexpr int RRB = RCH * 16;           // rope LDS row: chunk c of row r stored at c ^ (r & 7)
+  constexpr int BUF = BN * LRB;
+  constexpr int RBUF = DR > 0 ? BN * RRB : 16;
+  constexpr int QRBUF = DR > 0 ? BM * RRB : 16;
+  constexpr int PRB = BN * 2 + 16;        // P row: 32 keys + pad (80 bytes: conflict-free reads and writes)
+  constexpr int PBUF = BM * PRB;
+  constexpr int CPW = DV / 4;             // latent columns per PV wave
+  constexpr int NCB = CPW / 32;           // 32-column MFMA blocks per PV wave
+  constexpr int SROW = LRB;               // epilogue staging row
+  static_assert(DR == 0 || (DR == 64 && BN * RCH == 4 * kWave), "rope width 0 or 64: one rope copy per wave");
+  static_assert(BM * SROW <= 3 * BUF, "O staging fits in the tile buffers");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lat[3 * BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t krope[2 * RBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t qrope[QRBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t pl[2 * PBUF];
+  __shared__ __attribute__((aligned(16))) float red[BM * 2];   // per row: one float per key half
+  __shared__ float mref[BM];                                   // per row: the softmax reference
+  __shared__ uint32_t pfd[kWave];                              // landing slot of the L2 prefetch (never read)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int l16 = lane & 15, lg = lane >> 4;          // score layout: row block lane, key group
+  const int half = lane >> 5, l32 = lane & 31;        // PV layout
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int item = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, p.n_items));
+  if (item >= p.n_items) return;
+  const int rt = __builtin_amdgcn_readfirstlane(item % p.row_tiles);
+  const int g = __builtin_amdgcn_readfirstlane(item / p.row_tiles);
+  int b = 0, ps = g, off_b = p.off0, Kv = p.kv1;
+  if (p.B > 1) {
+    const SplitPos sp = decode_split(g, p.off, p.B, p.chunk);
+    b = __builtin_amdgcn_readfirstlane(sp.b);
+    ps = __builtin_amdgcn_readfirstlane(sp.s);
+    off_b = __builtin_amdgcn_readfirstlane(p.off[b]);
+    Kv = __builtin_amdgcn_readfirstlane(p.off[b + 1]) - off_b;
+  }
+  // SEL: off_b / Kv index the packed selection; cache rows start at koff[b] and
+  // the causal bound comes from the cache length Kt.
+  long long p0 = off_b;
+  int Kt = Kv;
+  if (SEL) {
+    p0 = p.B > 1 ? (long long)__builtin_amdgcn_readfirstlane(p.koff[b]) : (long long)p.koff0;
+    Kt = p.B > 1 ? __builtin_amdgcn_readfirstlane(p.koff[b + 1]) - (int)p0 : p.kvt1;
+  }
+  const int sel0 = off_b;
+  const int k0 = __builtin_amdgcn_readfirstlane(ps * p.chunk);
+  const int k1 = __builtin_amdgcn_readfirstlane(min(Kv, k0 + p.chunk));
+  const int T = (k1 - k0 + BN - 1) / BN;   // tiles of the split
+  // SEL: entries at or above a row's bound Kt - L + i + 1 are among the
+  // selection's last L - 1; lane j holds the j-th entry from the end.
+  const int ntail = min(p.L - 1, Kv);
+  int tailv = -1;
+  if (SEL && ntail <= kWave && lane < ntail) tailv = p.sel[sel0 + Kv - 1 - lane];
+  auto visible = [&](int i) -> int {   // split indices query row i may see
+    const int bound = Kt - p.L + i + 1;
+    if (!SEL) return bound;
+    if (ntail <= kWave) {
+      int above = 0;
+      for (int j = 0; j < ntail; ++j) above += __builtin_amdgcn_readlane(tailv, j) >= bound ? 1 : 0;
+      return Kv - above;
+    }
+    int lo = 0, hi = Kv;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.sel[sel0 + mid] < bound) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  // SEL: cache positions of the keys of the tile being copied (lane j: key j)
+  // and of the one after it
+  int sidx = 0, sidx_next = 0;
+  auto load_idx = [&](int t0) {
+    if (SEL) sidx_next = min(max(p.sel[sel0 + min(t0 + lane, k1 - 1)], 0), Kt - 1);
+  };
+  const int idx0 = rt * BM;
+  const int nrows = min(BM, p.rows - idx0);
+  const uint16_t* lbase = uniform_ptr(p.c_kv + p0 * DA);
+  const uint16_t* rseq = p.k_pe + p0 * DR;
+
+  // ---- tile copies, by the PV waves (cw = 0..3): NCP load instructions each ----
+  // item j < NRC: rope block cw (rows 8 cw .. + 7; lane l fills row 8 cw + l / 8,
+  // stored chunk l % 8, so it loads logical chunk (l % 8) ^ (l / 8)); the rest:
+  // latent row cw + 4 (j - NRC), one 1 KB row per instruction.
+  constexpr int NRC = DR > 0 ? 1 : 0;
+  constexpr int NCP = NRC + BN / 4;
+  const int rsw = (lane & 7) ^ (lane >> 3);
+  const uint32_t lat_a = lds_addr(lat), krope_a = lds_addr(krope), qrope_a = lds_addr(qrope), pfd_a = lds_addr(pfd);
+  // nb: the latent buffer (0..2), rb: the rope buffer (0, 1)
+  const int cw = wu - 4;
+  auto copy_item = [&](int t0, int nb, int rb, int j) {
+    if (j < NRC) {
+      const int blk = cw;
+      const int key = 8 * blk + (lane >> 3);
+      const int kr = SEL ? __shfl(sidx, key, kWave) : min(t0 + key, k1 - 1);
+      dma_to<16>(rseq + (long long)kr * DR + 8 * rsw, krope_a + rb * RBUF + 1024 * blk);
+    } else {
+      const int key = cw + 4 * (j - NRC);
+      const int kr = SEL ? __builtin_amdgcn_readlane(sidx, key) : __builtin_amdgcn_readfirstlane(min(t0 + key, k1 - 1));
+      dma_to<16>(lbase + (long long)kr * DA + 8 * lane, lat_a + nb * BUF + key * LRB);
+    }
+  };
+  auto issue_tile = [&](int t0, int nb, int rb) {
+#pragma unroll
+    for (int j = 0; j < NCP; ++j) copy_item(t0, nb, rb, j);
+  };
+  // Cache lines of positions [ta, tb) of the split -> L2 ahead of their copy:
+  // this workgroup takes the positions p with (p - k0) % row_tiles == rt (the
+  // row tiles of a split run on one XCD and share its L2), one 4-byte load per
+  // 128-byte line (line e of the list for lane e; lanes past the list repeat
+  // its last line), one load instruction per call.
+  constexpr int LPP = DA / 64 + (DR > 0 ? 1 : 0);   // 128-byte lines per position
+  auto prefetch_lines = [&](int ta, int tb, int e) {
+    tb = min(tb, k1);
+    const int rel = ta - k0;
+    const int first = ta + ((rt - rel % p.row_tiles) + p.row_tiles) % p.row_tiles;
+    const int cnt = first < tb ? (tb - 1 - first) / p.row_tiles + 1 : 0;
+    const int nl = cnt * LPP;
+    long long pos = p0 + k0;
+    int ln = 0;
+    if (nl > 0) {
+      const int ee = min(e, nl - 1);
+      const int j = ee / LPP;
+      ln = ee - j * LPP;
+      pos = p0 + first + (long long)p.row_tiles * j;
+    }
+    const uint16_t* src = ln < DA / 64 ? p.c_kv + pos * DA + 64 * ln : p.k_pe + pos * DR;
+    dma_to<4>(src, pfd_a);
+  };
+  auto lgkm_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  auto full_barrier = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  const bool prefetch = !SEL;
+  const int kPfAhead = p.pf_ahead;   // tiles of BN positions
+
+  const long long qflat0 = (long long)b * p.rows + idx0;
+
+  const long long gro = (long long)g * p.rows;
+  if (wu < 4) {
+    // ======================= scoring waves ====================================
+    const int kw = wu & 1, rw = wu >> 1;   // keys 16 kw .., rows 32 rw ..
+    const int srow = 32 * rw + l16;       // + 16 rb: this lane's rows
+    // the query block's latent part -> the staging rows (tile buffers 1 and 2,
+    // idle until the copy of tile 1), one 1 KB row per instruction (rows past
+    // the last query row repeat it; their results are never stored)
+    static_assert(BM * LRB <= 2 * BUF, "query staging fits in two tile buffers");
+#pragma unroll
+    for (int x = 0; x < BM / 4; ++x) {
+      const int row = wu + 4 * x;
+      dma_to<16>(p.q_lat + (qflat0 + min(row, nrows - 1)) * DA + 8 * lane, lat_a + BUF + row * LRB);
+    }
+    int kend[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) kend[rb] = min(k1, visible((idx0 + min(srow + 16 * rb, nrows - 1)) / p.H));
+    const int kfull = __builtin_amdgcn_readfirstlane(min(k1, visible(idx0 / p.H)));   // every row sees these
+    full_barrier();   // the query block, tile 0 (copied by the PV waves) in LDS
+    // query block, latent part, from its staging rows into registers in the B
+    // layout of the 16x16x32 MFMA: lane l holds row 32 rw + 16 rb + l % 16, k =
+    // 32 ks + 8 (l / 16) ..; kept in accumulation registers (the MFMA reads its
+    // B operand from there)
+    u32x4 qf[2][KL];
+    {
+      const uint8_t* qsrc = lat + BUF + srow * LRB + 16 * lg;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int ks = 0; ks < KL; ++ks) {
+          qf[rb][ks] = *reinterpret_cast<const u32x4*>(qsrc + 16 * rb * LRB + 64 * ks);
+          asm("" : "+a"(qf[rb][ks]));
+        }
+    }
+    // ... and its rope part (vector registers)
+    auto rope_off = [&](int ks) { return 16 * ((4 * ks + lg) ^ (l16 & 7)); };
+    const int qr_off = srow * RRB;                                         // + 16 rb RRB
+    u32x4 qr[2][KR > 0 ? KR : 1];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < KR; ++ks) qr[rb][ks] = *reinterpret_cast<const u32x4*>(qrope + qr_off + 16 * rb * RRB + rope_off(ks));
+    lgkm_barrier();   // the staging rows are free for tile 1
+    // the split's first lines -> L2 (tiles 1 .. kPfAhead); not waited for
+    if (prefetch) {
+      const int ta = k0 + BN, tb = min(k1, k0 + (kPfAhead + 1) * BN);
+      const int first = ta + ((rt - BN % p.row_tiles) + p.row_tiles) % p.row_tiles;
+      const int nl = (first < tb ? (tb - 1 - first) / p.row_tiles + 1 : 0) * LPP;
+      for (int e0 = 0; e0 < nl; e0 += 256) prefetch_lines(ta, tb, e0 + tid);
+    }
+
+    float m_ref[2], l_part[2], t_max[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) { m_ref[rb] = -INFINITY; l_part[rb] = 0.f; t_max[rb] = -INFINITY; }
+    bool rerun = false;
+    const int kq_off = (16 * kw + l16) * LRB + 16 * lg;                    // + 64 ks
+    const int kr_off = (16 * kw + l16) * RRB;
+    const int pw_off = srow * PRB + (16 * kw + 4 * lg) * 2;                // + 16 rb PRB
+    for (;;) {
+      const uint8_t* cur = lat;           // tile k's buffer
+      int nb = 1;                         // tile k + 1's (0..2)
+      for (int k = 0; k <= T; ++k) {
+        const int t0 = k0 + k * BN;
+        // the cache lines of tile k + kPfAhead + 1 (a quarter of them per wave)
+        if (prefetch && !rerun) prefetch_lines(t0 + (kPfAhead + 1) * BN, t0 + (kPfAhead + 2) * BN, tid);
+        if (k < T) {
+          const uint8_t* kro = krope + (k & 1) * RBUF;
+          // ---- scores: S^T [16 keys x 32 rows] ---------------------------------
+          f32x4 acc[2];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          {
+            // k steps 0 .. KL - 1 over the latent part, then KR over the rope
+            // part, key fragments read PF steps ahead of their MFMAs
+            constexpr int PF = 4, NK = KL + KR;
+            const uint8_t* kq = cur + kq_off;
+            auto kfrag = [&](int ks) -> u32x4 {
+              return ks < KL ? *reinterpret_cast<const u32x4*>(kq + 64 * ks)
+                             : *reinterpret_cast<const u32x4*>(kro + kr_off + rope_off(ks - KL));
+            };
+            u32x4 ka[PF];
+#pragma unroll
+            for (int c = 0; c < PF; ++c) ka[c] = kfrag(c);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < NK; ++ks) {
+              const u32x4 a = ka[ks % PF];
+              if (ks + PF < NK) ka[ks % PF] = kfrag(ks + PF);
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb) acc[rb] = mfma16(a, ks < KL ? qf[rb][ks] : qr[rb][ks - KL], acc[rb]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          // acc[rb][i] = q . k for key t0 + 16 kw + 4 lg + i, row srow + 16 rb
+          if (t0 + BN > kfull) {   // a tile past some row's causal end (uniform branch)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (t0 + 16 * kw + 4 * lg + i >= kend[rb]) acc[rb][i] = -INFINITY;
+          }
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            t_max[rb] = fmaxf(fmaxf(t_max[rb], fmaxf(acc[rb][0], acc[rb][1])), fmaxf(acc[rb][2], acc[rb][3]));
+          // the split's first tile sets each row's reference (a row sees a
+          // prefix of the split's positions, so its first finite scores are here)
+          if (k == 0 && !rerun) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              const float mx = group_max(fmaxf(fmaxf(acc[rb][0], acc[rb][1]), fmaxf(acc[rb][2], acc[rb][3])));
+              if (lg == 0) red[(srow + 16 * rb) * 2 + kw] = mx * p.sl2;
+            }
+            lgkm_barrier();   // (the PV waves meet it at the same point of phase 0)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              const f32x2 r2 = *reinterpret_cast<const f32x2*>(&red[(srow + 16 * rb) * 2]);
+              m_ref[rb] = fmaxf(r2[0], r2[1]);
+              if (kw == 0 && lg == 0) mref[srow + 16 * rb] = m_ref[rb];
+            }
+          }
+          // P = 2^(s - m) in bf16 (rows without a finite reference use 0: their
+          // masked keys give 0); the row sums add the rounded weights PV uses
+          uint8_t* pw = pl + (k & 1) * PBUF + pw_off;
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const float mb = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
+            float e[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(acc[rb][i], p.sl2, -mb));
+            u32x2 v;
+            v[0] = pack_bf16(e[0], e[1]);
+            v[1] = pack_bf16(e[2], e[3]);
+            *reinterpret_cast<u32x2*>(pw + 16 * rb * PRB) = v;
+            l_part[rb] = add_bf16x2(v[1], add_bf16x2(v[0], l_part[rb]));
+          }
+        }
+        lgkm_barrier();   // P(k) written
+        cur = lat + nb * BUF;
+        nb = nb == 2 ? 0 : nb + 1;
+      }
+      // Did some row's scores exceed its reference by more than 2^kRefSlack?
+      // Then its P, O and l may have overflowed: raise every reference to the
+      // row's maximum over the whole split and run the split again (the second
+      // pass cannot trigger another: its references bound every score).
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float mx = group_max(t_max[rb]);
+        if (lg == 0) red[(srow + 16 * rb) * 2 + kw] = mx * p.sl2;
+      }
+      lgkm_barrier();
+      const f32x2 rl = *reinterpret_cast<const f32x2*>(&red[lane * 2]);
+      const float mr = mref[lane];
+      const bool over = mr != -INFINITY && fmaxf(rl[0], rl[1]) > mr + kRefSlack;
+      if (rerun || __ballot(over) == 0) break;
+      rerun = true;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const f32x2 r2 = *reinterpret_cast<const f32x2*>(&red[(srow + 16 * rb) * 2]);
+        m_ref[rb] = m_ref[rb] == -INFINITY ? m_ref[rb] : fmaxf(m_ref[rb], fmaxf(r2[0], r2[1]));
+        l_part[rb] = 0.f;
+        t_max[rb] = -INFINITY;
+      }
+      lgkm_barrier();   // red read by every wave before the next write
+      lgkm_barrier();   // the PV waves copy tile 0 again
+    }
+    // ---- epilogue: row sums; the PV waves stage O -----------------------------
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no prefetch load outlives the workgroup
+    lgkm_barrier();   // every wave is done reading red
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float s = group_sum(l_part[rb]);
+      if (lg == 0) red[(srow + 16 * rb) * 2 + kw] = s;
+    }
+    lgkm_barrier();   // row sums and the staged O visible
+    if (kw == 0 && lg == 0) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row = srow + 16 * rb;
+        if (row < nrows) {
+          const f32x2 s2 = *reinterpret_cast<const f32x2*>(&red[row * 2]);
+          *reinterpret_cast<f32x2*>(p.ws_ml + (gro + idx0 + row) * 2) = f32x2{m_ref[rb], s2[0] + s2[1]};
+        }
+      }
+    }
+  } else {
+    // ======================= PV waves =========================================
+    // prologue: tile 0 and the query block's rope part (same swizzled layout as
+    // the rope keys: 64 rows, two copies per wave) -> LDS
+    load_idx(k0);
+    sidx = sidx_next;
+    issue_tile(k0, 0, 0);
+    load_idx(k0 + BN);
+    if (DR > 0) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int j = cw + 4 * x;
+        const int row = 8 * j + (lane >> 3);
+        dma_to<16>(p.q_pe + (qflat0 + min(row, nrows - 1)) * DR + 8 * rsw, qrope_a + 1024 * j);
+      }
+    }
+    f32x16 O[2][NCB];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[rb][cb][i] = 0.f;
+    full_barrier();   // tile 0, rope queries in LDS
+    lgkm_barrier();   // the scoring waves have read the query block
+    const int G = lane >> 4, s16 = lane & 15;
+    const int tr_off = (8 * (G >> 1) + (s16 >> 2)) * LRB + (cw * CPW + 16 * (G & 1) + 4 * (s16 & 3)) * 2;
+    const int pa_off = l32 * PRB + 16 * half;                              // + rb*32*PRB + 32 kc
+    bool rerun = false;
+    for (;;) {
+      uint8_t* prv = lat + 2 * BUF;       // tile k - 1's buffer
+      int nb = 1;                         // tile k + 1's (0..2)
+      for (int k = 0; k <= T; ++k) {
+        const int t0 = k0 + k * BN;
+        sidx = sidx_next;          // positions of tile k + 1
+        load_idx(t0 + 2 * BN);     // ... and of tile k + 2
+        const bool cp = k + 1 < T;
+        const int rnx = (k + 1) & 1;
+        if (k == 0 && cp) issue_tile(t0 + BN, nb, rnx);   // no PV in phase 0
+        if (k == 0 && !rerun) lgkm_barrier();   // the scoring waves' exchange of the references
+        if (k > 0) {
+          // ---- PV: O^T [128 columns x 64 rows] += V^T P^T for tile k - 1 ---------
+          const uint8_t* pa = pl + ((k - 1) & 1) * PBUF + pa_off;
+          const uint8_t* vb = prv + tr_off;
+          auto vfrag = [&](int kc, int cb) {
+            u32x4 bv;
+#pragma unroll
+            for (int ld = 0; ld < 2; ++ld) {
+              const uint8_t* src = vb + (16 * kc + 4 * ld) * LRB + 64 * cb;
+              const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src));
+              const u32x2 rr = __builtin_bit_cast(u32x2, r);
+              bv[2 * ld] = rr[0];
+              bv[2 * ld + 1] = rr[1];
+            }
+            return bv;
+          };
+          constexpr int NSTEP = (BN / 16) * NCB;
+          constexpr int VPF = 3;
+          u32x4 a[BN / 16][2];
+          u32x4 vq[VPF];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) a[0][rb] = *reinterpret_cast<const u32x4*>(pa + rb * 32 * PRB);
+#pragma unroll
+          for (int st = 0; st < VPF; ++st) {
+            if (st > 0 && st % NCB == 0) {
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb)
+                a[st / NCB][rb] = *reinterpret_cast<const u32x4*>(pa + rb * 32 * PRB + 32 * (st / NCB));
+            }
+            vq[st] = vfrag(st / NCB, st % NCB);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int st = 0; st < NSTEP; ++st) {
+            const int kc = st / NCB, cb = st % NCB;
+            const u32x4 bcur = vq[st % VPF];
+            const int sn = st + VPF;
+            if (sn < NSTEP) {
+              if (sn % NCB == 0) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                  a[sn / NCB][rb] = *reinterpret_cast<const u32x4*>(pa + rb * 32 * PRB + 32 * (sn / NCB));
+              }
+              vq[st % VPF] = vfrag(sn / NCB, sn % NCB);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) O[rb][cb] = mfma32(bcur, a[kc][rb], O[rb][cb]);   // O^T += V^T P^T
+            // the copy of tile k + 1: the rope blocks and a latent row at step 0,
+            // one latent row at each later step
+            static_assert(NSTEP == NCP - NRC, "one latent row per PV step");
+            if (cp) {
+              if (st == 0) {
+#pragma unroll
+                for (int j = 0; j < NRC; ++j) copy_item(t0 + BN, nb, rnx, j);
+              }
+              copy_item(t0 + BN, nb, rnx, NRC + st);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        full_barrier();   // this wave's copies have landed; P(k - 1) consumed
+        prv = prv + BUF == lat + 3 * BUF ? lat : prv + BUF;
+        nb = nb == 2 ? 0 : nb + 1;
+      }
+      // the decision of the scoring waves, from the same values
+      lgkm_barrier();
+      const f32x2 rl = *reinterpret_cast<const f32x2*>(&red[lane * 2]);
+      const float mr = mref[lane];
+      const bool over = mr != -INFINITY && fmaxf(rl[0], rl[1]) > mr + kRefSlack;
+      if (rerun || __ballot(over) == 0) break;
+      rerun = true;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) O[rb][cb][i] = 0.f;
+      lgkm_barrier();
+      load_idx(k0);
+      sidx = sidx_next;
+      issue_tile(k0, 0, 0);
+      load_idx(k0 + BN);
+      full_barrier();
+    }
+    // ---- epilogue: O -> bf16 staging rows (the tile buffers are free) ----------
+    lgkm_barrier();   // every wave is done reading red
+    {
+      // lane holds row 32 rb + l32, columns col0 + 32 cb + 8 q + 4 half + (0..3)
+      const int col0 = cw * CPW;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint8_t* dst = lat + (32 * rb + l32) * SROW + (col0 + 32 * cb + 8 * q + 4 * half) * 2;
+            const f32x16& o = O[rb][cb];
+            u32x2 v;
+            v[0] = pack_bf16(o[4 * q], o[4 * q + 1]);
+            v[1] = pack_bf16(o[4 * q + 2], o[4 * q + 3]);
+            *reinterpret_cast<u32x2*>(dst) = v;
+          }
+    }
+    lgkm_barrier();   // row sums and the staged O visible
+  }
+  // ---- every wave: the staged rows out with 16-byte stores ---------------------
+  {
+    constexpr int V16 = DV * 2 / 16;                // 16-byte chunks per row
+    constexpr int NST = BM * V16 / 512;
+    uint8_t* wso = reinterpret_cast<uint8_t*>(p.ws_o);
+    u32x4 v[NST];
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int e = tid + 512 * j;
+      v[j] = *reinterpret_cast<const u32x4*>(lat + (e / V16) * SROW + 16 * (e % V16));
+    }
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int e = tid + 512 * j;
+      const int row = e / V16;
+      if (row < nrows) st16(wso + ((gro + idx0 + row) * DV) * 2 + 16 * (e % V16), v[j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 namespace {
@@ -1144,10 +1193,10 @@ SplitArgs split_args(const AbsorbedLaunch& q) {
   a.B = q.B; a.L = q.L; a.H = q.H; a.rows = q.L * q.H;
   a.row_tiles = q.plan.row_tiles; a.chunk = q.plan.chunk; a.n_items = q.plan.n_items;
   a.sl2 = q.scale * 1.4426950408889634f;
-  // L2 prefetch window: an XCD's 32 CUs run 32 / row_tiles distinct splits at a
-  // time, each with pf_ahead tiles (72 KB) in flight; about row_tiles tiles keeps
-  // that near 2 MB of its 4 MB L2
-  a.pf_ahead = std::min(16, std::max(2, a.row_tiles));
+  // L2 prefetch window of the bf16 kernel: an XCD's 32 CUs run 32 / row_tiles
+  // distinct splits at a time, each with pf_ahead tiles (36 KB) in flight;
+  // about 2 row_tiles tiles keeps that near 2 MB of its 4 MB L2
+  a.pf_ahead = std::min(32, std::max(4, 2 * a.row_tiles));
   return a;
 }
 unsigned grid_of(int n_items) { return (unsigned)(((n_items + kXcds - 1) / kXcds) * kXcds); }
@@ -1158,8 +1207,8 @@ hipError_t absorbed_attn_bf16(const AbsorbedLaunch& q, hipStream_t st) {
   if (q.r != 512) return hipErrorInvalidValue;
   const dim3 grid(grid_of(a.n_items));
   switch (q.rope) {
-    case 0:  hipLaunchKernelGGL((absorbed_split_kernel<0, false>), grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((absorbed_split_kernel<64, false>), grid, dim3(256), 0, st, a); break;
+    case 0:  hipLaunchKernelGGL((absorbed_split_kernel<0, false>), grid, dim3(512), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((absorbed_split_kernel<64, false>), grid, dim3(512), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1212,8 +1261,8 @@ hipError_t absorbed_attn_sparse(const AbsorbedLaunch& q, const int32_t* sel, con
   if (q.r != 512) return hipErrorInvalidValue;
   const dim3 grid(grid_of(a.n_items));
   switch (q.rope) {
-    case 0:  hipLaunchKernelGGL((absorbed_split_kernel<0, true>), grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((absorbed_split_kernel<64, true>), grid, dim3(256), 0, st, a); break;
+    case 0:  hipLaunchKernelGGL((absorbed_split_kernel<0, true>), grid, dim3(512), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((absorbed_split_kernel<64, true>), grid, dim3(512), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
