@@ -109,14 +109,6 @@ __device__ __forceinline__ float group_sum(float x) {
 // in a tile buffer.
 // ---------------------------------------------------------------------------
 namespace {
-// x -> E4M3 codes of x / s (nearest, ties to even; |x| <= 448 s), four per word
-__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d, float s) {
-  typedef short s16x2 __attribute__((ext_vector_type(2)));
-  s16x2 r = {0, 0};
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, a, b, s, false);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, s, true);
-  return __builtin_bit_cast(uint32_t, r);
-}
 // Direct global -> LDS copy (BYTES = 16 or 4 per lane) written as inline asm:
 // the compiler then does not track it, so it adds no waits of its own before
 // LDS reads of other buffers.  The kernel waits for its copies itself (vmcnt)
@@ -166,15 +158,40 @@ template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
-__device__ __forceinline__ float absmax8(u32x4 v, float m) {
+// max |x| over the 32 bf16 values of v[0..3], as the bf16 bit pattern of the
+// magnitude: with the sign bits cleared, the patterns of non-NaN values order
+// as unsigned integers, so two 16-bit maxima per instruction.  A NaN orders
+// above infinity (the block's scale is then irrelevant: the row's scores are
+// NaN either way).
+__device__ __forceinline__ uint32_t absmax32(const u32x4 (&v)[4]) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
-  return m;
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[c][i] & 0x7fff7fffu));
+  return m[0] > m[1] ? m[0] : m[1];
 }
-// 8 bf16 values -> 8 E4M3 codes of x / s
+// e4m3_scale_exponent of the float whose bf16 pattern is the magnitude m (as
+// absmax32 gives it), without branches: the smallest k with m <= 448 x 2^k,
+// clamped to [-126, 127]; 0 for a zero block and for NaN.  448 = 1.75 x 2^8, so
+// k = E - 8, one more when the 7 mantissa bits exceed those of 1.75 (0x60).
+__device__ __forceinline__ int e4m3_scale_exponent_bf16(uint32_t m) {
+  const int k = max((int)(m >> 7) - 127 - 8 + ((m & 0x7fu) > 0x60u ? 1 : 0), -126);
+  return (m == 0u || m > 0x7f80u) ? 0 : k;
+}
+// 8 bf16 values -> 8 E4M3 codes of x / s (nearest, ties to even; the division
+// by a power of two is exact, so this is the rounding of x / s itself).  Each
+// conversion fills the low half of a word; byte permutes pair those halves.
+__device__ __forceinline__ uint32_t e4m3x2(uint32_t v, float s) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+                                          __builtin_bit_cast(s16x2, v), __builtin_bit_cast(bf16x2, v), s, false));
+}
 __device__ __forceinline__ u32x2 e4m3x8(u32x4 v, float s) {
-  return u32x2{cvt4_e4m3(bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1]), s),
-               cvt4_e4m3(bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3]), s)};
+  return u32x2{__builtin_amdgcn_perm(e4m3x2(v[1], s), e4m3x2(v[0], s), 0x05040100u),
+               __builtin_amdgcn_perm(e4m3x2(v[3], s), e4m3x2(v[2], s), 0x05040100u)};
 }
 }  // namespace
 
@@ -197,10 +214,13 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
   constexpr int NLW = NLI / 4;            // latent copies per wave per tile
   constexpr int NC = NLW / 2;             // ... of which these go with the scores, the rest with PV
   constexpr int SROW = DV * 2 + 8;        // epilogue staging row (bf16; 8 mod 256 bytes)
-  constexpr int QBYTES = NRB * KS * kWave * 32 + (DR > 0 ? NRB * kWave * 16 : 0);   // query codes
+  constexpr int QGS = 17 * 16, QHS = 81 * 16, QFS = 164 * 16;   // query staging strides (16-byte slots 1, 1, 4 mod 16)
+  constexpr int QSS = 68;                 // scale slots per (rb, ks): 64 lanes + 4 (banks 4 ks + 16 j + l % 16)
+  constexpr int QBYTES = NRB * KS * QFS + (DR > 0 ? NRB * kWave * 16 : 0);   // query codes
   static_assert(DR == 0 || DR == 64, "rope width 0 or 64");
   static_assert(BUF % 16 == 0, "layout");
-  static_assert(QBYTES <= BUF && NRB * NQ * kWave * 4 <= BM * PRB, "query codes fit in a tile buffer, their scales in pl");
+  static_assert(QHS >= 4 * QGS && QFS >= 2 * QHS, "staging strides");
+  static_assert(QBYTES <= BUF && NRB * NQ * QSS * 4 <= BM * PRB, "query codes fit in a tile buffer, their scales in pl");
   static_assert(BM * SROW <= BUF, "O staging fits in a tile buffer");
   static_assert(2 * BUF + BM * PRB + 4 * kWave <= 160 * 1024 / 2, "two workgroups per CU");
   static_assert(NRI <= 4 && NLW % 2 == 0, "copy layout");
@@ -320,22 +340,26 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
   // ---- query block -> E4M3 codes and block scales -----------------------------
   // One thread per (row, 32-wide block of the key dimension): the block's
   // scale 2^e is the smallest with every |q| <= 448 x 2^e, and its codes go to
-  // buf1 (idle until the next tile's copy) in the B layout of the score MFMA:
-  // lane l = row 16 rb + l % 16 over k = 128 ks + 16 (l / 16) .. (bytes 0..15)
-  // and 128 ks + 64 + 16 (l / 16) .. (bytes 16..31), fragment (rb, ks < KS) of
-  // lane l at 32 (64 (rb KS + ks) + l).  Block j of step ks thus fills bytes
-  // 16 (j / 2) .. of lane groups 2 (j % 2) and 2 (j % 2) + 1, and group j
-  // supplies its scale (an int per lane and step, in pl).  The rope step keeps
-  // only its lower halves (at 32 NRB KS 64 + 16 (64 rb + l)); its upper halves
-  // and blocks 2, 3 are zero.  Rows past the last query row repeat it (their
-  // results are never stored).  A thread's query loads are issued before the
-  // first tile's copy, so waiting for them does not wait for the tile.
+  // buf1 (idle until the next tile's copy) for the B operand of the score MFMA:
+  // lane l = row 16 rb + l % 16 over k = 128 ks + 16 (l / 16) .. (half 0) and
+  // 128 ks + 64 + 16 (l / 16) .. (half 1) of fragment (rb, ks < KS).  Block j
+  // of step ks thus fills half j / 2 of lane groups 2 (j % 2) and 2 (j % 2) + 1,
+  // and group j supplies its scale (an int per lane and step, in pl).  The
+  // staging holds 16 bytes per (fragment f, half h, lane group G, lane): at
+  // f QFS + h QHS + G QGS + 16 (l % 16), the strides padded so that the 16
+  // blocks of a row (ks < 4, j) fall in 16 distinct 16-byte bank slots (slot
+  // 4 ks + h + G mod 16) and the 16 lanes of a group read one contiguous 256
+  // bytes.  The rope step keeps only its lower halves (at ROPE_OFF + 16 (64 rb
+  // + l)); its upper halves and blocks 2, 3 are zero.  Rows past the last query
+  // row repeat it (their results are never stored).  A thread's query loads are
+  // issued before the first tile's copy, so waiting for them does not wait for
+  // the tile.
   i32x8 qf[NRB][NQ];
   int qs[NRB][(NQ + 3) / 4];   // E8M0 scales, step ks in byte ks % 4 of qs[rb][ks / 4]
   {
     constexpr int NB = DA / 32 + DR / 32;     // blocks per row
     constexpr int NU = (BM * NB + 255) / 256; // blocks per thread (the last round partial)
-    constexpr int ROPE_OFF = NRB * KS * kWave * 32;
+    constexpr int ROPE_OFF = NRB * KS * QFS;
     const long long qflat0 = (long long)b * p.rows + idx0;
     u32x4 qv[NU][4];
 #pragma unroll
@@ -356,8 +380,7 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
       const int u = tid + 256 * i;
       if (u < BM * NB) {
         const int row = u / NB, blk = u - row * NB;
-        const float m = absmax8(qv[i][3], absmax8(qv[i][2], absmax8(qv[i][1], absmax8(qv[i][0], 0.f))));
-        const int e = e4m3_scale_exponent(m);
+        const int e = e4m3_scale_exponent_bf16(absmax32(qv[i]));
         const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
         const int rb = row >> 4, r16 = row & 15;
         const u32x2 c0 = e4m3x8(qv[i][0], sc), c1 = e4m3x8(qv[i][1], sc), c2 = e4m3x8(qv[i][2], sc),
@@ -365,17 +388,16 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
         const u32x4 lo = u32x4{c0[0], c0[1], c1[0], c1[1]}, hi = u32x4{c2[0], c2[1], c3[0], c3[1]};
         if (blk < DA / 32) {
           const int ks = blk >> 2, j = blk & 3;
-          const int fl = 64 * (rb * KS + ks);
-          const int ga = 2 * (j & 1), hb = 16 * (j >> 1);
-          st16(buf1 + 32 * (fl + 16 * ga + r16) + hb, lo);
-          st16(buf1 + 32 * (fl + 16 * (ga + 1) + r16) + hb, hi);
-          qsl[64 * (rb * NQ + ks) + 16 * j + r16] = e + 127;
+          uint8_t* const dst = buf1 + (rb * KS + ks) * QFS + (j >> 1) * QHS + 2 * (j & 1) * QGS + 16 * r16;
+          st16(dst, lo);
+          st16(dst + QGS, hi);
+          qsl[QSS * (rb * NQ + ks) + 16 * j + r16] = e + 127;
         } else {
           const int j = blk - DA / 32;
           st16(buf1 + ROPE_OFF + 16 * (64 * rb + 16 * (2 * j) + r16), lo);
           st16(buf1 + ROPE_OFF + 16 * (64 * rb + 16 * (2 * j + 1) + r16), hi);
-          qsl[64 * (rb * NQ + NQ - 1) + 16 * j + r16] = e + 127;
-          qsl[64 * (rb * NQ + NQ - 1) + 16 * (j + 2) + r16] = 127;
+          qsl[QSS * (rb * NQ + NQ - 1) + 16 * j + r16] = e + 127;
+          qsl[QSS * (rb * NQ + NQ - 1) + 16 * (j + 2) + r16] = 127;
         }
       }
     }
@@ -384,8 +406,8 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
     for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int fl = 64 * (rb * KS + ks) + lane;
-        const u32x4 x0 = ld16(buf1 + 32 * fl), x1 = ld16(buf1 + 32 * fl + 16);
+        const uint8_t* const src = buf1 + (rb * KS + ks) * QFS + (lane >> 4) * QGS + 16 * l16;
+        const u32x4 x0 = ld16(src), x1 = ld16(src + QHS);
         qf[rb][ks] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
       }
       if (DR > 0) {
@@ -396,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
       for (int k4 = 0; k4 < (NQ + 3) / 4; ++k4) {
         int v = 0;
 #pragma unroll
-        for (int ks = 4 * k4; ks < min(NQ, 4 * k4 + 4); ++ks) v |= qsl[64 * (rb * NQ + ks) + lane] << (8 * (ks % 4));
+        for (int ks = 4 * k4; ks < min(NQ, 4 * k4 + 4); ++ks) v |= qsl[QSS * (rb * NQ + ks) + lane] << (8 * (ks % 4));
         qs[rb][k4] = v;
       }
     }
@@ -447,9 +469,10 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
   auto step = [&](int t0, const uint8_t* cur, uint8_t* nxt, bool pf) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // (A) tile t visible; PV(t-1) done, so the other buffer and pl are free
-    if (!rerun) {
+    if (!SEL && !rerun && wu * kWave < p.pf_lines) {   // the waves holding prefetch lanes
       if (t0 == k0) {
-        for (int d = 1; d <= kPfAhead; ++d) prefetch_tile(t0 + d * BN);
+        const int dn = min(kPfAhead, (k1 - 1 - t0) / BN);   // the split's later tiles, up to kPfAhead
+        for (int d = 1; d <= dn; ++d) prefetch_tile(t0 + d * BN);
       } else {
         prefetch_tile(t0 + kPfAhead * BN);
       }
