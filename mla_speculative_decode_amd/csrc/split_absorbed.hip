@@ -705,8 +705,9 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
 // tile k + 3 in phase k + 2), two rope-key buffers and two P buffers (each read
 // in one phase only), the rope part of the query block.  The PV waves copy the
 // next tile (direct global -> LDS loads issued as inline asm, which the
-// compiler does not track, spread over their MFMAs) and wait for their copies
-// (vmcnt) before the barrier that ends the phase; the scoring waves fetch the
+// compiler does not track, all of them behind the phase's first MFMAs, so that
+// they land while the rest of the PV runs) and wait for their copies (vmcnt)
+// before the barrier that ends the phase; the scoring waves fetch the
 // split's cache lines into L2 ahead of the copies (one load instruction a
 // phase) and never wait for those loads inside the tile loop, so the fetches
 // run many phases ahead.
@@ -1125,15 +1126,11 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
             }
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) O[rb][cb] = mfma32(bcur, a[kc][rb], O[rb][cb]);   // O^T += V^T P^T
-            // the copy of tile k + 1: the rope blocks and a latent row at step 0,
-            // one latent row at each later step
-            static_assert(NSTEP == NCP - NRC, "one latent row per PV step");
-            if (cp) {
-              if (st == 0) {
+            // the copy of tile k + 1, all of it behind the first MFMAs: it then
+            // lands while the rest of the PV runs, not after it
+            if (cp && st == 0) {
 #pragma unroll
-                for (int j = 0; j < NRC; ++j) copy_item(t0 + BN, nb, rnx, j);
-              }
-              copy_item(t0 + BN, nb, rnx, NRC + st);
+              for (int j = 0; j < NCP; ++j) copy_item(t0 + BN, nb, rnx, j);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
