@@ -648,8 +648,8 @@ __global__ __launch_bounds__(256) void combine_upproj_f32_kernel(const float* __
 // 64 output columns), the column tile varying fastest so that the items that
 // read the same partial sums run on one XCD and share its L2.  The W_UV tile
 // [r x 64] goes global -> LDS with direct loads while the partial sums come
-// into registers, 32 16-byte loads per lane in flight.  Wave w merges rows
-// w, w+4, .. (RPW of them; lane l: latent columns 8l..8l+7) in float32,
+// into registers, 16 16-byte loads per lane in flight.  Wave w merges rows
+// w, w+NW, .. (RPW of them; lane l: latent columns 8l..8l+7) in float32,
 // stores the merged latent as a bf16 pair hi + lo (hi = bf16(x),
 // lo = bf16(x - hi)) and multiplies both with 16x16x32 MFMAs, W fragments
 // read transposed from LDS.
@@ -662,18 +662,23 @@ struct MergeUpArgs {
   int MTS, CT, n_items;   // row tiles of 16 per sequence, column tiles of 64, items
 };
 
-// RPW: query rows per wave (1, 2 or 4: a row tile holds up to 4 * RPW rows).
-template <int R, int RPW>
-__global__ __launch_bounds__(256, 1) void merge_upproj_kernel(MergeUpArgs p) {
+// NW waves (4 or 8), RPW query rows per wave (NW RPW <= 16 rows per tile).
+// With eight waves twice the loads are in flight per CU; the product then
+// splits K over wave halves (waves 4..7 hand their partial sums over in LDS).
+template <int R, int RPW, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void merge_upproj_kernel(MergeUpArgs p) {
   static_assert(R / 8 == kWave, "one lane per 8 latent columns");
   constexpr int WRB = 64 * 2 + 16;            // W row: 64 bf16 + pad (bytes)
   constexpr int WCH = WRB / 16;               // 16-byte slots per W row (8 data + 1 pad)
   constexpr int WINST = R * WCH / kWave;      // direct-load wave instructions for the tile
   constexpr int ARB = R * 2 + 16;             // A row: R bf16 + pad
-  constexpr int SB = 32 / RPW;                // splits per row per round of loads
-  static_assert(WINST % 4 == 0 && kWave % SB == 0, "tile split over 4 waves; rounds inside a 64-split window");
+  constexpr int SB = (NW == 8 ? 16 : 32) / RPW;   // splits per row per round of loads
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(NW * RPW <= 16, "a row tile of at most 16 rows");
+  static_assert(WINST % NW == 0 && kWave % SB == 0, "tile split over the waves; rounds inside a 64-split window");
   __shared__ __attribute__((aligned(1024))) uint8_t wt[R * WRB];
   __shared__ __attribute__((aligned(16))) uint8_t at[2][16 * ARB];
+  __shared__ __attribute__((aligned(16))) f32x4 kpart[NW == 8 ? 4 * kWave : 1];   // K-half sums of waves 4..7
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int item = xcd_item(blockIdx.x, p.n_items);
@@ -692,8 +697,8 @@ __global__ __launch_bounds__(256, 1) void merge_upproj_kernel(MergeUpArgs p) {
   const uint16_t* wsrc = p.w_uv + (long long)h * R * p.V + ct * 64;
   auto issue_w = [&]() {
 #pragma unroll
-    for (int x = 0; x < WINST / 4; ++x) {
-      const int j = wu + 4 * x;
+    for (int x = 0; x < WINST / NW; ++x) {
+      const int j = wu + NW * x;
       const int pos = kWave * j + lane;
       const int row = pos / WCH;
       int ch = pos - row * WCH;
@@ -710,14 +715,14 @@ __global__ __launch_bounds__(256, 1) void merge_upproj_kernel(MergeUpArgs p) {
     g0 = __builtin_amdgcn_readfirstlane(g0);
     S = __builtin_amdgcn_readfirstlane(S);
   }
-  // rows of this wave: w + 4 rr for rr < nr (row m of the tile is query row i0 + m)
-  const int nr = min(RPW, mrows > wu ? (mrows - wu + 3) / 4 : 0);
+  // rows of this wave: w + NW rr for rr < nr (row m of the tile is query row i0 + m)
+  const int nr = min(RPW, mrows > wu ? (mrows - wu + NW - 1) / NW : 0);
   const uint16_t* obase = p.ws_o + (long long)g0 * rows_total * R + 8 * lane;
   // flat partial-sum row of each slot; slots past this wave's rows repeat its last row
   // (a wave without rows reads nothing)
   int prow[RPW];
 #pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) prow[rr] = (i0 + (nr > 0 ? wu + 4 * min(rr, nr - 1) : 0)) * p.H + h;
+  for (int rr = 0; rr < RPW; ++rr) prow[rr] = (i0 + (nr > 0 ? wu + NW * min(rr, nr - 1) : 0)) * p.H + h;
 
   float o[RPW][8];
   float M[RPW], inv[RPW], wl[RPW];   // wl: merge weight of split 64*(s0/64) + lane
@@ -806,8 +811,8 @@ __global__ __launch_bounds__(256, 1) void merge_upproj_kernel(MergeUpArgs p) {
 
   // ---- merged latent -> LDS as hi + lo bf16 (rows without a query row are zero)
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int m = wu + 4 * rr;
+  for (int rr = 0; rr < 16 / NW; ++rr) {
+    const int m = wu + NW * rr;
     u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
     if (rr < RPW && rr < nr) {
 #pragma unroll
@@ -823,14 +828,18 @@ __global__ __launch_bounds__(256, 1) void merge_upproj_kernel(MergeUpArgs p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of the W tile has landed
   __syncthreads();
 
-  // ---- out tile [16 rows x 64 columns]: wave w -> columns 16w..16w+15
+  // ---- out tile [16 rows x 64 columns]: wave w -> columns 16 cb .. + 15 (cb = w % 4),
+  // k steps kh R / 64 .. of the half kh = w / 4 (eight waves; all of them with four)
   const int r16 = lane & 15, G = lane >> 4;
-  const uint8_t* wb = wt + (8 * G + (r16 >> 2)) * WRB + (16 * w + 4 * (r16 & 3)) * 2;
+  const int cb = wu & 3, kh = NW == 8 ? wu >> 2 : 0;
+  constexpr int NKS = (R / 32) / (NW / 4);
+  const uint8_t* wb = wt + (8 * G + (r16 >> 2)) * WRB + (16 * cb + 4 * (r16 & 3)) * 2;
   const uint8_t* ab0 = at[0] + r16 * ARB + 16 * G;
   const uint8_t* ab1 = at[1] + r16 * ARB + 16 * G;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < R / 32; ++ks) {
+  for (int kk = 0; kk < NKS; ++kk) {
+    const int ks = kh * NKS + kk;
     u32x4 bv;
 #pragma unroll
     for (int ld = 0; ld < 2; ++ld) {
@@ -843,11 +852,19 @@ __global__ __launch_bounds__(256, 1) void merge_upproj_kernel(MergeUpArgs p) {
     acc = mfma16(*reinterpret_cast<const u32x4*>(ab0 + 64 * ks), bv, acc);
     acc = mfma16(*reinterpret_cast<const u32x4*>(ab1 + 64 * ks), bv, acc);
   }
+  if (NW == 8) {
+    if (kh == 1) kpart[cb * kWave + lane] = acc;
+    __syncthreads();
+    if (kh == 1) return;
+    const f32x4 o = kpart[cb * kWave + lane];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) acc[x] += o[x];
+  }
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     const int m = 4 * G + x;
     if (m < mrows)
-      p.out[(((long long)b * p.L + i0 + m) * p.H + h) * p.V + ct * 64 + 16 * w + r16] = acc[x];
+      p.out[(((long long)b * p.L + i0 + m) * p.H + h) * p.V + ct * 64 + 16 * cb + r16] = acc[x];
   }
 }
 
@@ -1070,11 +1087,10 @@ hipError_t combine_upproj(const AbsorbedLaunch& q, mla_dtype_t dt, float* out, h
     hipLaunchKernelGGL((merge_rows_kernel<512>), dim3(grid_xcd(a.n_items)), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  const int rpw = (std::min(16, q.L) + 3) / 4;   // query rows per wave
+  // eight waves, one or two query rows each
   const dim3 grid(grid_xcd(a.n_items));
-  if (rpw == 1) hipLaunchKernelGGL((merge_upproj_kernel<512, 1>), grid, dim3(256), 0, st, a);
-  else if (rpw == 2) hipLaunchKernelGGL((merge_upproj_kernel<512, 2>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((merge_upproj_kernel<512, 4>), grid, dim3(256), 0, st, a);
+  if (q.L <= 8) hipLaunchKernelGGL((merge_upproj_kernel<512, 1, 8>), grid, dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((merge_upproj_kernel<512, 2, 8>), grid, dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
