@@ -299,7 +299,7 @@ def main():
                 else peaks["hbm_read_GBps"])
     traffic = split_traffic_bytes() if (w.name == HEADLINE and not fp8) else None
     alg_bytes = cache_bytes + q_bytes + partial_bytes
-    roof = {"kernel": ("absorbed_split_f8_kernel (mla_absorbed_splits_fp8)" if fp8 else
+    roof = {"kernel": ("absorbed_split_f8_kernel (mla_absorbed_splits_fp8q)" if fp8 else
                        "absorbed_split_kernel (mla_absorbed_splits)"), **roof, "duration_us": round(us_split_b2b, 3),
             "traffic": traffic,
             "traffic_over_algorithmic": round(traffic / alg_bytes, 3) if traffic else None,
@@ -395,11 +395,13 @@ def absorbed_timing(w, x, cold_bytes, steps, warmup, fp8=False):
     if fp8:
         for st in sets:
             st["c_kv"], st["k_pe"] = st["codes"], st["codes"]
+    geom = mla.Geom(w.r, w.n, w.v, w.rope, H)
     for st in sets:
         st["q_lat"] = torch.empty((B, L, H, w.r), dtype=torch.bfloat16, device=dev)
         st["out"] = torch.empty((B, L, H, w.v), dtype=torch.float32, device=dev)
+        if fp8:   # the fold's E4M3 query block (mla_fold_query_fp8 -> mla_absorbed_attention_fp8q)
+            st["q8"] = torch.empty(mla.query_fp8_bytes(geom, B, L), dtype=torch.uint8, device=dev)
     offs = mla.Offsets(x.offsets.astype(np.int32), dev)
-    geom = mla.Geom(w.r, w.n, w.v, w.rope, H)
     ws_bytes = mla.absorbed_workspace_size(geom, _lib.MLA_BF16, L, offs)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream()
@@ -415,7 +417,8 @@ def absorbed_timing(w, x, cold_bytes, steps, warmup, fp8=False):
             ptrs("k_pe", idx), ptrs("w_uk", idx), ptrs("w_uv", idx), ptrs("q_lat", idx), ptrs("out", idx),
             offs.host_ptr(), offs.dev_ptr(), ctypes.c_float(x.scale), ctypes.c_void_p(ws.data_ptr()),
             ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream), warmup, steps, res,
-            ptrs("codes", idx) if fp8 else None, ptrs("scales", idx) if fp8 else None)
+            ptrs("codes", idx) if fp8 else None, ptrs("scales", idx) if fp8 else None,
+            ptrs("q8", idx) if fp8 else None)
         torch.cuda.synchronize()
         if rc != 0:
             raise RuntimeError(f"bench step failed: {lib.mla_status_string(rc).decode()}")

@@ -303,6 +303,43 @@ int mla_absorbed_splits_fp8(const mla_geom* g, int32_t B, int32_t L, const void*
                             void* stream);
 
 /*
+ * The fp8 route with the queries quantised once, by the fold, instead of in
+ * every split of the attention kernel (each split of a row tile would quantise
+ * the same rows again).
+ *
+ * mla_query_fp8_bytes -- bytes of the E4M3 query block for B sequences of L
+ * query rows: B x ceil(L H / 32) x 19456 (32 rows a tile).
+ *
+ * mla_fold_query_fp8 -- mla_fold_query (bf16) for B sequences of L rows
+ * (rows = B L), writing q_lat if it is not null and, into q8 (device,
+ * mla_query_fp8_bytes), the E4M3 block quantisation that
+ * mla_absorbed_attention_fp8 applies to q_lat and q_pe: per query row and
+ * 32-wide block of its key dimension, the smallest power-of-two scale 2^e with
+ * every |q| <= 448 x 2^e and the nearest E4M3 codes of q / 2^e, the latent
+ * part taken from the bf16-rounded fold (the values q_lat holds).  q_pe: device,
+ * [B, L, H, rope] bf16 (may be null when rope == 0).  The layout of q8 is the
+ * attention kernel's and is not part of the ABI; it is valid only for these g,
+ * B and L.  Supported: r = 512, rope in {0, 64}, n % 32 == 0, n <= 512;
+ * otherwise MLA_E_UNSUPPORTED.  Errors: MLA_E_NULL, MLA_E_SHAPE (B, L < 1 or
+ * B L H too large), MLA_E_HIP.
+ *
+ * mla_absorbed_attention_fp8q / mla_absorbed_splits_fp8q -- as
+ * mla_absorbed_attention_fp8 / mla_absorbed_splits_fp8 with the queries given
+ * as that block instead of q_lat and q_pe: the same kernels and, for the same
+ * bf16 query values, the same result bits.  Same workspace, errors and support.
+ */
+int mla_query_fp8_bytes(const mla_geom* g, int32_t B, int32_t L, size_t* bytes_out);
+int mla_fold_query_fp8(const mla_geom* g, int32_t B, int32_t L, const void* q_nope, const void* w_uk,
+                       const void* q_pe, void* q_lat, void* q8, void* stream);
+int mla_absorbed_attention_fp8q(const mla_geom* g, int32_t B, int32_t L, const void* q8, const void* codes,
+                                const float* scales, const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev,
+                                const void* w_uv, float scale, float* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+int mla_absorbed_splits_fp8q(const mla_geom* g, int32_t B, int32_t L, const void* q8, const void* codes,
+                             const float* scales, const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mla_absorbed_attention_sparse -- absorbed attention over selected cache
  * positions ("One guard, 110x off the verify step", section "The sparse model
  * is different": an indexer selects the top 2048 cached positions and attention

@@ -321,6 +321,61 @@ def absorbed_attention_fp8(q_lat, q_pe, codes, scales, w_uv, kv_offsets, scale=N
     return out
 
 
+def query_fp8_bytes(geom: Geom, B: int, L: int) -> int:
+    """Bytes of the E4M3 query block of B sequences of L rows (fold_query_fp8)."""
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    _lib.check("mla_query_fp8_bytes", lib.mla_query_fp8_bytes(ctypes.byref(geom), B, L, ctypes.byref(n)))
+    return n.value
+
+
+def fold_query_fp8(q_nope, w_uk, q_pe, q_lat=False, q8=None, stream=None):
+    """The fold for the fp8 route: q_nope [B, L, H, n], w_uk [H, n, r], q_pe
+    [B, L, H, rope] (bf16) -> (q_lat [B, L, H, r] or None, q8 uint8: the block
+    quantisation that absorbed_attention_fp8 applies to q_lat and q_pe, in the
+    attention kernel's layout).  q_lat=True allocates q_lat, a tensor receives it."""
+    torch = _torch()
+    lib = _lib.load()
+    B, L, H, n = q_nope.shape
+    r = w_uk.shape[-1]
+    rope = q_pe.shape[-1] if q_pe is not None else 0
+    g = Geom(r, n, 1, rope, H)
+    if q8 is None:
+        q8 = torch.empty(query_fp8_bytes(g, B, L), dtype=torch.uint8, device=q_nope.device)
+    if q_lat is True:
+        q_lat = torch.empty((B, L, H, r), dtype=torch.bfloat16, device=q_nope.device)
+    elif q_lat is False:
+        q_lat = None
+    _lib.check("mla_fold_query_fp8", lib.mla_fold_query_fp8(
+        ctypes.byref(g), B, L, _ptr(_dev(q_nope, "q_nope")), _ptr(_dev(w_uk, "w_uk")), _ptr(q_pe) if rope else None,
+        _ptr(q_lat) if q_lat is not None else None, _ptr(_dev(q8, "q8")), _stream(stream)))
+    return q_lat, q8
+
+
+def absorbed_attention_fp8q(q8, B, L, codes, scales, w_uv, kv_offsets, scale, rope=64, out=None, workspace=None,
+                            stream=None):
+    """absorbed_attention_fp8 with the queries given as fold_query_fp8's block q8."""
+    torch = _torch()
+    lib = _lib.load()
+    H, r, v = w_uv.shape
+    if codes.shape[-1] != r + rope:
+        raise ValueError("codes rows must hold r + rope values")
+    offs = _as_offsets(kv_offsets, q8.device)
+    if offs.B != B:
+        raise ValueError("offsets do not match the batch")
+    g = Geom(r, 0, v, rope, H)
+    need = absorbed_workspace_size(g, MLA_BF16, L, offs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q8.device)
+    if out is None:
+        out = torch.empty((B, L, H, v), dtype=torch.float32, device=q8.device)
+    _lib.check("mla_absorbed_attention_fp8q", lib.mla_absorbed_attention_fp8q(
+        ctypes.byref(g), B, L, _ptr(_dev(q8, "q8")), _ptr(_dev(codes, "codes")), _ptr(_dev(scales, "scales")),
+        offs.host_ptr(), offs.dev_ptr(), _ptr(_dev(w_uv, "w_uv")), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def absorbed_attention_sparse(q_lat, q_pe, c_kv, k_pe, w_uv, kv_offsets, sel, sel_offsets, scale=None, out=None,
                               workspace=None, stream=None, n=None):
     """Absorbed attention over selected positions: sequence b attends to

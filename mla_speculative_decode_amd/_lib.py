@@ -22,7 +22,8 @@ EXPORTS = ("mla_status_string", "mla_version", "mla_select_path", "mla_draft_cap
            "mla_absorbed_splits",
            "mla_absorbed_merge", "mla_materialize_kv",
            "mla_materialized_workspace_size", "mla_materialized_attention", "mla_quantize_latent_fp8",
-           "mla_absorbed_attention_fp8", "mla_absorbed_splits_fp8", "mla_absorbed_sparse_workspace_size",
+           "mla_absorbed_attention_fp8", "mla_absorbed_splits_fp8", "mla_query_fp8_bytes", "mla_fold_query_fp8",
+           "mla_absorbed_attention_fp8q", "mla_absorbed_splits_fp8q", "mla_absorbed_sparse_workspace_size",
            "mla_absorbed_attention_sparse", "mla_absorbed_attention_sparse_fp8", "mla_indexer_pool_init", "mla_indexer_pool_plan",
            "mla_indexer_pool_step", "mla_indexer_update_list", "mla_indexer_pool_step_fixed", "mla_indexer_pool_trim", "mla_indexer_scores", "mla_indexer_pool_step_scores",
            "mla_indexer_selection_offsets", "mla_indexer_select")
@@ -108,6 +109,16 @@ def load() -> ctypes.CDLL:
     lib.mla_absorbed_splits_fp8.restype = ctypes.c_int
     lib.mla_absorbed_splits_fp8.argtypes = [GP, I32, I32, VP, VP, VP, VP, VP, VP, ctypes.c_float, VP,
                                             ctypes.c_size_t, VP]
+    lib.mla_query_fp8_bytes.restype = ctypes.c_int
+    lib.mla_query_fp8_bytes.argtypes = [GP, I32, I32, SZP]
+    lib.mla_fold_query_fp8.restype = ctypes.c_int
+    lib.mla_fold_query_fp8.argtypes = [GP, I32, I32, VP, VP, VP, VP, VP, VP]
+    lib.mla_absorbed_attention_fp8q.restype = ctypes.c_int
+    lib.mla_absorbed_attention_fp8q.argtypes = [GP, I32, I32, VP, VP, VP, VP, VP, VP, ctypes.c_float, VP, VP,
+                                                ctypes.c_size_t, VP]
+    lib.mla_absorbed_splits_fp8q.restype = ctypes.c_int
+    lib.mla_absorbed_splits_fp8q.argtypes = [GP, I32, I32, VP, VP, VP, VP, VP, ctypes.c_float, VP,
+                                             ctypes.c_size_t, VP]
     lib.mla_absorbed_sparse_workspace_size.restype = ctypes.c_int
     lib.mla_absorbed_sparse_workspace_size.argtypes = [GP, I32, I32, VP, VP, SZP]
     lib.mla_absorbed_attention_sparse.restype = ctypes.c_int

@@ -346,6 +346,53 @@ int mla_absorbed_attention_fp8(const mla_geom* g, int32_t B, int32_t L, const vo
   return hip_status(combine_upproj(q, kBF16, out, s));
 }
 
+int mla_query_fp8_bytes(const mla_geom* g, int32_t B, int32_t L, size_t* bytes_out) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (!bytes_out) return MLA_E_NULL;
+  if (B < 1 || L < 1 || (int64_t)L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
+  *bytes_out = (size_t)B * (size_t)(((int64_t)L * g->heads + 31) / 32) * kQ8TileBytes;
+  return MLA_OK;
+}
+
+int mla_fold_query_fp8(const mla_geom* g, int32_t B, int32_t L, const void* q_nope, const void* w_uk,
+                       const void* q_pe, void* q_lat, void* q8, void* stream) {
+  int st = check_geom(g);
+  if (st) return st;
+  if (B < 1 || L < 1 || (int64_t)B * L * g->heads > INT32_MAX / 64) return MLA_E_SHAPE;
+  if (!q_nope || !w_uk || !q8) return MLA_E_NULL;
+  if (g->rope > 0 && !q_pe) return MLA_E_NULL;
+  if (g->r != 512 || !(g->rope == 0 || g->rope == 64) || g->n % 32 != 0 || g->n > 512) return MLA_E_UNSUPPORTED;
+  return hip_status(fold_query_fp8(B, L, g->heads, g->n, g->rope, q_nope, w_uk, q_pe, q_lat, q8, (hipStream_t)stream));
+}
+
+int mla_absorbed_splits_fp8q(const mla_geom* g, int32_t B, int32_t L, const void* q8, const void* codes,
+                             const float* scales, const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q8) return MLA_E_NULL;
+  AbsorbedLaunch q{};
+  int st = absorbed_prepare_fp8(g, B, L, q8, q8, codes, scales, kv_offsets_host, kv_offsets_dev, nullptr, nullptr,
+                                workspace, workspace_bytes, scale, false, &q);
+  if (st) return st;
+  q.q8 = q8;
+  return hip_status(absorbed_attn_fp8(q, codes, scales, (hipStream_t)stream));
+}
+
+int mla_absorbed_attention_fp8q(const mla_geom* g, int32_t B, int32_t L, const void* q8, const void* codes,
+                                const float* scales, const int32_t* kv_offsets_host, const int32_t* kv_offsets_dev,
+                                const void* w_uv, float scale, float* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!q8) return MLA_E_NULL;
+  AbsorbedLaunch q{};
+  int st = absorbed_prepare_fp8(g, B, L, q8, q8, codes, scales, kv_offsets_host, kv_offsets_dev, w_uv, out,
+                                workspace, workspace_bytes, scale, true, &q);
+  if (st) return st;
+  q.q8 = q8;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = hip_status(absorbed_attn_fp8(q, codes, scales, s)))) return st;
+  return hip_status(combine_upproj(q, kBF16, out, s));
+}
+
 namespace {
 // Selections: B >= 1, sel_off[0] >= 0, 1 <= k_b <= Kv_b for every sequence.
 int check_selection(int32_t B, const int32_t* kv_off, const int32_t* sel_off) {

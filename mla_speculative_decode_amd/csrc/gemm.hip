@@ -30,16 +30,49 @@ namespace mla {
 // row-major tile (ds_read_b64_tr_b16).  Each wave owns 16 output columns; the
 // weight stream is read once per MT rows.
 // ---------------------------------------------------------------------------
-template <int MT, int KMAX>
+//
+// Q8 (the fold for the fp8 route): the rows are also written as the E4M3 query
+// block (the layout of kQ8TileBytes): each 32-wide block of an output row is
+// columns 32 jb .. + 31 of a tile; the tile goes through LDS and one thread
+// quantises each (row, block).  The codes are those of the bf16-rounded
+// products (the values q_lat holds).  Items past the GEMM's quantise q_pe, one
+// thread per (row, 32-wide block).
+template <int MT, int KMAX, bool Q8>
 __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
   constexpr int WRB = 64 * 2 + 16;          // W row: 64 bf16 + pad
   constexpr int ARB = KMAX * 2 + 16;        // A row: K bf16 + pad
   constexpr int RB = MT / 16;
   __shared__ __attribute__((aligned(16))) uint8_t wt[KMAX * WRB];
   __shared__ __attribute__((aligned(16))) uint8_t at[MT * ARB];
+  __shared__ __attribute__((aligned(16))) uint16_t stg[Q8 ? MT * 64 : 8];   // Q8: the bf16 output tile
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int item = xcd_item(blockIdx.x, g.n_items);
   if (item >= g.n_items) return;
+  if (Q8 && item >= g.gemm_items) {
+    // ---- rope part of the query block: thread = (row b L H + l H + h, block j)
+    const int NBR = g.rope / 32;
+    const long long u = (long long)(item - g.gemm_items) * 256 + tid;
+    if (u >= (long long)g.M * g.H * NBR) return;
+    const long long rowg = u / NBR;
+    const int j = (int)(u - rowg * NBR);
+    const int LH = g.L * g.H;
+    const int b = (int)(rowg / LH), iseq = (int)(rowg - (long long)b * LH);
+    const int r = iseq & 31;
+    uint8_t* const tb = g.q8 + ((long long)b * g.row_tiles + (iseq >> 5)) * kQ8TileBytes;
+    u32x4 v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = ld16(g.q_pe + rowg * g.rope + 32 * j + 8 * c);
+    const int e = e4m3_scale_exponent_bf16(absmax32(v));
+    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+    const u32x2 c0 = e4m3x8(v[0], sc), c1 = e4m3x8(v[1], sc), c2 = e4m3x8(v[2], sc), c3 = e4m3x8(v[3], sc);
+    uint8_t* const rp = tb + kQ8RopeOff + 16 * (kWave * (r >> 4) + 32 * j + (r & 15));
+    st16(rp, u32x4{c0[0], c0[1], c1[0], c1[1]});
+    st16(rp + 16 * 16, u32x4{c2[0], c2[1], c3[0], c3[1]});
+    uint32_t* const sp = reinterpret_cast<uint32_t*>(tb + kQ8ScaleOff) + kWave * (2 * (r >> 4) + 1) + (r & 15);
+    sp[16 * j] = (uint32_t)(e + 127);
+    sp[16 * (j + 2)] = 127u;
+    return;
+  }
   const int CT = g.N / 64, MTS = (g.M + MT - 1) / MT;
   const int mt = item % MTS;
   const int tmp = item / MTS;
@@ -107,34 +140,85 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
     }
   }
   // C layout: lane holds column 16w + lane%16, rows 4*(lane/16) + x
+  if (!Q8 || g.C) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int m = m0 + 16 * rb + 4 * G + x;
-      if (m < g.M) {
-        const long long o = (long long)h * g.c_head + (long long)m * g.c_row + ct * 64 + 16 * w + r16;
-        g.C[o] = __builtin_bit_cast(uint16_t, (__bf16)acc[rb][x]);
+      for (int x = 0; x < 4; ++x) {
+        const int m = m0 + 16 * rb + 4 * G + x;
+        if (m < g.M) {
+          const long long o = (long long)h * g.c_head + (long long)m * g.c_row + ct * 64 + 16 * w + r16;
+          g.C[o] = __builtin_bit_cast(uint16_t, (__bf16)acc[rb][x]);
+        }
       }
+  }
+  if (Q8) {
+    // ---- latent part of the query block: the bf16-rounded tile -> LDS, then
+    // one thread per (row, 32-column block): row m = b L + l is sequence row
+    // l H + h; block jb of this tile is block 2 (ct % 2) + jb of step ct / 2,
+    // half ct % 2 of lane groups 2 jb and 2 jb + 1
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) stg[(16 * rb + 4 * G + x) * 64 + 16 * w + r16] = __builtin_bit_cast(uint16_t, (__bf16)acc[rb][x]);
+    __syncthreads();
+    const int row_t = tid >> 1, jb = tid & 1, m = m0 + row_t;
+    if (tid < 2 * MT && m < g.M) {
+      u32x4 v[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const u32x4*>(stg + row_t * 64 + 32 * jb + 8 * c);
+      const int e = e4m3_scale_exponent_bf16(absmax32(v));
+      const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+      const u32x2 c0 = e4m3x8(v[0], sc), c1 = e4m3x8(v[1], sc), c2 = e4m3x8(v[2], sc), c3 = e4m3x8(v[3], sc);
+      const int b = m / g.L, iseq = (m - b * g.L) * g.H + h, r = iseq & 31;
+      const int ks = ct >> 1, hh = ct & 1;
+      uint8_t* const tb = g.q8 + ((long long)b * g.row_tiles + (iseq >> 5)) * kQ8TileBytes;
+      uint8_t* const cd = tb + 16 * ((2 * (4 * (r >> 4) + ks) + hh) * kWave + 32 * jb + (r & 15));
+      st16(cd, u32x4{c0[0], c0[1], c1[0], c1[1]});
+      st16(cd + 16 * 16, u32x4{c2[0], c2[1], c3[0], c3[1]});
+      tb[kQ8ScaleOff + 4 * (kWave * 2 * (r >> 4) + 16 * (2 * hh + jb) + (r & 15)) + ks] = (uint8_t)(e + 127);
     }
+  }
 }
 
 hipError_t gemm_smallm(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
   if (a.K % 32 != 0 || a.K > 512 || a.N % 64 != 0) return hipErrorInvalidValue;
+  const bool q8 = a.q8 != nullptr;
+  if (q8 && (a.N != 512 || !(a.rope == 0 || a.rope == 64) || a.L < 1 || a.M % a.L != 0)) return hipErrorInvalidValue;
   const int MT = a.M <= 16 ? 16 : 64;       // rows per workgroup
-  a.n_items = a.H * (a.N / 64) * ((a.M + MT - 1) / MT);
+  a.gemm_items = a.H * (a.N / 64) * ((a.M + MT - 1) / MT);
+  const long long rope_threads = q8 ? (long long)a.M * a.H * (a.rope / 32) : 0;
+  const long long items = a.gemm_items + (rope_threads + 255) / 256;
+  if (items > INT32_MAX) return hipErrorInvalidValue;
+  a.n_items = (int)items;
   const unsigned grid = (unsigned)(((a.n_items + kXcds - 1) / kXcds) * kXcds);
   // LDS and staging registers are sized by KMAX: small K keeps several workgroups per CU
   const int KM = a.K <= 128 ? 128 : (a.K <= 256 ? 256 : 512);
-#define MLA_GEMM(M_, KM_)                                                                \
-  if (MT == M_ && KM == KM_) {                                                           \
-    hipLaunchKernelGGL((gemm_smallm_kernel<M_, KM_>), dim3(grid), dim3(256), 0, st, a);  \
-    return hipGetLastError();                                                            \
+#define MLA_GEMM(M_, KM_)                                                                                \
+  if (MT == M_ && KM == KM_) {                                                                           \
+    if (q8) hipLaunchKernelGGL((gemm_smallm_kernel<M_, KM_, true>), dim3(grid), dim3(256), 0, st, a);    \
+    else hipLaunchKernelGGL((gemm_smallm_kernel<M_, KM_, false>), dim3(grid), dim3(256), 0, st, a);      \
+    return hipGetLastError();                                                                            \
   }
   MLA_GEMM(16, 128) MLA_GEMM(64, 128) MLA_GEMM(16, 256) MLA_GEMM(64, 256) MLA_GEMM(16, 512) MLA_GEMM(64, 512)
 #undef MLA_GEMM
   return hipErrorInvalidValue;
+}
+
+// the fold for the fp8 route: q_lat (optional) and the E4M3 query block of
+// the sequence rows (latent part from the bf16 products, rope part from q_pe)
+hipError_t fold_query_fp8(int B, int L, int H, int n, int rope, const void* q_nope, const void* w_uk,
+                          const void* q_pe, void* q_lat, void* q8, hipStream_t st) {
+  if (n % 32 != 0 || n > 512) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.A = (const uint16_t*)q_nope; a.a_row = (long long)H * n; a.a_head = n;
+  a.W = (const uint16_t*)w_uk;
+  a.C = (uint16_t*)q_lat; a.c_row = (long long)H * 512; a.c_head = 512;
+  a.M = B * L; a.K = n; a.N = 512; a.H = H;
+  a.q8 = (uint8_t*)q8; a.q_pe = (const uint16_t*)q_pe;
+  a.L = L; a.rope = rope; a.row_tiles = (L * H + 31) / 32;
+  return gemm_smallm(a, st);
 }
 
 __global__ __launch_bounds__(256) void fold_f32_kernel(const float* __restrict__ q_nope, const float* __restrict__ w_uk,

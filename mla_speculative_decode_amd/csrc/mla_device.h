@@ -60,6 +60,41 @@ __device__ __forceinline__ int e4m3_scale_exponent(float a) {
   return k < -126 ? -126 : (k > 127 ? 127 : k);
 }
 
+// max |x| over the 32 bf16 values of v[0..3], as the bf16 bit pattern of the
+// magnitude: with the sign bits cleared, the patterns of non-NaN values order
+// as unsigned integers, so two 16-bit maxima per instruction.  A NaN orders
+// above infinity (the block's scale is then irrelevant: the row's scores are
+// NaN either way).
+__device__ __forceinline__ uint32_t absmax32(const u32x4 (&v)[4]) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[c][i] & 0x7fff7fffu));
+  return m[0] > m[1] ? m[0] : m[1];
+}
+// e4m3_scale_exponent of the float whose bf16 pattern is the magnitude m (as
+// absmax32 gives it), without branches: the smallest k with m <= 448 x 2^k,
+// clamped to [-126, 127]; 0 for a zero block and for NaN.  448 = 1.75 x 2^8, so
+// k = E - 8, one more when the 7 mantissa bits exceed those of 1.75 (0x60).
+__device__ __forceinline__ int e4m3_scale_exponent_bf16(uint32_t m) {
+  const int k = max((int)(m >> 7) - 127 - 8 + ((m & 0x7fu) > 0x60u ? 1 : 0), -126);
+  return (m == 0u || m > 0x7f80u) ? 0 : k;
+}
+// 8 bf16 values -> 8 E4M3 codes of x / s (nearest, ties to even; the division
+// by a power of two is exact, so this is the rounding of x / s itself).  Each
+// conversion fills the low half of a word; byte permutes pair those halves.
+__device__ __forceinline__ uint32_t e4m3x2(uint32_t v, float s) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+                                          __builtin_bit_cast(s16x2, v), __builtin_bit_cast(bf16x2, v), s, false));
+}
+__device__ __forceinline__ u32x2 e4m3x8(u32x4 v, float s) {
+  return u32x2{__builtin_amdgcn_perm(e4m3x2(v[1], s), e4m3x2(v[0], s), 0x05040100u),
+               __builtin_amdgcn_perm(e4m3x2(v[3], s), e4m3x2(v[2], s), 0x05040100u)};
+}
 
 // ---- bfloat16 ----------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

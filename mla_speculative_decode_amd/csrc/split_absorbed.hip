@@ -44,6 +44,7 @@ struct SplitArgs {
   const uint16_t* k_pe;    // [T, DR]
   const uint8_t* c8;       // fp8 form: E4M3 codes [T, 512 + DR] (latent | rope)
   const float* s8;         // fp8 form: one power-of-two scale per position [T]
+  const uint8_t* q8;       // fp8 form: the E4M3 query blocks (kQ8TileBytes per 32 rows), or null: quantise here
   const int32_t* sel;      // SEL: selected positions per sequence (packed by off; relative, increasing)
   const int32_t* koff;     // SEL: cache offsets [B+1] (off then indexes the selection)
   int koff0, kvt1;         // SEL, B == 1: koff[0] and koff[1] - koff[0]
@@ -158,44 +159,10 @@ template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
-// max |x| over the 32 bf16 values of v[0..3], as the bf16 bit pattern of the
-// magnitude: with the sign bits cleared, the patterns of non-NaN values order
-// as unsigned integers, so two 16-bit maxima per instruction.  A NaN orders
-// above infinity (the block's scale is then irrelevant: the row's scores are
-// NaN either way).
-__device__ __forceinline__ uint32_t absmax32(const u32x4 (&v)[4]) {
-  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-  u16x2 m = {0, 0};
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[c][i] & 0x7fff7fffu));
-  return m[0] > m[1] ? m[0] : m[1];
-}
-// e4m3_scale_exponent of the float whose bf16 pattern is the magnitude m (as
-// absmax32 gives it), without branches: the smallest k with m <= 448 x 2^k,
-// clamped to [-126, 127]; 0 for a zero block and for NaN.  448 = 1.75 x 2^8, so
-// k = E - 8, one more when the 7 mantissa bits exceed those of 1.75 (0x60).
-__device__ __forceinline__ int e4m3_scale_exponent_bf16(uint32_t m) {
-  const int k = max((int)(m >> 7) - 127 - 8 + ((m & 0x7fu) > 0x60u ? 1 : 0), -126);
-  return (m == 0u || m > 0x7f80u) ? 0 : k;
-}
-// 8 bf16 values -> 8 E4M3 codes of x / s (nearest, ties to even; the division
-// by a power of two is exact, so this is the rounding of x / s itself).  Each
-// conversion fills the low half of a word; byte permutes pair those halves.
-__device__ __forceinline__ uint32_t e4m3x2(uint32_t v, float s) {
-  typedef short s16x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
-                                          __builtin_bit_cast(s16x2, v), __builtin_bit_cast(bf16x2, v), s, false));
-}
-__device__ __forceinline__ u32x2 e4m3x8(u32x4 v, float s) {
-  return u32x2{__builtin_amdgcn_perm(e4m3x2(v[1], s), e4m3x2(v[0], s), 0x05040100u),
-               __builtin_amdgcn_perm(e4m3x2(v[3], s), e4m3x2(v[2], s), 0x05040100u)};
-}
 }  // namespace
 
-template <int DR, bool SEL>
+// Q8: the queries come quantised (the fold's E4M3 query block, p.q8).
+template <int DR, bool SEL, bool Q8>
 __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) {
   constexpr int DA = 512, DV = 512;
   constexpr int BM = 32, BN = 64;
@@ -356,7 +323,37 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
   // the tile.
   i32x8 qf[NRB][NQ];
   int qs[NRB][(NQ + 3) / 4];   // E8M0 scales, step ks in byte ks % 4 of qs[rb][ks / 4]
-  {
+  if (Q8) {
+    // the block quantised by the fold: one copy into buf1, then registers (rows
+    // past the last query row: zero codes, scale 2^0)
+    static_assert(kQ8TileBytes % 1024 == 0 && kQ8TileBytes <= BUF && NRB == 2 && KS == 4, "query block layout");
+    const uint8_t* qt = p.q8 + ((long long)b * p.row_tiles + rt) * kQ8TileBytes;
+#pragma unroll
+    for (int x = wu; x < kQ8TileBytes / 1024; x += 4) dma<16>(qt + 1024 * x + 16 * lane, buf1 + 1024 * x);
+    load_idx(k0);
+    issue_tile(k0, buf0);
+    load_idx(k0 + BN);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const bool ok = 16 * rb + l16 < nrows;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint8_t* const src = buf1 + 16 * (2 * (KS * rb + ks) * kWave + lane);
+        const u32x4 x0 = ok ? ld16(src) : u32x4{0u, 0u, 0u, 0u}, x1 = ok ? ld16(src + 16 * kWave) : u32x4{0u, 0u, 0u, 0u};
+        qf[rb][ks] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
+      if (DR > 0) {
+        const u32x4 x0 = ok ? ld16(buf1 + kQ8RopeOff + 16 * (kWave * rb + lane)) : u32x4{0u, 0u, 0u, 0u};
+        qf[rb][NQ - 1] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int k4 = 0; k4 < (NQ + 3) / 4; ++k4)
+        qs[rb][k4] = ok ? *reinterpret_cast<const int*>(buf1 + kQ8ScaleOff + 4 * (kWave * (2 * rb + k4) + lane)) : 0x7f7f7f7f;
+    }
+    // buf1 is written again only after barrier (A) of the first tile
+  } else {
     constexpr int NB = DA / 32 + DR / 32;     // blocks per row
     constexpr int NU = (BM * NB + 255) / 256; // blocks per thread (the last round partial)
     constexpr int ROPE_OFF = NRB * KS * QFS;
@@ -1206,7 +1203,7 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
 namespace {
 SplitArgs split_args(const AbsorbedLaunch& q) {
   SplitArgs a{};
-  a.q_lat = (const uint16_t*)q.q_lat; a.q_pe = (const uint16_t*)q.q_pe;
+  a.q_lat = (const uint16_t*)q.q_lat; a.q_pe = (const uint16_t*)q.q_pe; a.q8 = (const uint8_t*)q.q8;
   a.c_kv = (const uint16_t*)q.c_kv; a.k_pe = (const uint16_t*)q.k_pe;
   a.off = q.off_dev; a.off0 = q.off0; a.kv1 = q.kv1;
   a.ws_o = (uint16_t*)q.ws_o; a.ws_ml = q.ws_ml;
@@ -1250,9 +1247,16 @@ hipError_t absorbed_attn_fp8(const AbsorbedLaunch& q, const void* codes, const f
   f8_rows(a, q.rope);
   if (q.r != 512) return hipErrorInvalidValue;
   const dim3 grid(grid_of(a.n_items));
+  const bool q8 = a.q8 != nullptr;
   switch (q.rope) {
-    case 0:  hipLaunchKernelGGL((absorbed_split_f8_kernel<0, false>), grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((absorbed_split_f8_kernel<64, false>), grid, dim3(256), 0, st, a); break;
+    case 0:
+      if (q8) hipLaunchKernelGGL((absorbed_split_f8_kernel<0, false, true>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((absorbed_split_f8_kernel<0, false, false>), grid, dim3(256), 0, st, a);
+      break;
+    case 64:
+      if (q8) hipLaunchKernelGGL((absorbed_split_f8_kernel<64, false, true>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((absorbed_split_f8_kernel<64, false, false>), grid, dim3(256), 0, st, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1267,8 +1271,8 @@ hipError_t absorbed_attn_sparse_fp8(const AbsorbedLaunch& q, const void* codes, 
   if (q.r != 512) return hipErrorInvalidValue;
   const dim3 grid(grid_of(a.n_items));
   switch (q.rope) {
-    case 0:  hipLaunchKernelGGL((absorbed_split_f8_kernel<0, true>), grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((absorbed_split_f8_kernel<64, true>), grid, dim3(256), 0, st, a); break;
+    case 0:  hipLaunchKernelGGL((absorbed_split_f8_kernel<0, true, false>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((absorbed_split_f8_kernel<64, true, false>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

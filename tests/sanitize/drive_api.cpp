@@ -104,6 +104,12 @@ int main() {
         CHECK(mla_absorbed_attention_fp8(&g, B, L, fake(64), fake(64), fake(64), (float*)fake(64), off.data(),
                                          (int32_t*)fake(64), fake(64), 0.1f, (float*)fake(64), fake(256), ws,
                                          nullptr) == (g.r == 512 ? MLA_OK : MLA_E_UNSUPPORTED));
+        CHECK(mla_absorbed_attention_fp8q(&g, B, L, fake(64), fake(64), (float*)fake(64), off.data(),
+                                          (int32_t*)fake(64), fake(64), 0.1f, (float*)fake(64), fake(256), ws,
+                                          nullptr) == (g.r == 512 ? MLA_OK : MLA_E_UNSUPPORTED));
+        size_t qb = 0;
+        CHECK(mla_query_fp8_bytes(&g, B, L, &qb) == MLA_OK);
+        CHECK(qb == (size_t)B * (size_t)(((int64_t)L * g.heads + 31) / 32) * 19456);
       }
     } else {
       CHECK(st == MLA_E_UNSUPPORTED || st == MLA_E_SHAPE);
@@ -149,6 +155,9 @@ int main() {
     CHECK(mla_materialize_kv(&g, MLA_BF16, 8192, fake(64), fake(64), fake(64), fake(64), fake(64), fake(64),
                              nullptr) == MLA_OK);
     CHECK(mla_quantize_latent_fp8(&g, 8192, fake(64), fake(64), fake(64), (float*)fake(64), nullptr) == MLA_OK);
+    CHECK(mla_fold_query_fp8(&g, 0, 8, fake(64), fake(64), fake(64), nullptr, fake(64), nullptr) == MLA_E_SHAPE);
+    CHECK(mla_fold_query_fp8(&g, 1, 8, fake(64), fake(64), nullptr, nullptr, fake(64), nullptr) == MLA_E_NULL);
+    CHECK(mla_fold_query_fp8(&g, 1, 8, fake(64), fake(64), fake(64), nullptr, fake(64), nullptr) == MLA_OK);
   }
 
   // pooled indexer: random steps, trims, scores and selections on the host state

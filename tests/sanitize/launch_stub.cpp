@@ -50,6 +50,9 @@ hipError_t gemm_smallm(const GemmArgs&, hipStream_t) { return reached(); }
 hipError_t fold_query(mla_dtype_t, int, int, int, int, const void*, const void*, void*, hipStream_t) {
   return reached();
 }
+hipError_t fold_query_fp8(int, int, int, int, int, const void*, const void*, const void*, void*, void*, hipStream_t) {
+  return reached();
+}
 hipError_t materialize_kv(mla_dtype_t, long long, int, int, int, int, int, const void*, const void*, const void*,
                           const void*, void*, void*, hipStream_t) {
   return reached();

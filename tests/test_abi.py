@@ -186,3 +186,28 @@ def test_noalloc_rejects_partials_beyond_its_array(lib):
     assert st == -4   # MLA_E_WORKSPACE
     assert lib.mla_absorbed_attention_noalloc(None, _lib.MLA_BF16, 1, 8, dummy, dummy, dummy, dummy, vp, dummy,
                                               dummy, ctypes.c_float(0.1), dummy, None) == -1
+
+
+def test_fp8_query_block_entry_points_validate_on_host(lib):
+    g = Geom(512, 128, 128, 64, 128)
+    sz = ctypes.c_size_t(0)
+    assert lib.mla_query_fp8_bytes(ctypes.byref(g), 1, 8, ctypes.byref(sz)) == 0
+    assert sz.value == 32 * 19456                       # 1024 rows in tiles of 32
+    assert lib.mla_query_fp8_bytes(ctypes.byref(g), 3, 3, ctypes.byref(sz)) == 0
+    assert sz.value == 3 * 12 * 19456                   # 384 rows a sequence
+    assert lib.mla_query_fp8_bytes(ctypes.byref(g), 0, 8, ctypes.byref(sz)) == -2
+    assert lib.mla_query_fp8_bytes(ctypes.byref(g), 1, 8, None) == -1
+    d = ctypes.c_void_p(256)
+    assert lib.mla_fold_query_fp8(ctypes.byref(g), 1, 8, d, d, None, None, d, None) == -1    # rope > 0, no q_pe
+    assert lib.mla_fold_query_fp8(ctypes.byref(g), 1, 8, d, d, d, None, None, None) == -1    # no q8
+    assert lib.mla_fold_query_fp8(ctypes.byref(g), 0, 8, d, d, d, None, d, None) == -2
+    bad = Geom(256, 128, 128, 64, 128)
+    assert lib.mla_fold_query_fp8(ctypes.byref(bad), 1, 8, d, d, d, None, d, None) == -3
+    bad = Geom(512, 100, 128, 64, 128)
+    assert lib.mla_fold_query_fp8(ctypes.byref(bad), 1, 8, d, d, d, None, d, None) == -3
+    off = np.array([0, 64], dtype=np.int32)
+    vp = off.ctypes.data_as(ctypes.c_void_p)
+    assert lib.mla_absorbed_attention_fp8q(ctypes.byref(g), 1, 8, None, d, d, vp, d, d, ctypes.c_float(0.1), d, d,
+                                           1 << 30, None) == -1
+    assert lib.mla_absorbed_splits_fp8q(ctypes.byref(g), 1, 8, d, d, d, vp, d, ctypes.c_float(0.1), d, 16,
+                                        None) == -4      # workspace too small
