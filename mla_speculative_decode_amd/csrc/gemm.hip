@@ -35,8 +35,8 @@ namespace mla {
 // block (the layout of kQ8TileBytes): each 32-wide block of an output row is
 // columns 32 jb .. + 31 of a tile; the tile goes through LDS and one thread
 // quantises each (row, block).  The codes are those of the bf16-rounded
-// products (the values q_lat holds).  Items past the GEMM's quantise q_pe, one
-// thread per (row, 32-wide block).
+// products (the values q_lat holds).  The rope part (q_pe) is spread over the
+// same workgroups, one thread per (row, 32-wide block).
 template <int MT, int KMAX, bool Q8>
 __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
   constexpr int WRB = 64 * 2 + 16;          // W row: 64 bf16 + pad
@@ -44,40 +44,50 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
   constexpr int RB = MT / 16;
   __shared__ __attribute__((aligned(16))) uint8_t wt[KMAX * WRB];
   __shared__ __attribute__((aligned(16))) uint8_t at[MT * ARB];
-  __shared__ __attribute__((aligned(16))) uint16_t stg[Q8 ? MT * 64 : 8];   // Q8: the bf16 output tile
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int item = xcd_item(blockIdx.x, g.n_items);
   if (item >= g.n_items) return;
-  if (Q8 && item >= g.gemm_items) {
-    // ---- rope part of the query block: thread = (row b L H + l H + h, block j)
-    const int NBR = g.rope / 32;
-    const long long u = (long long)(item - g.gemm_items) * 256 + tid;
-    if (u >= (long long)g.M * g.H * NBR) return;
-    const long long rowg = u / NBR;
-    const int j = (int)(u - rowg * NBR);
-    const int LH = g.L * g.H;
-    const int b = (int)(rowg / LH), iseq = (int)(rowg - (long long)b * LH);
-    const int r = iseq & 31;
-    uint8_t* const tb = g.q8 + ((long long)b * g.row_tiles + (iseq >> 5)) * kQ8TileBytes;
-    u32x4 v[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = ld16(g.q_pe + rowg * g.rope + 32 * j + 8 * c);
-    const int e = e4m3_scale_exponent_bf16(absmax32(v));
-    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
-    const u32x2 c0 = e4m3x8(v[0], sc), c1 = e4m3x8(v[1], sc), c2 = e4m3x8(v[2], sc), c3 = e4m3x8(v[3], sc);
-    uint8_t* const rp = tb + kQ8RopeOff + 16 * (kWave * (r >> 4) + 32 * j + (r & 15));
-    st16(rp, u32x4{c0[0], c0[1], c1[0], c1[1]});
-    st16(rp + 16 * 16, u32x4{c2[0], c2[1], c3[0], c3[1]});
-    uint32_t* const sp = reinterpret_cast<uint32_t*>(tb + kQ8ScaleOff) + kWave * (2 * (r >> 4) + 1) + (r & 15);
-    sp[16 * j] = (uint32_t)(e + 127);
-    sp[16 * (j + 2)] = 127u;
-    return;
-  }
+
   const int CT = g.N / 64, MTS = (g.M + MT - 1) / MT;
   const int mt = item % MTS;
   const int tmp = item / MTS;
   const int ct = tmp % CT, h = tmp / CT;
   const int K = g.K, m0 = mt * MT;
+
+  // ---- Q8: rope part of the query block, spread over the GEMM's workgroups:
+  // thread tid takes block u = tid * items + item of the rows' rope parts (row
+  // b L H + l H + h, 32-wide block j); its loads go out first and it is
+  // quantised as soon as they land, while the tiles' loads are in flight
+  u32x4 rv[4];
+  long long rrow = 0;
+  int rj = 0;
+  bool has_rope = false;
+  if (Q8 && g.rope > 0) {
+    const int NBR = g.rope / 32;
+    const long long u = (long long)tid * g.n_items + item;
+    if (u < (long long)g.M * g.H * NBR) {
+      has_rope = true;
+      rrow = u / NBR;
+      rj = (int)(u - rrow * NBR);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rv[c] = ld16(g.q_pe + rrow * g.rope + 32 * rj + 8 * c);
+    }
+  }
+  auto rope_block = [&]() {
+    const int LH = g.L * g.H;
+    const int b = (int)(rrow / LH), iseq = (int)(rrow - (long long)b * LH);
+    const int r = iseq & 31;
+    uint8_t* const tb = g.q8 + ((long long)b * g.row_tiles + (iseq >> 5)) * kQ8TileBytes;
+    const int e = e4m3_scale_exponent_bf16(absmax32(rv));
+    const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+    const u32x2 c0 = e4m3x8(rv[0], sc), c1 = e4m3x8(rv[1], sc), c2 = e4m3x8(rv[2], sc), c3 = e4m3x8(rv[3], sc);
+    uint8_t* const rp = tb + kQ8RopeOff + 16 * (kWave * (r >> 4) + 32 * rj + (r & 15));
+    st16(rp, u32x4{c0[0], c0[1], c1[0], c1[1]});
+    st16(rp + 16 * 16, u32x4{c2[0], c2[1], c3[0], c3[1]});
+    uint32_t* const sp = reinterpret_cast<uint32_t*>(tb + kQ8ScaleOff) + kWave * (2 * (r >> 4) + 1) + (r & 15);
+    sp[16 * rj] = (uint32_t)(e + 127);
+    sp[16 * (rj + 2)] = 127u;
+  };
 
   // ---- W tile: K rows x 64 columns (K * 8 chunks of 16 B) --------------------
   const uint16_t* wsrc = g.W + (long long)h * K * g.N + ct * 64;
@@ -101,6 +111,7 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
       v = ld16(g.A + (long long)h * g.a_head + (long long)(m0 + r) * g.a_row + (long long)c * 8);
     ast[x] = v;
   }
+  if (Q8 && has_rope) rope_block();   // waits for the rope loads only (issued first)
 #pragma unroll
   for (int x = 0; x < WCH_T; ++x) {
     const int C = tid + 256 * x;
@@ -157,6 +168,10 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(GemmArgs g) {
     // one thread per (row, 32-column block): row m = b L + l is sequence row
     // l H + h; block jb of this tile is block 2 (ct % 2) + jb of step ct / 2,
     // half ct % 2 of lane groups 2 jb and 2 jb + 1
+    // the staging reuses the A tile's LDS once every wave is past its MFMAs
+    static_assert(MT * 64 * 2 <= MT * ARB, "output tile fits in the A tile");
+    uint16_t* const stg = reinterpret_cast<uint16_t*>(at);
+    __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -187,11 +202,9 @@ hipError_t gemm_smallm(const GemmArgs& a0, hipStream_t st) {
   const bool q8 = a.q8 != nullptr;
   if (q8 && (a.N != 512 || !(a.rope == 0 || a.rope == 64) || a.L < 1 || a.M % a.L != 0)) return hipErrorInvalidValue;
   const int MT = a.M <= 16 ? 16 : 64;       // rows per workgroup
-  a.gemm_items = a.H * (a.N / 64) * ((a.M + MT - 1) / MT);
-  const long long rope_threads = q8 ? (long long)a.M * a.H * (a.rope / 32) : 0;
-  const long long items = a.gemm_items + (rope_threads + 255) / 256;
-  if (items > INT32_MAX) return hipErrorInvalidValue;
-  a.n_items = (int)items;
+  a.n_items = a.H * (a.N / 64) * ((a.M + MT - 1) / MT);
+  // Q8: the rope blocks (M H rope / 32) are spread over the workgroups' 256 threads
+  if (q8 && (long long)a.M * a.H * (a.rope / 32) > 256LL * a.n_items) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(((a.n_items + kXcds - 1) / kXcds) * kXcds);
   // LDS and staging registers are sized by KMAX: small K keeps several workgroups per CU
   const int KM = a.K <= 128 ? 128 : (a.K <= 256 ? 256 : 512);

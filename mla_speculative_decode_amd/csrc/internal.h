@@ -105,7 +105,7 @@ struct GemmArgs {
   // fold for the fp8 route: the E4M3 query blocks of C's rows and of q_pe
   uint8_t* q8;            // B x row_tiles blocks of kQ8TileBytes
   const uint16_t* q_pe;   // [B, L, H, rope]
-  int L, rope, row_tiles, gemm_items;
+  int L, rope, row_tiles;
 };
 hipError_t gemm_smallm(const GemmArgs& a, hipStream_t st);
 hipError_t fold_query(mla_dtype_t dt, int rows, int H, int n, int r, const void* q_nope, const void* w_uk,
