@@ -683,7 +683,8 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
     for (int j = 0; j < NST; ++j) {
       const int e = tid + 256 * j;
       const int row = e / V16;
-      if (row < nrows) st16(wso + ((gro + idx0 + row) * DV) * 2 + 16 * (e % V16), v[j]);
+      if (row < nrows)   // streaming stores: the partials are read once, by the merge
+        __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4*>(wso + ((gro + idx0 + row) * DV) * 2 + 16 * (e % V16)));
     }
   }
 }
@@ -1192,7 +1193,8 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
     for (int j = 0; j < NST; ++j) {
       const int e = tid + 512 * j;
       const int row = e / V16;
-      if (row < nrows) st16(wso + ((gro + idx0 + row) * DV) * 2 + 16 * (e % V16), v[j]);
+      if (row < nrows)   // streaming stores: the partials are read once, by the merge
+        __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4*>(wso + ((gro + idx0 + row) * DV) * 2 + 16 * (e % V16)));
     }
   }
 }
