@@ -704,7 +704,8 @@ __global__ __launch_bounds__(64 * NW, 1) void merge_upproj_kernel(MergeUpArgs p)
       int ch = pos - row * WCH;
       if (ch == WCH - 1) ch = 0;
       __builtin_amdgcn_global_load_lds(wsrc + (long long)row * p.V + 8 * ch,
-                                       (__attribute__((address_space(3))) void*)(wt + 1024 * j), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(wt + 1024 * j), 16, 0,
+                                       2 /* streaming: each W_UV line is read by one workgroup */);
     }
   };
 
@@ -864,7 +865,7 @@ __global__ __launch_bounds__(64 * NW, 1) void merge_upproj_kernel(MergeUpArgs p)
   for (int x = 0; x < 4; ++x) {
     const int m = 4 * G + x;
     if (m < mrows)
-      p.out[(((long long)b * p.L + i0 + m) * p.H + h) * p.V + ct * 64 + 16 * cb + r16] = acc[x];
+      __builtin_nontemporal_store(acc[x], &p.out[(((long long)b * p.L + i0 + m) * p.H + h) * p.V + ct * 64 + 16 * cb + r16]);
   }
 }
 
