@@ -846,10 +846,45 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
     const uint16_t* src = ln < DA / 64 ? p.c_kv + pos * DA + 64 * ln : p.k_pe + pos * DR;
     dma_to<4>(src, pfd_a);
   };
+  // The same for tile k + kPfAhead + 1 in phase k (positions [ta, ta + BN)),
+  // with the per-phase arithmetic kept small (it runs on the scoring waves, whose
+  // instruction count bounds the phase): the list starts at ta + pf_off, pf_off
+  // stepping down by BN mod row_tiles a phase; this lane's entry (j, line) is fixed;
+  // the one division by row_tiles uses a reciprocal (exact: the dividend is < BN).
+  // With no list (tiles past the split) the load goes to the split's first line:
+  // a build that skipped it measured slower (0.6 us per launch at 128 heads x 8
+  // rows x 8192 positions, where every phase is such a phase).
+  const int kPfAhead = p.pf_ahead;   // tiles of BN positions
+  const int R = p.row_tiles;
+  const int bn_mod = BN % R;
+  int pf_off = ((rt - ((kPfAhead + 1) * BN) % R) % R + R) % R;
+  const uint32_t rinv = R > 1 ? 0xffffffffu / (uint32_t)R + 1u : 0u;   // ceil(2^32 / R)
+  const int lj = tid / LPP, lln = tid - lj * LPP;
+  auto phase_prefetch = [&](int t0) {
+    const int ta = t0 + (kPfAhead + 1) * BN;
+    const int tb = min(ta + BN, k1);
+    const int first = ta + pf_off;
+    pf_off -= bn_mod;
+    if (pf_off < 0) pf_off += R;
+    long long pos = p0 + k0;   // no list: the split's first line again
+    int ln = 0;
+    if (first < tb) {
+      const uint32_t x = (uint32_t)(tb - 1 - first);
+      const int nl = ((R > 1 ? (int)__umulhi(x, rinv) : (int)x) + 1) * LPP;
+      int j = lj;
+      ln = lln;
+      if (tid >= nl) {   // lanes past the list repeat its last line
+        j = (nl - 1) / LPP;
+        ln = (nl - 1) - j * LPP;
+      }
+      pos = p0 + first + (long long)R * j;
+    }
+    const uint16_t* src = ln < DA / 64 ? p.c_kv + pos * DA + 64 * ln : p.k_pe + pos * DR;
+    dma_to<4>(src, pfd_a);
+  };
   auto lgkm_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   auto full_barrier = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   const bool prefetch = !SEL;
-  const int kPfAhead = p.pf_ahead;   // tiles of BN positions
 
   const long long qflat0 = (long long)b * p.rows + idx0;
 
@@ -917,7 +952,7 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
       for (int k = 0; k <= T; ++k) {
         const int t0 = k0 + k * BN;
         // the cache lines of tile k + kPfAhead + 1 (a quarter of them per wave)
-        if (prefetch && !rerun) prefetch_lines(t0 + (kPfAhead + 1) * BN, t0 + (kPfAhead + 2) * BN, tid);
+        if (prefetch && !rerun) phase_prefetch(t0);
         if (k < T) {
           const uint8_t* kro = krope + (k & 1) * RBUF;
           // ---- scores: S^T [16 keys x 32 rows] ---------------------------------
