@@ -665,7 +665,10 @@ struct MergeUpArgs {
 // NW waves (4 or 8), RPW query rows per wave (NW RPW <= 16 rows per tile).
 // With eight waves twice the loads are in flight per CU; the product then
 // splits K over wave halves (waves 4..7 hand their partial sums over in LDS).
-template <int R, int RPW, int NW>
+// WSTREAM: the W_UV tile is loaded with the streaming hint, for launches in which
+// one workgroup reads each W_UV line (one sequence, one row tile); with more, the
+// workgroups of the other sequences and row tiles re-read it from L2.
+template <int R, int RPW, int NW, bool WSTREAM>
 __global__ __launch_bounds__(64 * NW, 1) void merge_upproj_kernel(MergeUpArgs p) {
   static_assert(R / 8 == kWave, "one lane per 8 latent columns");
   constexpr int WRB = 64 * 2 + 16;            // W row: 64 bf16 + pad (bytes)
@@ -705,7 +708,7 @@ __global__ __launch_bounds__(64 * NW, 1) void merge_upproj_kernel(MergeUpArgs p)
       if (ch == WCH - 1) ch = 0;
       __builtin_amdgcn_global_load_lds(wsrc + (long long)row * p.V + 8 * ch,
                                        (__attribute__((address_space(3))) void*)(wt + 1024 * j), 16, 0,
-                                       2 /* streaming: each W_UV line is read by one workgroup */);
+                                       WSTREAM ? 2 : 0);
     }
   };
 
@@ -1090,8 +1093,11 @@ hipError_t combine_upproj(const AbsorbedLaunch& q, mla_dtype_t dt, float* out, h
   }
   // eight waves, one or two query rows each
   const dim3 grid(grid_xcd(a.n_items));
-  if (q.L <= 8) hipLaunchKernelGGL((merge_upproj_kernel<512, 1, 8>), grid, dim3(512), 0, st, a);
-  else hipLaunchKernelGGL((merge_upproj_kernel<512, 2, 8>), grid, dim3(512), 0, st, a);
+  const bool once = q.B == 1 && a.MTS == 1;   // each W_UV line read by one workgroup
+  if (q.L <= 8 && once) hipLaunchKernelGGL((merge_upproj_kernel<512, 1, 8, true>), grid, dim3(512), 0, st, a);
+  else if (q.L <= 8) hipLaunchKernelGGL((merge_upproj_kernel<512, 1, 8, false>), grid, dim3(512), 0, st, a);
+  else if (once) hipLaunchKernelGGL((merge_upproj_kernel<512, 2, 8, true>), grid, dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((merge_upproj_kernel<512, 2, 8, false>), grid, dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
