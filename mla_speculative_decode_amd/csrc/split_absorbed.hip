@@ -716,7 +716,14 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
   constexpr int BM = 64, BN = 32;
   constexpr int KL = DA / 32;             // 32-wide k steps of the score MFMA over the latent part
   constexpr int KR = DR / 32;             // ... over the rope part
-  constexpr int LRB = DA * 2 + 48;        // latent LDS row (48 mod 256 bytes: conflict-free fragment reads)
+  // Latent LDS rows: 1088 bytes (64 mod 256) with the 16-byte chunk index of row r
+  // XOR-ed with lsw(r) = 2 ((r >> 2) & 1).  A ds_read_b128 serves 16 lanes per cycle
+  // (lanes of one half-wave whose bits 2 ^ 3 ^ 4 agree), a ds_read_b64_tr_b16 32
+  // lanes; with this layout the 16 lanes of a score fragment read (16 rows x 4
+  // chunks) and the 32 lanes of a transposed V read (4 rows x 64 bytes) each touch
+  // every bank once.  The copies apply the swizzle: lane i of a row's 1 KB copy
+  // loads chunk i ^ lsw(r).
+  constexpr int LRB = DA * 2 + 64;
   constexpr int RCH = DR / 8;             // 16-byte rope chunks per row
   constexpr int RRB = RCH * 16;           // rope LDS row: chunk c of row r stored at c ^ (r & 7)
   constexpr int BUF = BN * LRB;
@@ -726,7 +733,7 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
   constexpr int PBUF = BM * PRB;
   constexpr int CPW = DV / 4;             // latent columns per PV wave
   constexpr int NCB = CPW / 32;           // 32-column MFMA blocks per PV wave
-  constexpr int SROW = LRB;               // epilogue staging row
+  constexpr int SROW = DA * 2 + 48;       // epilogue staging row (unswizzled)
   static_assert(DR == 0 || (DR == 64 && BN * RCH == 4 * kWave), "rope width 0 or 64: one rope copy per wave");
   static_assert(BM * SROW <= 3 * BUF, "O staging fits in the tile buffers");
 
@@ -807,6 +814,7 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
   const uint32_t lat_a = lds_addr(lat), krope_a = lds_addr(krope), qrope_a = lds_addr(qrope), pfd_a = lds_addr(pfd);
   // nb: the latent buffer (0..2), rb: the rope buffer (0, 1)
   const int cw = wu - 4;
+  auto lsw = [](int r) { return ((r >> 2) & 1) << 1; };   // chunk swizzle of latent row r
   auto copy_item = [&](int t0, int nb, int rb, int j) {
     if (j < NRC) {
       const int blk = cw;
@@ -816,7 +824,7 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
     } else {
       const int key = cw + 4 * (j - NRC);
       const int kr = SEL ? __builtin_amdgcn_readlane(sidx, key) : __builtin_amdgcn_readfirstlane(min(t0 + key, k1 - 1));
-      dma_to<16>(lbase + (long long)kr * DA + 8 * lane, lat_a + nb * BUF + key * LRB);
+      dma_to<16>(lbase + (long long)kr * DA + 8 * (lane ^ lsw(key)), lat_a + nb * BUF + key * LRB);
     }
   };
   auto issue_tile = [&](int t0, int nb, int rb) {
@@ -900,7 +908,7 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
 #pragma unroll
     for (int x = 0; x < BM / 4; ++x) {
       const int row = wu + 4 * x;
-      dma_to<16>(p.q_lat + (qflat0 + min(row, nrows - 1)) * DA + 8 * lane, lat_a + BUF + row * LRB);
+      dma_to<16>(p.q_lat + (qflat0 + min(row, nrows - 1)) * DA + 8 * (lane ^ lsw(row)), lat_a + BUF + row * LRB);
     }
     int kend[2];
 #pragma unroll
@@ -913,7 +921,7 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
     // B operand from there)
     u32x4 qf[2][KL];
     {
-      const uint8_t* qsrc = lat + BUF + srow * LRB + 16 * lg;
+      const uint8_t* qsrc = lat + BUF + srow * LRB + 16 * (lg ^ lsw(srow));   // rows srow + 16 rb: the same swizzle
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -943,7 +951,7 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) { m_ref[rb] = -INFINITY; l_part[rb] = 0.f; t_max[rb] = -INFINITY; }
     bool rerun = false;
-    const int kq_off = (16 * kw + l16) * LRB + 16 * lg;                    // + 64 ks
+    const int kq_off = (16 * kw + l16) * LRB + 16 * (lg ^ lsw(l16));      // + 64 ks
     const int kr_off = (16 * kw + l16) * RRB;
     const int pw_off = srow * PRB + (16 * kw + 4 * lg) * 2;                // + 16 rb PRB
     for (;;) {
@@ -1098,7 +1106,11 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
     full_barrier();   // tile 0, rope queries in LDS
     lgkm_barrier();   // the scoring waves have read the query block
     const int G = lane >> 4, s16 = lane & 15;
-    const int tr_off = (8 * (G >> 1) + (s16 >> 2)) * LRB + (cw * CPW + 16 * (G & 1) + 4 * (s16 & 3)) * 2;
+    // rows 16 kc + 4 ld + 8 (G >> 1) + s16 / 4: bit 2 of the row is ld, so the rows
+    // of the ld = 1 reads have chunk bit 1 (byte bit 5, i.e. G & 1) flipped
+    const int tr_col = (cw * CPW + 16 * (G & 1) + 4 * (s16 & 3)) * 2;
+    const int tr_off = (8 * (G >> 1) + (s16 >> 2)) * LRB + tr_col;
+    const int tr_off1 = (8 * (G >> 1) + (s16 >> 2)) * LRB + (tr_col ^ 32);
     const int pa_off = l32 * PRB + 16 * half;                              // + rb*32*PRB + 32 kc
     bool rerun = false;
     for (;;) {
@@ -1116,11 +1128,12 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
           // ---- PV: O^T [128 columns x 64 rows] += V^T P^T for tile k - 1 ---------
           const uint8_t* pa = pl + ((k - 1) & 1) * PBUF + pa_off;
           const uint8_t* vb = prv + tr_off;
+          const uint8_t* vb1 = prv + tr_off1;
           auto vfrag = [&](int kc, int cb) {
             u32x4 bv;
 #pragma unroll
             for (int ld = 0; ld < 2; ++ld) {
-              const uint8_t* src = vb + (16 * kc + 4 * ld) * LRB + 64 * cb;
+              const uint8_t* src = (ld ? vb1 : vb) + (16 * kc + 4 * ld) * LRB + 64 * cb;
               const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src));
               const u32x2 rr = __builtin_bit_cast(u32x2, r);
               bv[2 * ld] = rr[0];
