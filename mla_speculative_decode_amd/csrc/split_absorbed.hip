@@ -124,6 +124,17 @@ __device__ __forceinline__ void dma(const void* gsrc, const void* lds_dst) {
   else
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(m) : "memory");
 }
+// the same with a uniform 64-bit base (scalar registers) and a per-lane 32-bit
+// byte offset: the address needs no 64-bit vector arithmetic
+template <int BYTES>
+__device__ __forceinline__ void dma_sv(const void* sbase, uint32_t voff, const void* lds_dst) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_dst);
+  if (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m) : "memory");
+}
 // the same with the LDS destination given as an LDS address (uniform)
 template <int BYTES>
 __device__ __forceinline__ void dma_to(const void* gsrc, uint32_t lds_addr) {
@@ -267,18 +278,32 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
   auto pos_of = [&](int t0, int key) -> int {              // cache position of tile row `key` (per lane)
     return SEL ? __shfl(sidx, key, kWave) : min(t0 + key, k1 - 1);
   };
+  // Dense tiles address the codes from the tile's first position (a scalar
+  // base) plus a per-lane 32-bit offset (rows clamped to the split's last);
+  // selected positions are arbitrary and keep the 64-bit per-lane form.
   auto issue_latent = [&](int t0, uint8_t* kdst, int x) {
-    const int pos = pos_of(t0, 8 * x + lrow);
-    dma<16>(cbase + (long long)pos * DW + ((x & 1) ? lsw1 : lsw0), kdst + 1024 * (wu + 4 * x));
+    if (SEL) {
+      const int pos = pos_of(t0, 8 * x + lrow);
+      dma<16>(cbase + (long long)pos * DW + ((x & 1) ? lsw1 : lsw0), kdst + 1024 * (wu + 4 * x));
+    } else {
+      const int row = min(8 * x + lrow, k1 - 1 - t0);
+      dma_sv<16>(cbase + (long long)t0 * DW, (uint32_t)(row * DW + ((x & 1) ? lsw1 : lsw0)), kdst + 1024 * (wu + 4 * x));
+    }
   };
   auto issue_rope = [&](int t0, uint8_t* kdst, int j) {
     const int r = 16 * j + rrow;
-    const int pos = pos_of(t0, r);
-    dma<16>(cbase + (long long)pos * DW + DA + 16 * (rpc ^ (r & 3)), kdst + ROPE + 1024 * j);
+    if (SEL) {
+      const int pos = pos_of(t0, r);
+      dma<16>(cbase + (long long)pos * DW + DA + 16 * (rpc ^ (r & 3)), kdst + ROPE + 1024 * j);
+    } else {
+      const int row = min(r, k1 - 1 - t0);
+      dma_sv<16>(cbase + (long long)t0 * DW, (uint32_t)(row * DW + DA + 16 * (rpc ^ (r & 3))), kdst + ROPE + 1024 * j);
+    }
   };
   // the tile's 64 scales (lane j: key j)
   auto issue_scales = [&](int t0, uint8_t* kdst) {
-    dma<4>(sbase + pos_of(t0, lane), kdst + SOFF);
+    if (SEL) dma<4>(sbase + pos_of(t0, lane), kdst + SOFF);
+    else dma_sv<4>(sbase + t0, (uint32_t)(4 * min(lane, k1 - 1 - t0)), kdst + SOFF);
   };
   // copy x of this wave (x < NLW: latent pair wu + 4 x; NLW: its rope block or
   // the scales)
