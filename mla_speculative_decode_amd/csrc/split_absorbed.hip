@@ -137,6 +137,14 @@ __device__ __forceinline__ void dma_sv(const void* sbase, uint32_t voff, const v
 }
 // the same with the LDS destination given as an LDS address (uniform)
 template <int BYTES>
+__device__ __forceinline__ void dma_sv_to(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
+  if (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m) : "memory");
+}
+template <int BYTES>
 __device__ __forceinline__ void dma_to(const void* gsrc, uint32_t lds_addr) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
   if (BYTES == 16)
@@ -849,7 +857,7 @@ __global__ __launch_bounds__(512, 1) void absorbed_split_kernel(SplitArgs p) {
     } else {
       const int key = cw + 4 * (j - NRC);
       const int kr = SEL ? __builtin_amdgcn_readlane(sidx, key) : __builtin_amdgcn_readfirstlane(min(t0 + key, k1 - 1));
-      dma_to<16>(lbase + (long long)kr * DA + 8 * (lane ^ lsw(key)), lat_a + nb * BUF + key * LRB);
+      dma_sv_to<16>(lbase + (long long)kr * DA, (uint32_t)(16 * (lane ^ lsw(key))), lat_a + nb * BUF + key * LRB);
     }
   };
   auto issue_tile = [&](int t0, int nb, int rb) {
