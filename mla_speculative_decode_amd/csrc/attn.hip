@@ -887,7 +887,6 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(MergeUpArgs p) {
   static_assert(R / 8 == kWave, "one lane per 8 latent columns");
   __shared__ __attribute__((aligned(16))) float part[4][R];
   __shared__ __attribute__((aligned(16))) float ocol[32][64 + 4];
-  __shared__ float wstat[2];
   static_assert(R == 32 * 16, "32 slices of 16 latent indices");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int item = xcd_item(blockIdx.x, p.n_items);
@@ -907,8 +906,24 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(MergeUpArgs p) {
     S = __builtin_amdgcn_readfirstlane(S);
   }
   const float* ml = p.ws_ml + ((long long)g0 * rows_total + prow) * 2;
-  // merge statistics: M = max_s m_s, den = sum_s 2^(m_s - M) l_s (wave 0, lane-strided)
-  if (w == 0) {
+  const uint16_t* obase = p.ws_o + ((long long)g0 * rows_total + prow) * R + 8 * lane;
+  // The partial sums of this wave's first NPRE splits (w, w + 4, ..) and this
+  // thread's W_UV slice are requested before the merge statistics, which they
+  // do not depend on: one memory round trip instead of two.
+  constexpr int NPRE = 16;
+  u32x4 vpre[NPRE];
+#pragma unroll
+  for (int j = 0; j < NPRE; ++j)
+    if (w + 4 * j < S) vpre[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(obase + (long long)(w + 4 * j) * rows_total * R));
+  const int cg = tid & 7, ks = tid >> 3;
+  const uint16_t* wsrc = p.w_uv + (long long)h * R * p.V + (long long)(16 * ks) * p.V + ct * 64 + 8 * cg;
+  u32x4 wv[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) wv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + (long long)k * p.V));
+  // merge statistics, M = max_s m_s, den = sum_s 2^(m_s - M) l_s, lane-strided
+  // over the splits; every wave computes them (the same order, the same values)
+  float M, inv;
+  {
     float mx = -INFINITY;
     for (int s = lane; s < S; s += kWave) mx = fmaxf(mx, ml[(long long)s * rows_total * 2]);
 #pragma unroll
@@ -920,22 +935,27 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(MergeUpArgs p) {
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d, kWave);
-    if (lane == 0) { wstat[0] = mx; wstat[1] = den; }
+    M = mx;
+    inv = 1.f / den;
   }
-  __syncthreads();
-  const float M = wstat[0], inv = 1.f / wstat[1];
-  // this thread's W_UV slice, loaded while the partial sums stream in
-  const int cg = tid & 7, ks = tid >> 3;
-  const uint16_t* wsrc = p.w_uv + (long long)h * R * p.V + (long long)(16 * ks) * p.V + ct * 64 + 8 * cg;
-  u32x4 wv[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) wv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + (long long)k * p.V));
-  // this wave's splits: 8 latent columns per lane, float32
+  // this wave's splits: 8 latent columns per lane, float32, in split order
   float o[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) o[c] = 0.f;
-  const uint16_t* obase = p.ws_o + ((long long)g0 * rows_total + prow) * R + 8 * lane;
-  int s = w;
+#pragma unroll
+  for (int j = 0; j < NPRE; ++j) {
+    const int s = w + 4 * j;
+    if (s < S) {
+      const float m = ml[(long long)s * rows_total * 2];
+      const float wt = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M) * inv;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        o[2 * c] = fmaf(wt, bf16_lo(vpre[j][c]), o[2 * c]);
+        o[2 * c + 1] = fmaf(wt, bf16_hi(vpre[j][c]), o[2 * c + 1]);
+      }
+    }
+  }
+  int s = w + 4 * NPRE;
   for (; s + 12 < S; s += 16) {   // four splits of this wave in flight
     u32x4 v[4];
     float wt[4];
