@@ -273,15 +273,17 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
 
   // ---- tile copy: global -> LDS ----------------------------------------------
   // Latent rows of 512 codes, unpadded, 16-byte chunk c of row r stored at
-  // chunk c ^ (r & 15): the 16 rows of a score fragment, and the 8 rows of a
-  // transposed V read, then fall in distinct bank groups.  One wave
+  // chunk c ^ 2 (r & 7).  A ds_read_b128 serves the 16 lanes of a half-wave
+  // whose lane bits 2 ^ 3 ^ 4 agree, a transposed read a half-wave: with this
+  // swizzle the 16 lanes of a score-fragment read, and the 8 rows x 2 chunks of
+  // a transposed V read, each touch every bank once.  One wave
   // instruction fills two rows (lane l: row 2 j + l / 32, stored chunk l % 32),
   // every lane active; the rope parts (64 bytes a row, chunk c at c ^ (r & 3))
   // take one instruction per 16 rows, the scales one per tile.
   // This wave's latent pairs are j = wu + 4 x: lane l copies row r = 2 j + l / 32
-  // = 8 x + (2 wu + l / 32), whose swizzle r & 15 is 8 (x & 1) + (2 wu + l / 32).
+  // = 8 x + (2 wu + l / 32), whose swizzle 2 (r & 7) is 2 (2 wu + l / 32) for every x.
   const int lrow = 2 * wu + (lane >> 5);                   // row of the pair (x = 0) for this lane
-  const int lsw0 = 16 * ((lane & 31) ^ lrow), lsw1 = 16 * ((lane & 31) ^ (8 + lrow));
+  const int lsw0 = 16 * ((lane & 31) ^ (2 * lrow)), lsw1 = lsw0;
   const int rrow = lane >> 2, rpc = lane & 3;              // rope copy: row in the 16, stored chunk
   auto pos_of = [&](int t0, int key) -> int {              // cache position of tile row `key` (per lane)
     return SEL ? __shfl(sidx, key, kWave) : min(t0 + key, k1 - 1);
@@ -467,18 +469,18 @@ __global__ __launch_bounds__(256, 2) void absorbed_split_f8_kernel(SplitArgs p) 
     for (int i = 0; i < 16; ++i) O[cb][i] = 0.f;
 
   // score A fragment of key 16 w + l16: logical chunk 8 ks + lg (+ 4) is stored
-  // at (8 ks + lg) ^ l16 = (lg ^ l16) ^ 8 ks (the bits do not overlap)
-  const int ka_row = (16 * w + l16) * DA + 16 * (lg ^ l16);
+  // at (8 ks + lg) ^ 2 (l16 & 7) = (lg ^ 2 (l16 & 7)) ^ 8 ks (chunk bits do not carry)
+  const int ka_row = (16 * w + l16) * DA + 16 * (lg ^ (2 * (l16 & 7)));
   const int kr_off = ROPE + (16 * w + l16) * DR + 16 * (lg ^ (l16 & 3));
   const int G = lane >> 4, s16 = lane & 15;
   // V^T fragment of the 32x32x16 MFMA (col 32 cb + l32, keys 16 kc + 8 half ..):
   // source lane s16 of group G reads key 8 (G >> 1) + s16 / 2, 8 codes at column
   // 16 (G & 1) + 8 (s16 & 1); the read hands lane s16 column s16 of the 8 keys.
-  // The key's low 4 bits (the swizzle) do not depend on kc.
-  // (logical chunk 8 w + 2 cb + (G & 1) is stored at ((8 w + (G & 1)) ^ key) ^ 2 cb)
+  // The key's low 3 bits (the swizzle) do not depend on kc.
+  // (logical chunk 8 w + 2 cb + (G & 1) is stored at ((8 w + (G & 1)) ^ 2 (key & 7)) ^ 2 cb)
   const int tr_key = 8 * (G >> 1) + (s16 >> 1);
   const int tr_base = tr_key * DA + 8 * (s16 & 1);
-  const int tr_sw = (8 * w + (G & 1)) ^ tr_key;
+  const int tr_sw = (8 * w + (G & 1)) ^ (2 * (tr_key & 7));
   const int pa_off = l32 * PRB + 16 * half;                              // P^T fragment: + 32 kc
   const int pw_off = l16 * PRB + (16 * w + 4 * lg) * 2;                  // + 16 rb PRB
 
