@@ -196,6 +196,8 @@ def parse():
     ap.add_argument("--indexer", action="store_true",
                     help="time the pooled top-k indexer step (tail vs full pooling, scores, selection) and the "
                          "sparse attention it feeds, caches of 8192 and 131072")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="LDS lane groups of ds_read_b128 / ds_read_b64_tr_b16 and the split kernel's read layouts")
     ap.add_argument("--write-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                     help="write the split kernel's counter summary from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
                          "CSVs of the benchmark and of --copy-calibration runs (no GPU needed)")
@@ -207,6 +209,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.lds_probe:
+        lds_probe()
+        return
     if args.write_counters:
         cmds = ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o fetch -- python bench.py --steps 20 "
                 "--warmup 5 --no-cpu-baseline",
@@ -343,6 +348,46 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def lds_probe():
+    """Which lanes of one LDS read the hardware serves in the same cycle (a pair
+    of lanes on one bank set slows the read only then), and the cycles per read
+    of the bf16 split kernel's score-fragment and transposed V reads under the
+    row layouts it was measured with.  Prints one JSON line."""
+    import torch
+    blib = ctypes.CDLL(os.path.join(ROOT, "mla_speculative_decode_amd", "libmla_bench.so"))
+    scratch = torch.zeros(256 * 8, dtype=torch.int64, device="cuda:0")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    clk = ctypes.c_double()
+    args = (ctypes.c_void_p(scratch.data_ptr()), ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream),
+            ctypes.byref(clk))
+    blib.mlab_lds_pair.restype = ctypes.c_int
+    blib.mlab_lds_layout.restype = ctypes.c_int
+
+    def pair(op, li, lj, same):
+        if blib.mlab_lds_pair(op, li, lj, same, 200, *args) != 0:
+            raise RuntimeError("LDS probe failed")
+        return clk.value
+
+    def layout(pat, lrb, swz):
+        if blib.mlab_lds_layout(pat, lrb, swz, 400, *args) != 0:
+            raise RuntimeError("LDS probe failed")
+        return round(clk.value, 2)
+
+    groups = {}
+    for op, name in ((0, "ds_read_b128"), (1, "ds_read_b64_tr_b16")):
+        groups[name] = {}
+        for li in (0, 4, 32):
+            same_cycle = [lj for lj in range(64) if lj == li or pair(op, li, lj, 1) > 1.06 * pair(op, li, lj, 0)]
+            groups[name]["lane %d" % li] = same_cycle
+    layouts = {}
+    for lrb, swz in ((1072, 0), (1056, 0), (1088, 0), (1088, 1)):
+        key = "%d-byte rows%s" % (lrb, ", chunk swizzle" if swz else "")
+        layouts[key] = {"score fragments (ds_read_b128)": layout(0, lrb, swz),
+                        "transposed V (ds_read_b64_tr_b16)": layout(1, lrb, swz)}
+    print(json.dumps({"lds_lanes_served_together": groups, "lds_clk_per_read": layouts}), flush=True)
 
 
 def measured_peaks():

@@ -1,7 +1,10 @@
 // bench_peaks.hip -- the two achievable peaks the benchmark reports fractions
 // against, measured on the running GPU (part of libmla_bench.so, used only by
 // bench.py): a streaming read of a large buffer (HBM) and a dense stream of
-// independent bf16 32x32x16 MFMAs.
+// independent bf16 32x32x16 MFMAs.  Also two LDS probes behind the split
+// kernels' LDS layouts: which lanes of one read instruction LDS serves in the
+// same cycle, and the cycles of the score-fragment and transposed V reads under
+// a given row layout.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -55,6 +58,111 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float* __rest
   if (s == 1.2345f) sink[0] = s;   // keeps the products live
 }
 
+
+// ---- LDS probes: one 512-thread workgroup per CU (136 KB of LDS each), 8 waves,
+// `iters` rounds of 16 reads 1 KB apart (the same banks, distinct addresses);
+// cycles per wave from s_memtime.  Every address stays below 48 KB.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kLdsProbeBytes = 139264;
+
+template <int OP>
+__device__ __forceinline__ uint32_t lds_read(const uint8_t* a) {
+  if (OP == 0) { const u32x4 r = *reinterpret_cast<const u32x4*>(a); return r[0] ^ r[3]; }
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a));
+  const u32x2 rr = __builtin_bit_cast(u32x2, r);
+  return rr[0] ^ rr[1];
+}
+
+// Lane pair (OP 0: ds_read_b128, 1: ds_read_b64_tr_b16): every
+// lane reads one broadcast address except lanes li and lj, lane li at bank set
+// 5 (bytes 80..95 of a 256-byte bank row), lane lj at bank set 5 (same = 1) or
+// 9, each at another address.  Same-set pairs served in one cycle conflict.
+template <int OP>
+__global__ __launch_bounds__(512, 1) void lds_pair_kernel(int li, int lj, int same, int iters,
+                                                         unsigned long long* __restrict__ cycles,
+                                                         uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsProbeBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kLdsProbeBytes / 16; i += 512) reinterpret_cast<u32x4*>(lds)[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  int base = 0;
+  if (lane == li) base = 16 * 5 + 4096;
+  if (lane == lj) base = 16 * (same ? 5 : 9) + 8192;
+  base += 20480 * (w & 1);
+  uint32_t acc = 0;
+  __syncthreads();
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    int a = base;
+    asm volatile("" : "+v"(a));
+    uint32_t x[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = lds_read<OP>(lds + a + 1024 * k);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc ^= x[k];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) cycles[blockIdx.x * 8 + w] = t1 - t0;
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+// The bf16 split kernel's two heavy read patterns over latent rows of `lrb`
+// bytes whose 16-byte chunk index is XOR-ed with 2 ((row >> 2) & 1) when swz:
+// PAT 0, score fragments (ds_read_b128: rows 16 (w & 1) + lane % 16, chunk
+// 4 ks + lane / 16); PAT 1, transposed V reads (ds_read_b64_tr_b16: rows
+// 16 kc + 4 ld + 8 (lane / 32) + lane % 16 / 4, bytes 256 (w & 3) + 32 (lane / 16
+// & 1) + 8 (lane & 3) + 64 cb).
+template <int PAT>
+__global__ __launch_bounds__(512, 1) void lds_layout_kernel(int lrb, int swz, int iters,
+                                                           unsigned long long* __restrict__ cycles,
+                                                           uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsProbeBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kLdsProbeBytes / 16; i += 512) reinterpret_cast<u32x4*>(lds)[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  auto at = [&](int row, int byte) {
+    int c = byte >> 4;
+    if (swz) c ^= ((row >> 2) & 1) << 1;
+    return row * lrb + 16 * c + (byte & 15);
+  };
+  int addr[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    if (PAT == 0) {
+      addr[k] = at(16 * (w & 1) + (lane & 15), 64 * k + 16 * (lane >> 4));
+    } else {
+      const int kc = k >> 3, ld = (k >> 2) & 1, cb = k & 3, G = lane >> 4, s16 = lane & 15;
+      addr[k] = at(16 * kc + 4 * ld + 8 * (G >> 1) + (s16 >> 2), 256 * (w & 3) + 32 * (G & 1) + 8 * (s16 & 3) + 64 * cb);
+    }
+  }
+  uint32_t acc = 0;
+  __syncthreads();
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(addr[k]));   // in place: no copies
+    uint32_t x[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = lds_read<PAT == 0 ? 0 : 1>(lds + addr[k]);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc ^= x[k];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) cycles[blockIdx.x * 8 + w] = t1 - t0;
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+double mean_cycles(const unsigned long long* dev, hipStream_t st) {
+  unsigned long long h[256 * 8];
+  if (hipMemcpyAsync(h, dev, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess) return -1.0;
+  if (hipStreamSynchronize(st) != hipSuccess) return -1.0;
+  double s = 0.0;
+  for (unsigned long long x : h) s += (double)x;
+  return s / (256 * 8);
+}
 }  // namespace
 
 extern "C" {
@@ -100,6 +208,44 @@ int mlab_mfma_peak(void* sink, void* stream, int iters, double* tflops) {
   hipEventDestroy(b);
   *tflops = (double)grid * 4 * iters * 4 * (2.0 * 32 * 32 * 16) / (ms * 1e-3) / 1e12;
   return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+
+// LDS lane pair: LDS cycles per read instruction (a wave's cycles over its 16
+// x `iters` reads, divided by the 8 waves sharing the CU's LDS) with lanes li, lj (0..63) at the same (same = 1) or different
+// bank sets; op 0 ds_read_b128, 1 ds_read_b64_tr_b16.  `scratch`:
+// 256 x 8 x 8 bytes of device memory, `sink` 4 bytes.  Synchronises `stream`.
+int mlab_lds_pair(int op, int li, int lj, int same, int iters, void* scratch, void* sink, void* stream,
+                  double* clk_per_read) {
+  if (op < 0 || op > 1 || li < -1 || li > 63 || lj < -1 || lj > 63 || iters < 1) return -2;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned long long* cyc = (unsigned long long*)scratch;
+  uint32_t* sk = (uint32_t*)sink;
+  if (op == 0) hipLaunchKernelGGL(lds_pair_kernel<0>, dim3(256), dim3(512), 0, st, li, lj, same, iters, cyc, sk);
+  if (op == 1) hipLaunchKernelGGL(lds_pair_kernel<1>, dim3(256), dim3(512), 0, st, li, lj, same, iters, cyc, sk);
+  if (hipGetLastError() != hipSuccess) return -5;
+  const double c = mean_cycles(cyc, st);
+  if (c < 0.0) return -5;
+  *clk_per_read = c / (16.0 * iters * 8.0);
+  return 0;
+}
+
+// LDS layout: LDS cycles per read (as above) of the split kernel's score-fragment (pattern
+// 0) or transposed V (pattern 1) reads over rows of `lrb` bytes (a multiple of
+// 16, 1024..1280), chunk-swizzled when swz.  Same buffers as mlab_lds_pair.
+int mlab_lds_layout(int pattern, int lrb, int swz, int iters, void* scratch, void* sink, void* stream,
+                    double* clk_per_read) {
+  if (pattern < 0 || pattern > 1 || lrb < 1024 || lrb > 1280 || lrb % 16 != 0 || iters < 1) return -2;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned long long* cyc = (unsigned long long*)scratch;
+  uint32_t* sk = (uint32_t*)sink;
+  if (pattern == 0) hipLaunchKernelGGL(lds_layout_kernel<0>, dim3(256), dim3(512), 0, st, lrb, swz, iters, cyc, sk);
+  else hipLaunchKernelGGL(lds_layout_kernel<1>, dim3(256), dim3(512), 0, st, lrb, swz, iters, cyc, sk);
+  if (hipGetLastError() != hipSuccess) return -5;
+  const double c = mean_cycles(cyc, st);
+  if (c < 0.0) return -5;
+  *clk_per_read = c / (16.0 * iters * 8.0);
+  return 0;
 }
 
 }  // extern "C"
